@@ -1,0 +1,20 @@
+"""CPU fp64 oracle of the attention layer's forward pass.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and ``bench.py``'s ``cpu_baseline`` leg, never by the product library.
+"""
+
+from .qknorm_rope_attn import (  # noqa: F401
+    split_qkv,
+    rms_norm,
+    rope_frequencies,
+    rope_rotate_half,
+    qk_norm_rope,
+    softmax,
+    causal_gqa_attention,
+    attend_prefix,
+    prefill,
+    prefill_rows,
+    decode,
+    round_to_bf16,
+)

@@ -1,0 +1,388 @@
+"""Checks that pin the oracle to facts outside itself.
+
+Each ``check_*`` takes the oracle module and raises ``AssertionError`` when
+the oracle disagrees with a closed form, an invariant the pages state, an
+independent evaluator or a printed shape.  ``test_oracle_pins.py`` runs them on
+the real oracle; ``test_oracle_mutations.py`` runs them on deliberately broken
+copies of oracle functions and expects each copy to fail at least one check.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import pathlib
+
+import numpy as np
+import torch
+
+import evaluators
+
+GOLDEN = pathlib.Path(__file__).parent / "golden"
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _layer_args(hq, hkv, d, eps=1e-6, base=1e4):
+    return dict(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, rms_eps=eps, rope_base=base)
+
+
+def _random_prefill(orc, seqlens, hq, hkv, d, seed, base=1e4, eps=1e-6, qkv=None):
+    r = _rng(seed)
+    n = int(sum(seqlens))
+    width = (hq + 2 * hkv) * d
+    if qkv is None:
+        qkv = r.standard_normal((n, width))
+    wq = 1 + 0.1 * r.standard_normal(d)
+    wk = 1 + 0.1 * r.standard_normal(d)
+    pos = np.concatenate([np.arange(t) for t in seqlens]) if seqlens else np.zeros(0)
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int64)
+    res = orc.prefill(qkv, wq, wk, pos, cu, cache_capacity=max(seqlens), **_layer_args(hq, hkv, d, eps, base))
+    return qkv, wq, wk, pos, cu, res
+
+
+# ---------------------------------------------------------------------------
+# Split (column layout of the packed projection)
+# ---------------------------------------------------------------------------
+
+def check_split_layout(orc):
+    hq, hkv, d = 4, 2, 3
+    width = (hq + 2 * hkv) * d
+    # Column c of the packed row holds the value c: Q heads, then K, then V.
+    qkv = np.tile(np.arange(width, dtype=np.float64), (2, 1))
+    q, k, v = orc.split_qkv(qkv, hq, hkv, d)
+    assert q.shape == (2, hq, d) and k.shape == (2, hkv, d) and v.shape == (2, hkv, d)
+    for h in range(hq):
+        assert list(q[1, h]) == [h * d + e for e in range(d)]
+    for g in range(hkv):
+        assert list(k[0, g]) == [(hq + g) * d + e for e in range(d)]
+        assert list(v[0, g]) == [(hq + hkv + g) * d + e for e in range(d)]
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm
+# ---------------------------------------------------------------------------
+
+def check_rmsnorm_constant_vector(orc):
+    d, c, eps = 16, 0.37, 1e-2
+    w = 1 + 0.1 * _rng(1).standard_normal(d)
+    got = orc.rms_norm(np.full((1, d), c), w, eps)
+    want = c / math.sqrt(c * c + eps) * w
+    np.testing.assert_allclose(got[0], want, rtol=1e-14, atol=0)
+
+
+def check_rmsnorm_library(orc):
+    # torch.nn.functional.rms_norm: x * rsqrt(mean(x^2) + eps) * weight.
+    r = _rng(2)
+    x = r.standard_normal((5, 3, 32)) * 3
+    w = 1 + 0.1 * r.standard_normal(32)
+    for eps in (1e-6, 0.5):
+        want = torch.nn.functional.rms_norm(torch.from_numpy(x), (32,), torch.from_numpy(w), eps).numpy()
+        np.testing.assert_allclose(orc.rms_norm(x, w, eps), want, rtol=1e-13, atol=1e-14)
+
+
+def check_rmsnorm_unit_rms(orc):
+    x = _rng(3).standard_normal((7, 64)) * 5
+    y = orc.rms_norm(x, np.ones(64), 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=1e-13)
+    # Scale invariance when eps = 0.
+    np.testing.assert_allclose(orc.rms_norm(2.5 * x, np.ones(64), 0.0), y, rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------
+
+def check_rope_d2_rotation(orc):
+    # D = 2: theta_0 = base^0 = 1, so position p turns (x0, x1) by p radians.
+    x = np.array([[[0.6, -1.3]]])
+    for p in (0, 1, 7, 1234):
+        y = orc.rope_rotate_half(x, np.array([p]), 1e4)[0, 0]
+        c, s = math.cos(p), math.sin(p)
+        np.testing.assert_allclose(y, [0.6 * c + 1.3 * s, -1.3 * c + 0.6 * s], rtol=0, atol=1e-12)
+
+
+def check_rope_d4_frequencies(orc):
+    # D = 4, base 1e4: theta = (1, 1e4^(-1/2) = 0.01).  Unit vectors pick out
+    # each pair's angle.
+    p = 100
+    e0 = np.array([[[1.0, 0.0, 0.0, 0.0]]])
+    e1 = np.array([[[0.0, 1.0, 0.0, 0.0]]])
+    y0 = orc.rope_rotate_half(e0, np.array([p]), 1e4)[0, 0]
+    y1 = orc.rope_rotate_half(e1, np.array([p]), 1e4)[0, 0]
+    np.testing.assert_allclose(y0, [math.cos(100.0), 0, math.sin(100.0), 0], atol=1e-12)
+    np.testing.assert_allclose(y1, [0, math.cos(1.0), 0, math.sin(1.0)], atol=1e-12)
+
+
+def check_rope_complex_form(orc):
+    # Rotate-half RoPE is multiplication of z_i = x_i + i x_{i+D/2} by
+    # exp(i p theta_i), theta_i = base^(-2i/D) (RoFormer).
+    r = _rng(4)
+    d, base = 64, 1e6
+    x = r.standard_normal((9, 3, d))
+    pos = np.array([0, 1, 2, 5, 100, 4095, 4096, 32767, 77])
+    theta = base ** (-np.arange(0, d, 2, dtype=np.float64) / d)
+    z = (x[..., : d // 2] + 1j * x[..., d // 2:]) * np.exp(1j * pos[:, None, None] * theta[None, None, :])
+    want = np.concatenate([z.real, z.imag], axis=-1)
+    np.testing.assert_allclose(orc.rope_rotate_half(x, pos, base), want, rtol=0, atol=1e-11)
+
+
+def check_rope_norm_and_relativity(orc):
+    r = _rng(5)
+    d = 128
+    q = r.standard_normal((1, 1, d))
+    k = r.standard_normal((1, 1, d))
+    for base in (1e4, 1e6):
+        qm = orc.rope_rotate_half(q, np.array([37]), base)
+        np.testing.assert_allclose(np.linalg.norm(qm), np.linalg.norm(q), rtol=1e-13)
+        dots = []
+        for shift in (0, 5, 1000):
+            a = orc.rope_rotate_half(q, np.array([37 + shift]), base)
+            b = orc.rope_rotate_half(k, np.array([12 + shift]), base)
+            dots.append(float(np.sum(a * b)))
+        np.testing.assert_allclose(dots, dots[0], rtol=1e-11)
+        # Position 0 is the identity.
+        assert np.array_equal(orc.rope_rotate_half(q, np.array([0]), base), q)
+
+
+# ---------------------------------------------------------------------------
+# Attention against independent evaluators
+# ---------------------------------------------------------------------------
+
+def _attn_case(seed, t, hq, hkv, d):
+    r = _rng(seed)
+    return r.standard_normal((t, hq, d)), r.standard_normal((t, hkv, d)), r.standard_normal((t, hkv, d))
+
+
+def _teaching_layout(x):
+    return torch.from_numpy(np.ascontiguousarray(np.transpose(x, (1, 0, 2))))[None]
+
+
+def check_attention_vs_expansion(orc):
+    for seed, (t, hq, hkv, d) in enumerate([(1, 4, 2, 8), (3, 4, 2, 8), (17, 8, 2, 16), (40, 6, 3, 32),
+                                            (33, 4, 4, 16), (9, 8, 1, 8)]):
+        q, k, v = _attn_case(10 + seed, t, hq, hkv, d)
+        out, probs = orc.causal_gqa_attention(q, k, v, return_probs=True)
+        want, want_p = evaluators.expanded_attention(_teaching_layout(q), _teaching_layout(k), _teaching_layout(v))
+        np.testing.assert_allclose(out, want[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(probs, want_p[0].numpy(), rtol=0, atol=1e-12)
+
+
+def check_attention_vs_library(orc):
+    for seed, (t, hq, hkv, d) in enumerate([(5, 4, 2, 8), (64, 4, 2, 64), (130, 16, 8, 32), (31, 32, 8, 16)]):
+        q, k, v = _attn_case(20 + seed, t, hq, hkv, d)
+        out = orc.causal_gqa_attention(q, k, v, block=48)
+        for native in (False, True):
+            want = evaluators.library_attention(_teaching_layout(q), _teaching_layout(k), _teaching_layout(v), native)
+            np.testing.assert_allclose(out, want[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def check_layer_brute_force(orc):
+    cases = [([3], 4, 2, 8, 1e4), ([1, 4], 2, 1, 4, 1e6), ([8], 4, 2, 16, 1e4), ([2, 0, 5], 4, 4, 8, 10.0)]
+    for seed, (seqlens, hq, hkv, d, base) in enumerate(cases):
+        qkv, wq, wk, pos, cu, res = _random_prefill(orc, seqlens, hq, hkv, d, 30 + seed, base=base, eps=1e-3)
+        want = evaluators.brute_force_layer(qkv.tolist(), wq.tolist(), wk.tolist(), pos.tolist(), seqlens,
+                                            hq, hkv, d, 1e-3, base)
+        got = res["out"].reshape(-1, hq, d)
+        np.testing.assert_allclose(got, np.array(want).reshape(got.shape), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms and invariants the pages state
+# ---------------------------------------------------------------------------
+
+def check_single_token_returns_v(orc):
+    # T = 1: the only visible key is the token itself, so p = 1 and o_h = v_{h//G}.
+    for hq, hkv in [(4, 2), (8, 8), (6, 1)]:
+        qkv, wq, wk, pos, cu, res = _random_prefill(orc, [1, 1], hq, hkv, 8, 40)
+        _, _, v = orc.split_qkv(qkv, hq, hkv, 8)
+        out = res["out"].reshape(2, hq, 8)
+        for h in range(hq):
+            np.testing.assert_allclose(out[:, h], v[:, h // (hq // hkv)], rtol=0, atol=1e-14)
+
+
+def check_zero_query_prefix_mean(orc):
+    # Zero Q rows normalise to zero, every score is zero, so row i is the mean
+    # of v_0..v_i of its KV head.
+    hq, hkv, d, t = 4, 2, 8, 11
+    r = _rng(41)
+    qkv = r.standard_normal((t, (hq + 2 * hkv) * d))
+    qkv[:, : hq * d] = 0.0
+    _, _, _, _, _, res = _random_prefill(orc, [t], hq, hkv, d, 41, qkv=qkv)
+    _, _, v = orc.split_qkv(qkv, hq, hkv, d)
+    out = res["out"].reshape(t, hq, d)
+    for h in range(hq):
+        g = h // (hq // hkv)
+        want = np.cumsum(v[:, g], axis=0) / np.arange(1, t + 1)[:, None]
+        np.testing.assert_allclose(out[:, h], want, rtol=0, atol=1e-13)
+
+
+def check_softmax_rows(orc):
+    q, k, v = _attn_case(42, 13, 4, 2, 16)
+    _, probs = orc.causal_gqa_attention(q, k, v, return_probs=True)
+    np.testing.assert_allclose(probs.sum(-1), 1.0, rtol=0, atol=1e-14)
+    future = np.triu(np.ones((13, 13), dtype=bool), 1)
+    assert np.all(probs[:, future] == 0.0)
+    assert np.all(probs[:, ~future] > 0.0)
+
+
+def check_causality(orc):
+    hq, hkv, d, t = 4, 2, 16, 20
+    qkv, wq, wk, pos, cu, res = _random_prefill(orc, [t], hq, hkv, d, 43)
+    for i in (0, 7, 18):
+        changed = qkv.copy()
+        changed[i + 1:] = _rng(44 + i).standard_normal(changed[i + 1:].shape)
+        res2 = orc.prefill(changed, wq, wk, pos, cu, cache_capacity=t, **_layer_args(hq, hkv, d))
+        assert np.array_equal(res2["out"][: i + 1], res["out"][: i + 1])
+        assert not np.allclose(res2["out"][i + 1:], res["out"][i + 1:])
+
+
+def check_request_isolation(orc):
+    hq, hkv, d = 4, 2, 8
+    seqlens = [5, 9, 3]
+    qkv, wq, wk, pos, cu, res = _random_prefill(orc, seqlens, hq, hkv, d, 45)
+    changed = qkv.copy()
+    changed[5:14] = _rng(46).standard_normal((9, qkv.shape[1]))
+    res2 = orc.prefill(changed, wq, wk, pos, cu, cache_capacity=9, **_layer_args(hq, hkv, d))
+    np.testing.assert_array_equal(res2["out"][:5], res["out"][:5])
+    np.testing.assert_array_equal(res2["out"][14:], res["out"][14:])
+    # Each request alone gives the same rows as the packed batch.
+    for r in range(3):
+        lo, hi = int(cu[r]), int(cu[r + 1])
+        alone = orc.prefill(qkv[lo:hi], wq, wk, pos[lo:hi], [0, hi - lo], cache_capacity=hi - lo,
+                            **_layer_args(hq, hkv, d))
+        np.testing.assert_allclose(alone["out"], res["out"][lo:hi], rtol=0, atol=1e-14)
+
+
+def check_gqa_grouping(orc):
+    # Repeating each KV head G times in a row (so Hkv becomes Hq) gives the
+    # same output as reading KV head h // G; with Hq=4, Hkv=2 this differs
+    # from reading h % Hkv.
+    q, k, v = _attn_case(47, 9, 4, 2, 8)
+    grouped = orc.causal_gqa_attention(q, k, v)
+    repeated = orc.causal_gqa_attention(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1))
+    np.testing.assert_allclose(grouped, repeated, rtol=0, atol=1e-15)
+    modulo = orc.causal_gqa_attention(q, np.tile(k, (1, 2, 1)), np.tile(v, (1, 2, 1)))
+    assert not np.allclose(grouped, modulo)
+
+
+def check_prefill_cache_layout(orc):
+    hq, hkv, d = 4, 2, 8
+    seqlens = [3, 0, 5]
+    qkv, wq, wk, pos, cu, res = _random_prefill(orc, seqlens, hq, hkv, d, 48)
+    q_t, k_t, v = orc.qk_norm_rope(qkv, wq, wk, pos, **_layer_args(hq, hkv, d))
+    _, _, v_raw = orc.split_qkv(qkv, hq, hkv, d)
+    kc, vc = res["k_cache"], res["v_cache"]
+    assert kc.shape == (3, hkv, 5, d)
+    for r, (lo, t) in enumerate(zip(cu[:-1], seqlens)):
+        for j in range(5):
+            if j < t:
+                np.testing.assert_array_equal(vc[r, :, j], v_raw[lo + j])
+                np.testing.assert_allclose(kc[r, :, j], k_t[lo + j], rtol=0, atol=0)
+            else:
+                assert np.all(np.isnan(kc[r, :, j])) and np.all(np.isnan(vc[r, :, j]))
+
+
+def check_decode_is_last_prefill_row(orc):
+    # A decode step over a cache of L entries equals row L of a prefill over
+    # the L+1 tokens (the cache grows by one, then the new row attends).
+    hq, hkv, d = 8, 2, 16
+    for seed, length in enumerate([0, 1, 6, 21]):
+        t = length + 1
+        qkv, wq, wk, pos, cu, res = _random_prefill(orc, [t], hq, hkv, d, 50 + seed)
+        cap = t + 2
+        kc = np.full((1, hkv, cap, d), np.nan)
+        vc = np.full((1, hkv, cap, d), np.nan)
+        kc[0, :, :length] = res["k_cache"][0, :, :length]
+        vc[0, :, :length] = res["v_cache"][0, :, :length]
+        dec = orc.decode(qkv[length:], wq, wk, [length], [length], kc, vc, **_layer_args(hq, hkv, d))
+        np.testing.assert_allclose(dec["out"][0], res["out"][length], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dec["k_cache"][0, :, : t], res["k_cache"][0, :, : t], rtol=0, atol=1e-15)
+        np.testing.assert_array_equal(dec["v_cache"][0, :, : t], res["v_cache"][0, :, : t])
+        assert np.all(np.isnan(dec["k_cache"][0, :, t:]))
+
+
+def check_sampled_rows(orc):
+    hq, hkv, d = 4, 2, 8
+    seqlens = [7, 12]
+    qkv, wq, wk, pos, cu, res = _random_prefill(orc, seqlens, hq, hkv, d, 55)
+    rows = orc.prefill_rows(res["q_tilde"], res["k_tilde"], res["v"], cu, [0, 6, 7, 13, 18])
+    full = res["out"].reshape(-1, hq, d)
+    for n, row in rows.items():
+        np.testing.assert_allclose(row, full[n], rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Shapes and cache lengths the pages print
+# ---------------------------------------------------------------------------
+
+def check_golden_shapes(orc):
+    fx = json.loads((GOLDEN / "shapes_walkthrough_sec5.json").read_text())
+    t, hq, hkv, d = fx["T"], fx["Hq"], fx["Hkv"], fx["D"]
+    qkv, wq, wk, pos, cu, res = _random_prefill(orc, [t], hq, hkv, d, 60)
+    q, k, v = orc.split_qkv(qkv, hq, hkv, d)
+    assert [1] + list(np.transpose(q, (1, 0, 2)).shape) == fx["q_shape"]
+    assert [1] + list(np.transpose(k, (1, 0, 2)).shape) == fx["kv_shape"]
+    _, probs = orc.causal_gqa_attention(res["q_tilde"], res["k_tilde"], res["v"], return_probs=True)
+    assert [1] + list(probs.shape) == fx["scores_shape"]
+
+    fx = json.loads((GOLDEN / "shapes_qwen3_4b_prefill.json").read_text())
+    t, hq, hkv, d = fx["T"], fx["Hq"], fx["Hkv"], fx["D"]
+    r = _rng(61)
+    qkv = r.standard_normal((t, (hq + 2 * hkv) * d))
+    q, k, v = orc.split_qkv(qkv, hq, hkv, d)
+    assert [1, t, q.shape[1] * d] == fx["q_proj"] and [1, t, k.shape[1] * d] == fx["kv_proj"]
+    assert [1] + list(q.shape) == fx["q_view"] and [1] + list(k.shape) == fx["kv_view"]
+    res = orc.prefill(qkv, np.ones(d), np.ones(d), np.arange(t), [0, t], cache_capacity=t + 1,
+                      **_layer_args(hq, hkv, d, base=1e6))
+    _, probs = orc.causal_gqa_attention(res["q_tilde"], res["k_tilde"], res["v"], return_probs=True)
+    assert [1] + list(probs.shape) == fx["attn_weights"]
+    assert [1] + list(res["out"].shape) == fx["attn_output_flat"]
+
+
+def check_golden_cache_lengths(orc):
+    fx = json.loads((GOLDEN / "cache_lengths_prefill_decode.json").read_text())
+    hq, hkv, d = 4, 2, 8
+    t = fx["prompt_tokens"]
+    qkv, wq, wk, pos, cu, res = _random_prefill(orc, [t], hq, hkv, d, 62)
+
+    def filled(cache):
+        return int(np.sum(~np.isnan(cache[0, 0, :, 0])))
+
+    assert filled(np.full((1, hkv, t + 1, d), np.nan)) == fx["before_prefill"]
+    kc = np.full((1, hkv, t + 1, d), np.nan)
+    kc[:, :, :t] = res["k_cache"]
+    vc = np.full((1, hkv, t + 1, d), np.nan)
+    vc[:, :, :t] = res["v_cache"]
+    assert filled(kc) == fx["after_prefill"] == fx["decode_before_update"]
+    row = _rng(63).standard_normal((1, qkv.shape[1]))
+    dec = orc.decode(row, wq, wk, [t], [t], kc, vc, **_layer_args(hq, hkv, d))
+    assert filled(dec["k_cache"]) == filled(dec["v_cache"]) == fx["decode_after_update"]
+
+
+ALL_CHECKS = [
+    check_split_layout,
+    check_rmsnorm_constant_vector,
+    check_rmsnorm_library,
+    check_rmsnorm_unit_rms,
+    check_rope_d2_rotation,
+    check_rope_d4_frequencies,
+    check_rope_complex_form,
+    check_rope_norm_and_relativity,
+    check_attention_vs_expansion,
+    check_attention_vs_library,
+    check_layer_brute_force,
+    check_single_token_returns_v,
+    check_zero_query_prefix_mean,
+    check_softmax_rows,
+    check_causality,
+    check_request_isolation,
+    check_gqa_grouping,
+    check_prefill_cache_layout,
+    check_decode_is_last_prefill_row,
+    check_sampled_rows,
+    check_golden_shapes,
+    check_golden_cache_lengths,
+]

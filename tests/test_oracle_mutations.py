@@ -1,0 +1,121 @@
+"""Each plausible mistake planted in a copy of an oracle function fails some pin.
+
+The mistakes are planted on the CPU, in the oracle's module namespace, for the
+duration of one test (pytest's monkeypatch restores the real functions).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.qknorm_rope_attn as orc
+import pins
+
+REAL = {name: getattr(orc, name) for name in
+        ("split_qkv", "rms_norm", "rope_rotate_half", "rope_frequencies", "causal_gqa_attention",
+         "attend_prefix", "qk_norm_rope", "softmax")}
+
+
+def _rope_sign(x, positions, base):
+    y = REAL["rope_rotate_half"](x, positions, base)
+    half = y.shape[-1] // 2
+    z = REAL["rope_rotate_half"](x, -np.asarray(positions, dtype=np.float64), base)
+    return np.concatenate([y[..., :half], z[..., half:]], axis=-1)
+
+
+def _freq_exponent(head_dim, base):
+    return np.power(float(base), -np.arange(head_dim // 2, dtype=np.float64) / head_dim)
+
+
+def _eps_outside(x, w, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps) * np.asarray(w, dtype=np.float64)
+
+
+def _no_weight(x, w, eps):
+    return REAL["rms_norm"](x, np.ones_like(np.asarray(w, dtype=np.float64)), eps)
+
+
+def _mean_not_rms(x, w, eps):
+    x = np.asarray(x, dtype=np.float64)
+    c = x - x.mean(axis=-1, keepdims=True)
+    return REAL["rms_norm"](c, w, eps)
+
+
+def _scale_one_over_d(q, k, v, return_probs=False, block=1024):
+    q = np.asarray(q, dtype=np.float64)
+    return REAL["causal_gqa_attention"](q / math.sqrt(q.shape[-1]), k, v, return_probs, block)
+
+
+def _gqa_modulo(q, k, v, return_probs=False, block=1024):
+    hq, hkv = np.shape(q)[1], np.shape(k)[1]
+    idx = [h % hkv for h in range(hq)]
+    return REAL["causal_gqa_attention"](q, np.asarray(k)[:, idx], np.asarray(v)[:, idx], return_probs, block)
+
+
+def _mask_sees_next(q, k, v, return_probs=False, block=1024):
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    t, hq, d = q.shape
+    group = hq // k.shape[1]
+    out = np.empty_like(q)
+    probs = np.zeros((hq, t, t))
+    for h in range(hq):
+        s = q[:, h] @ k[:, h // group].T / math.sqrt(d)
+        allowed = np.arange(t)[None, :] <= np.arange(t)[:, None] + 1
+        s = np.where(allowed, s, -np.inf)
+        p = REAL["softmax"](s)
+        out[:, h] = p @ v[:, h // group]
+        probs[h] = p
+    return (out, probs) if return_probs else out
+
+
+def _kv_swapped(qkv, hq, hkv, d):
+    q, k, v = REAL["split_qkv"](qkv, hq, hkv, d)
+    return q, v, k
+
+
+def _v_normalised(qkv, wq, wk, positions, hq, hkv, d, eps, base):
+    q, k, v = REAL["qk_norm_rope"](qkv, wq, wk, positions, hq, hkv, d, eps, base)
+    return q, k, REAL["rms_norm"](v, np.ones(d), eps)
+
+
+def _decode_without_self(q_row, keys, values):
+    if len(keys) > 1:
+        return REAL["attend_prefix"](q_row, keys[:-1], values[:-1])
+    return REAL["attend_prefix"](q_row, keys, values)
+
+
+def _softmax_no_norm(scores, axis=-1):
+    s = np.asarray(scores, dtype=np.float64)
+    return np.exp(s - np.max(s, axis=axis, keepdims=True))
+
+
+MUTANTS = {
+    "rope_wrong_sign": ("rope_rotate_half", _rope_sign),
+    "rope_frequency_exponent": ("rope_frequencies", _freq_exponent),
+    "rmsnorm_eps_outside_sqrt": ("rms_norm", _eps_outside),
+    "rmsnorm_weight_dropped": ("rms_norm", _no_weight),
+    "rmsnorm_mean_centred": ("rms_norm", _mean_not_rms),
+    "scale_one_over_d": ("causal_gqa_attention", _scale_one_over_d),
+    "gqa_modulo_mapping": ("causal_gqa_attention", _gqa_modulo),
+    "mask_off_by_one": ("causal_gqa_attention", _mask_sees_next),
+    "k_v_columns_swapped": ("split_qkv", _kv_swapped),
+    "v_normalised": ("qk_norm_rope", _v_normalised),
+    "decode_skips_new_token": ("attend_prefix", _decode_without_self),
+    "softmax_not_normalised": ("softmax", _softmax_no_norm),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(orc, attr, fn)
+    caught = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(orc)
+        except Exception as exc:  # any failure (assertion, shape error) means the pin noticed
+            caught.append((check.__name__, type(exc).__name__))
+            break
+    assert caught, f"mutant {name} passed every pin"

@@ -1,0 +1,39 @@
+"""The seeded generators: deterministic, shaped as the layer expects, sentinel-filled caches."""
+
+import torch
+
+from workloads import HeadConfig, build_workload, make_decode_inputs, make_prefill_inputs, qkv_width
+
+
+def test_prefill_generator_shapes_and_determinism():
+    h = HeadConfig(4, 2, 16, 1e-6, 1e4)
+    a = make_prefill_inputs(h, [3, 0, 7], seed=5)
+    b = make_prefill_inputs(h, [3, 0, 7], seed=5)
+    assert torch.equal(a.qkv.float(), b.qkv.float())
+    assert a.qkv.shape == (10, qkv_width(h)) and a.qkv.dtype == torch.bfloat16
+    assert a.cu_seqlens.tolist() == [0, 3, 3, 10]
+    assert a.positions.tolist() == [0, 1, 2] + list(range(7))
+    assert a.k_cache.shape == (3, 2, 7, 16) and torch.isnan(a.k_cache.float()).all()
+    assert a.max_seqlen == 7 and a.num_tokens == 10 and a.num_seqs == 3
+
+
+def test_decode_generator_fills_only_valid_slots():
+    h = HeadConfig(4, 2, 8, 1e-6, 1e4)
+    d = make_decode_inputs(h, [0, 3, 5], seed=9, dtype=torch.float32)
+    assert d.k_cache.shape == (3, 2, 6, 8)
+    for b, L in enumerate([0, 3, 5]):
+        assert not torch.isnan(d.k_cache[b, :, :L]).any()
+        assert torch.isnan(d.k_cache[b, :, L:]).all() and torch.isnan(d.v_cache[b, :, L:]).all()
+    assert d.positions.tolist() == [0, 3, 5]
+    z = make_decode_inputs(h, [2], seed=9, parity=False)
+    assert (z.k_cache[0, :, 2:].float() == 0).all()
+
+
+def test_named_small_workloads():
+    w = build_workload("single_t64_hq4_hkv2_d64")
+    assert w.prefill.qkv.shape == (64, (4 + 4) * 64) and len(w.chained_decode_qkv) == 1
+    assert w.prefill.heads.rope_base == 1e4
+    w = build_workload("pages_t12_decode9")
+    assert w.prefill.seqlens == [12] and len(w.chained_decode_qkv) == 9
+    w = build_workload("qwen3_0p6b_prefill_varlen8")
+    assert len(w.prefill.seqlens) == 8 and all(128 <= t <= 2048 for t in w.prefill.seqlens)

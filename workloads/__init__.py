@@ -1,0 +1,19 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the oracle checks.
+
+This package draws random numbers and lays them out in the shapes the attention
+path consumes.  It contains none of the method's arithmetic (no normalisation,
+rotation, softmax or matrix products), so both the HIP path and the CPU oracle
+can be fed from it without sharing any computation.
+"""
+
+from .synth import (  # noqa: F401
+    HeadConfig,
+    PrefillInputs,
+    DecodeInputs,
+    WorkloadInputs,
+    WORKLOADS,
+    build_workload,
+    make_prefill_inputs,
+    make_decode_inputs,
+    qkv_width,
+)

@@ -1,0 +1,293 @@
+"""Seeded synthetic workloads for QK-norm + RoPE + causal GQA attention.
+
+Every tensor here is drawn from a seeded generator; nothing is computed from
+the drawn values.  The shapes follow the layouts of the attention layer the
+pages describe:
+
+* packed ``qkv`` rows ``[N, (Hq + 2*Hkv) * D]`` -- Q heads, then K heads, then
+  V heads, each ``D`` columns wide (zero-to-sglang "Chapter 3 ... (Code
+  Walkthrough)", section 3.3; jq-wei "transformer basics", "Attention
+  calculation: part 1");
+* per-head norm weights ``[D]``, drawn as ``1 + 0.1 * N(0, 1)``;
+* requests packed back to back and delimited by ``cu_seqlens`` (the packed
+  ``[N, C]`` batch of the code walkthrough, section 3.1);
+* a contiguous K/V cache ``[B, Hkv, S_cap, D]`` per request and KV head (the
+  per-layer cache that prefill fills and decode extends, "transformer
+  basics", "Prefill vs Decode").
+
+Draw order for one workload (all on one CPU ``torch.Generator`` seeded with the
+workload's seed): request / cache lengths, then ``qkv`` (fp32 normal, rounded
+to the storage dtype), then the Q-norm weight, then the K-norm weight.  Decode
+cache contents (K slots below each cache length, then V) are drawn afterwards
+from a second generator, seeded with ``seed + 1``, on the device that will hold
+the cache, because the long-context caches run to gigabytes.  Cache slots that
+hold no token are filled with NaN in parity runs (so any stray read or write
+shows) and with zeros in timing runs.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class HeadConfig:
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    rms_eps: float = 1e-6
+    rope_base: float = 1e6
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+
+def qkv_width(h: HeadConfig) -> int:
+    return (h.num_q_heads + 2 * h.num_kv_heads) * h.head_dim
+
+
+@dataclasses.dataclass
+class PrefillInputs:
+    heads: HeadConfig
+    qkv: torch.Tensor            # [N, (Hq+2Hkv)*D]
+    q_norm_weight: torch.Tensor  # [D]
+    k_norm_weight: torch.Tensor  # [D]
+    positions: torch.Tensor      # int32 [N]
+    cu_seqlens: torch.Tensor     # int32 [B+1]
+    seqlens: List[int]
+    cache_capacity: int
+    k_cache: torch.Tensor        # [B, Hkv, S_cap, D], initial contents
+    v_cache: torch.Tensor
+
+    @property
+    def num_tokens(self) -> int:
+        return int(sum(self.seqlens))
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.seqlens)
+
+    @property
+    def max_seqlen(self) -> int:
+        return max(self.seqlens) if self.seqlens else 0
+
+
+@dataclasses.dataclass
+class DecodeInputs:
+    heads: HeadConfig
+    qkv: torch.Tensor            # [B, (Hq+2Hkv)*D], one new token per request
+    q_norm_weight: torch.Tensor
+    k_norm_weight: torch.Tensor
+    positions: torch.Tensor      # int32 [B]
+    cache_lens: torch.Tensor     # int32 [B], valid entries before this step
+    cache_capacity: int
+    k_cache: torch.Tensor        # [B, Hkv, S_cap, D]
+    v_cache: torch.Tensor
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.qkv.shape[0])
+
+    @property
+    def max_cache_len(self) -> int:
+        return int(self.cache_lens.max().item()) if self.num_seqs else 0
+
+
+@dataclasses.dataclass
+class WorkloadInputs:
+    name: str
+    description: str
+    prefill: Optional[PrefillInputs]
+    decode: Optional[DecodeInputs]
+    # Rows for decode steps that continue the prefill's own cache: one
+    # [B_prefill, W] tensor per step; step s runs at position T_r + s.
+    chained_decode_qkv: List[torch.Tensor] = dataclasses.field(default_factory=list)
+
+
+def _sentinel(parity: bool) -> float:
+    return float("nan") if parity else 0.0
+
+
+def _empty_cache(h: HeadConfig, batch: int, capacity: int, dtype, device, parity: bool):
+    shape = (batch, h.num_kv_heads, capacity, h.head_dim)
+    k = torch.full(shape, _sentinel(parity), dtype=dtype, device=device)
+    v = torch.full(shape, _sentinel(parity), dtype=dtype, device=device)
+    return k, v
+
+
+def _draw_rows(g: torch.Generator, rows: int, h: HeadConfig, dtype) -> torch.Tensor:
+    return torch.randn((rows, qkv_width(h)), generator=g, dtype=torch.float32).to(dtype)
+
+
+def _draw_norm_weight(g: torch.Generator, h: HeadConfig, dtype) -> torch.Tensor:
+    return (1.0 + 0.1 * torch.randn((h.head_dim,), generator=g, dtype=torch.float32)).to(dtype)
+
+
+def _fill_decode_cache(h: HeadConfig, cache_lens: torch.Tensor, capacity: int, seed: int,
+                       dtype, device, parity: bool):
+    """K then V cache with N(0,1) in slots < cache_len, sentinel elsewhere."""
+    batch = int(cache_lens.numel())
+    shape = (batch, h.num_kv_heads, capacity, h.head_dim)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    lens_dev = cache_lens.to(device=device, dtype=torch.int64)
+    unused = (torch.arange(capacity, device=device)[None, :] >= lens_dev[:, None])  # [B, S]
+    unused = unused[:, None, :, None]
+    caches = []
+    for _ in range(2):
+        c = torch.empty(shape, dtype=dtype, device=device)
+        c.normal_(generator=g)
+        c.masked_fill_(unused, _sentinel(parity))
+        caches.append(c)
+    return caches[0], caches[1]
+
+
+def _prefill_from_rows(h: HeadConfig, rows: torch.Tensor, wq, wk, seqlens: Sequence[int],
+                       capacity: Optional[int], dtype, device, parity: bool) -> PrefillInputs:
+    seqlens = [int(t) for t in seqlens]
+    cu = [0]
+    for t in seqlens:
+        cu.append(cu[-1] + t)
+    positions = torch.cat([torch.arange(t, dtype=torch.int32) for t in seqlens]) if seqlens else \
+        torch.zeros((0,), dtype=torch.int32)
+    cap = capacity if capacity is not None else max(seqlens + [1])
+    k_cache, v_cache = _empty_cache(h, len(seqlens), cap, dtype, device, parity)
+    return PrefillInputs(
+        heads=h, qkv=rows.to(device), q_norm_weight=wq.to(device), k_norm_weight=wk.to(device),
+        positions=positions.to(device), cu_seqlens=torch.tensor(cu, dtype=torch.int32).to(device),
+        seqlens=seqlens, cache_capacity=cap, k_cache=k_cache, v_cache=v_cache)
+
+
+def make_prefill_inputs(h: HeadConfig, seqlens: Sequence[int], seed: int, dtype=torch.bfloat16,
+                        device="cpu", capacity: Optional[int] = None, parity: bool = True) -> PrefillInputs:
+    """A prefill batch of requests with the given lengths (positions 0..T_r-1 each)."""
+    g = torch.Generator().manual_seed(seed)
+    rows = _draw_rows(g, int(sum(seqlens)), h, dtype)
+    wq = _draw_norm_weight(g, h, dtype)
+    wk = _draw_norm_weight(g, h, dtype)
+    return _prefill_from_rows(h, rows, wq, wk, seqlens, capacity, dtype, device, parity)
+
+
+def make_decode_inputs(h: HeadConfig, cache_lens: Sequence[int], seed: int, dtype=torch.bfloat16,
+                       device="cpu", capacity: Optional[int] = None, parity: bool = True) -> DecodeInputs:
+    """One new token per request on top of a cache holding ``cache_lens[b]`` entries."""
+    g = torch.Generator().manual_seed(seed)
+    lens = torch.tensor([int(x) for x in cache_lens], dtype=torch.int32)
+    rows = _draw_rows(g, int(lens.numel()), h, dtype)
+    wq = _draw_norm_weight(g, h, dtype)
+    wk = _draw_norm_weight(g, h, dtype)
+    cap = capacity if capacity is not None else (int(lens.max().item()) + 1 if lens.numel() else 1)
+    k_cache, v_cache = _fill_decode_cache(h, lens, cap, seed + 1, dtype, device, parity)
+    return DecodeInputs(heads=h, qkv=rows.to(device), q_norm_weight=wq.to(device),
+                        k_norm_weight=wk.to(device), positions=lens.clone().to(device),
+                        cache_lens=lens.to(device), cache_capacity=cap, k_cache=k_cache, v_cache=v_cache)
+
+
+# ---------------------------------------------------------------------------
+# Named workloads.  Head shapes follow the Qwen3 configurations the pages
+# trace (Qwen3-4B: 32 query heads, 8 KV heads, head_dim 128 -- "transformer
+# basics", "Qwen3 analogies"); lengths and mixes are the benchmark's.
+# ---------------------------------------------------------------------------
+
+def _pages_t12_decode9(dtype, device, parity):
+    # The pages' own run: a 12-token prompt, then 9 generated tokens, on
+    # Qwen3-4B heads ("transformer basics", "Prefill vs Decode").
+    h = HeadConfig(32, 8, 128, 1e-6, 1e6)
+    g = torch.Generator().manual_seed(1000)
+    rows = _draw_rows(g, 12 + 9, h, dtype)
+    wq = _draw_norm_weight(g, h, dtype)
+    wk = _draw_norm_weight(g, h, dtype)
+    pre = _prefill_from_rows(h, rows[:12], wq, wk, [12], 21, dtype, device, parity)
+    steps = [rows[12 + s: 13 + s].to(device) for s in range(9)]
+    return WorkloadInputs("pages_t12_decode9",
+                          "prefill T=12 then 9 chained decode steps, Hq=32 Hkv=8 D=128, base 1e6",
+                          pre, None, steps)
+
+
+def _single_t64(dtype, device, parity):
+    h = HeadConfig(4, 2, 64, 1e-6, 1e4)
+    g = torch.Generator().manual_seed(1001)
+    rows = _draw_rows(g, 64 + 1, h, dtype)
+    wq = _draw_norm_weight(g, h, dtype)
+    wk = _draw_norm_weight(g, h, dtype)
+    pre = _prefill_from_rows(h, rows[:64], wq, wk, [64], 65, dtype, device, parity)
+    return WorkloadInputs("single_t64_hq4_hkv2_d64",
+                          "one request T=64, Hq=4 Hkv=2 D=64, base 1e4; then one decode at position 64",
+                          pre, None, [rows[64:65].to(device)])
+
+
+def _qwen3_0p6b_varlen8(dtype, device, parity):
+    h = HeadConfig(16, 8, 128, 1e-6, 1e6)
+    g = torch.Generator().manual_seed(1002)
+    lens = torch.randint(128, 2048 + 1, (8,), generator=g).tolist()
+    rows = _draw_rows(g, int(sum(lens)), h, dtype)
+    wq = _draw_norm_weight(g, h, dtype)
+    wk = _draw_norm_weight(g, h, dtype)
+    pre = _prefill_from_rows(h, rows, wq, wk, lens, max(lens), dtype, device, parity)
+    return WorkloadInputs("qwen3_0p6b_prefill_varlen8",
+                          "prefill of 8 packed requests, lengths U[128,2048], Hq=16 Hkv=8 D=128",
+                          pre, None)
+
+
+def _qwen3_4b_decode64(dtype, device, parity):
+    h = HeadConfig(32, 8, 128, 1e-6, 1e6)
+    g = torch.Generator().manual_seed(1003)
+    lens = torch.randint(512, 8192 + 1, (64,), generator=g).to(torch.int32)
+    rows = _draw_rows(g, 64, h, dtype)
+    wq = _draw_norm_weight(g, h, dtype)
+    wk = _draw_norm_weight(g, h, dtype)
+    k, v = _fill_decode_cache(h, lens, 8193, 1003 + 1, dtype, device, parity)
+    dec = DecodeInputs(h, rows.to(device), wq.to(device), wk.to(device), lens.clone().to(device),
+                       lens.to(device), 8193, k, v)
+    return WorkloadInputs("qwen3_4b_decode64",
+                          "decode of 64 requests, cache lengths U[512,8192], Hq=32 Hkv=8 D=128",
+                          None, dec)
+
+
+def _long_prefill_32k(dtype, device, parity):
+    h = HeadConfig(32, 8, 128, 1e-6, 1e6)
+    g = torch.Generator().manual_seed(1004)
+    rows = _draw_rows(g, 32768, h, dtype)
+    wq = _draw_norm_weight(g, h, dtype)
+    wk = _draw_norm_weight(g, h, dtype)
+    pre = _prefill_from_rows(h, rows, wq, wk, [32768], 32768, dtype, device, parity)
+    return WorkloadInputs("long_prefill_32k",
+                          "one request T=32768, Hq=32 Hkv=8 D=128, base 1e6", pre, None)
+
+
+def _mixed_qwen3_8b(dtype, device, parity):
+    h = HeadConfig(32, 8, 128, 1e-6, 1e6)
+    g = torch.Generator().manual_seed(1005)
+    lens = torch.randint(1, 16384 + 1, (128,), generator=g).to(torch.int32)
+    rows = _draw_rows(g, 4 * 4096 + 128, h, dtype)
+    wq = _draw_norm_weight(g, h, dtype)
+    wk = _draw_norm_weight(g, h, dtype)
+    pre = _prefill_from_rows(h, rows[:4 * 4096], wq, wk, [4096] * 4, 4096, dtype, device, parity)
+    k, v = _fill_decode_cache(h, lens, 16385, 1005 + 1, dtype, device, parity)
+    dec = DecodeInputs(h, rows[4 * 4096:].contiguous().to(device), wq.to(device), wk.to(device),
+                       lens.clone().to(device), lens.to(device), 16385, k, v)
+    return WorkloadInputs("mixed_qwen3_8b",
+                          "one step: prefill of 4x4096 tokens plus decode of 128 requests with cache "
+                          "lengths U[1,16384], Hq=32 Hkv=8 D=128", pre, dec)
+
+
+WORKLOADS: Dict[str, object] = {
+    "pages_t12_decode9": _pages_t12_decode9,
+    "single_t64_hq4_hkv2_d64": _single_t64,
+    "qwen3_0p6b_prefill_varlen8": _qwen3_0p6b_varlen8,
+    "qwen3_4b_decode64": _qwen3_4b_decode64,
+    "long_prefill_32k": _long_prefill_32k,
+    "mixed_qwen3_8b": _mixed_qwen3_8b,
+}
+
+
+def build_workload(name: str, dtype=torch.bfloat16, device="cpu", parity: bool = True) -> WorkloadInputs:
+    try:
+        fn = WORKLOADS[name]
+    except KeyError:
+        raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS)}") from None
+    return fn(dtype, device, parity)
