@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Throughput of QK-norm + RoPE + causal GQA attention on one MI355X.
+
+A step is one pass of the whole attention hot path over one batch: the
+default workload is the mixed packed step on Qwen3-8B-shaped heads (Hq=32,
+Hkv=8, D=128): a prefill of 4 requests x 4096 tokens (QK-norm + RoPE +
+K/V-cache write + causal attention) followed, on the same stream, by one
+decode step for 128 requests whose caches hold U[1, 16384] entries.
+
+Metric: attention work as a fraction of the MI355X roofline.  For a step,
+    value = 100 * (F / P_mfma + B / P_hbm) / t_step
+with F the causal prefill FLOPs (sum over requests of 2*D*Hq*T(T+1)), B the
+decode K/V bytes (sum over requests of 2*Hkv*(L+1)*D*2), P_mfma = 2500 TFLOP/s
+(dense bf16 MFMA) and P_hbm = 8000 GB/s; i.e. the ideal time of the step's
+work on each roofline divided by the measured step time.  Inputs are resident
+in HBM before timing starts.
+
+Prints one JSON line.  ``--gpus N`` with N > 1 is refused: this path runs on
+one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "prefill_attn_mfma_bf16": "decoder_attention_amd/csrc/prefill_mfma.hip",
+    "decode_attn_split": "decoder_attention_amd/csrc/decode.hip",
+    "qknorm_rope_kv_prefill": "decoder_attention_amd/csrc/qknorm_rope.hip",
+    "qknorm_rope_kv_decode": "decoder_attention_amd/csrc/qknorm_rope.hip",
+    "decode_attn_combine": "decoder_attention_amd/csrc/decode.hip",
+}
+
+
+def prefill_flops(seqlens, hq, d) -> float:
+    return float(sum(2 * d * hq * t * (t + 1) for t in seqlens))
+
+
+def decode_kv_bytes(cache_lens, hkv, d, elem) -> float:
+    return float(sum(2 * hkv * (int(L) + 1) * d * elem for L in cache_lens))
+
+
+def source_digest(path: str) -> str:
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it is for this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = table.get(kernel, {}).get(workload)
+    src = KERNEL_SOURCES.get(kernel)
+    if not entry or not src or entry.get("source_sha256") != source_digest(src):
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+class Runner:
+    """Holds device inputs/outputs/workspaces of a workload and issues its step."""
+
+    def __init__(self, w, torch, da):
+        self.torch, self.da, self.w = torch, da, w
+        self.calls = []
+        if w.prefill is not None:
+            p = w.prefill
+            h = p.heads
+            cfg = da.make_config(h.num_q_heads, h.num_kv_heads, h.head_dim, p.qkv.dtype, h.rms_eps, h.rope_base)
+            out = torch.empty((p.num_tokens, h.num_q_heads * h.head_dim), dtype=p.qkv.dtype, device=p.qkv.device)
+            ws_bytes = da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_PREFILL, p.num_tokens, p.max_seqlen)
+            ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=p.qkv.device)
+            args = (cfg, p.qkv, p.q_norm_weight, p.k_norm_weight, p.positions, p.cu_seqlens, p.num_tokens,
+                    p.num_seqs, p.max_seqlen, p.k_cache, p.v_cache, p.cache_capacity, out, ws, ws_bytes)
+            self.calls.append((da.qknorm_rope_attn_prefill, args, (out, ws)))
+        if w.decode is not None:
+            d = w.decode
+            h = d.heads
+            cfg = da.make_config(h.num_q_heads, h.num_kv_heads, h.head_dim, d.qkv.dtype, h.rms_eps, h.rope_base)
+            out = torch.empty((d.num_seqs, h.num_q_heads * h.head_dim), dtype=d.qkv.dtype, device=d.qkv.device)
+            ws_bytes = da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_DECODE, d.num_seqs, d.max_cache_len)
+            ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=d.qkv.device)
+            args = (cfg, d.qkv, d.q_norm_weight, d.k_norm_weight, d.positions, d.cache_lens, d.num_seqs,
+                    d.max_cache_len, d.k_cache, d.v_cache, d.cache_capacity, out, ws, ws_bytes)
+            self.calls.append((da.qknorm_rope_attn_decode, args, (out, ws)))
+
+    def step(self):
+        for fn, args, _ in self.calls:
+            status = fn(*args)
+            if status != 0:
+                raise self.da.QkraError(status, fn.__name__)
+
+    def work(self):
+        F = B = 0.0
+        if self.w.prefill is not None:
+            h = self.w.prefill.heads
+            F = prefill_flops(self.w.prefill.seqlens, h.num_q_heads, h.head_dim)
+        if self.w.decode is not None:
+            h = self.w.decode.heads
+            B = decode_kv_bytes(self.w.decode.cache_lens.tolist(), h.num_kv_heads, h.head_dim,
+                                self.w.decode.qkv.element_size())
+        return F, B
+
+
+def time_steps(runner, steps: int, warmup: int):
+    torch, da = runner.torch, runner.da
+    for _ in range(warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    da.qknorm_rope_attn_read_kernel_timing()          # drop anything recorded before
+    da.qknorm_rope_attn_set_kernel_timing(True)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        runner.step()
+    stop.record()
+    torch.cuda.synchronize()
+    da.qknorm_rope_attn_set_kernel_timing(False)
+    kernels = da.qknorm_rope_attn_read_kernel_timing()
+    return start.elapsed_time(stop) / steps, kernels
+
+
+def roofline_for(name, kernels, F, B, workload):
+    total_ms, launches = kernels[name]
+    avg_s = total_ms / launches / 1e3
+    if name.startswith("prefill_attn"):
+        achieved = F / avg_s / 1e12
+        rf = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+              "frac": achieved / PEAK_MFMA_TFLOPS}
+    elif name == "decode_attn_split":
+        achieved = B / avg_s / 1e9
+        rf = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+              "frac": achieved / PEAK_HBM_GBPS}
+    else:
+        return None
+    rf["kernel"] = name
+    rf["avg_launch_ms"] = total_ms / launches
+    rf["traffic"] = measured_traffic(name, workload)
+    return rf
+
+
+def cpu_baseline(w, F_total, B_total, budget_s: float = 20.0):
+    """The oracle, as it stands, on a bounded sample of the same workload, scaled to the step."""
+    import numpy as np
+
+    import oracle
+
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:  # threadpoolctl missing or no BLAS pools
+        threads = None
+    cores = threads or len(os.sched_getaffinity(0))
+
+    def f64(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    t_total = 0.0
+    parts = []
+    if w.prefill is not None and F_total > 0:
+        p = w.prefill
+        h = p.heads
+        lo, hi = int(p.cu_seqlens[0]), int(p.cu_seqlens[1])
+        t0 = time.perf_counter()
+        qt, kt, v = oracle.qk_norm_rope(f64(p.qkv[lo:hi]), f64(p.q_norm_weight), f64(p.k_norm_weight),
+                                        p.positions[lo:hi].cpu().numpy(), h.num_q_heads, h.num_kv_heads,
+                                        h.head_dim, h.rms_eps, h.rope_base)
+        g = h.num_q_heads // h.num_kv_heads
+        oracle.causal_gqa_attention(qt[:, :g], kt[:, :1], v[:, :1])
+        dt = time.perf_counter() - t0
+        T = hi - lo
+        f_sample = 2.0 * h.head_dim * g * T * (T + 1)
+        t_total += dt * F_total / f_sample
+        parts.append(f"prefill: request 0 ({T} tokens), KV head 0 and its {g} query heads, {dt:.1f} s")
+    if w.decode is not None and B_total > 0:
+        d = w.decode
+        h = d.heads
+        lens = d.cache_lens.cpu().tolist()
+        order = sorted(range(len(lens)), key=lambda b: lens[b])
+        subset = order[len(order) // 2: len(order) // 2 + 4]
+        import torch
+
+        idx = torch.tensor(subset, device=d.k_cache.device)
+        top = max(lens[b] for b in subset) + 1
+        kc = f64(d.k_cache.index_select(0, idx)[:, :, :top])
+        vc = f64(d.v_cache.index_select(0, idx)[:, :, :top])
+        t0 = time.perf_counter()
+        oracle.decode(f64(d.qkv.index_select(0, idx)), f64(d.q_norm_weight), f64(d.k_norm_weight),
+                      np.array(lens)[subset], np.array(lens)[subset], kc, vc, h.num_q_heads, h.num_kv_heads,
+                      h.head_dim, h.rms_eps, h.rope_base)
+        dt = time.perf_counter() - t0
+        b_sample = decode_kv_bytes([lens[b] for b in subset], h.num_kv_heads, h.head_dim, d.qkv.element_size())
+        t_total += dt * B_total / b_sample
+        parts.append(f"decode: 4 median-length requests ({[lens[b] for b in subset]} cached), all heads, {dt:.1f} s")
+    value = 100.0 * (F_total / (PEAK_MFMA_TFLOPS * 1e12) + B_total / (PEAK_HBM_GBPS * 1e9)) / t_total
+    return {"value": value, "unit": "% of MI355X peak", "cores": cores, "kind": "oracle",
+            "sample": "; ".join(parts) + f"; scaled linearly to the whole step: {t_total:.1f} s per step",
+            "step_seconds_est": t_total}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixed_qwen3_8b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the long-prefill and decode-only side runs")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; this attention path runs on one GPU "
+              "(each GPU would take its own share of KV heads or requests, with no exchange).", file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: launched with WORLD_SIZE > 1; this benchmark runs on one GPU only.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import decoder_attention_amd as da
+    from workloads import build_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    da.lib()
+    dev = "cuda:0"
+
+    def measure(name, steps, warmup):
+        w = build_workload(name, device=dev, parity=False)
+        runner = Runner(w, torch, da)
+        ms, kernels = time_steps(runner, steps, warmup)
+        F, B = runner.work()
+        return w, runner, ms, kernels, F, B
+
+    w, runner, ms, kernels, F, B = measure(args.workload, args.steps, args.warmup)
+    t = ms / 1e3
+    value = 100.0 * (F / (PEAK_MFMA_TFLOPS * 1e12) + B / (PEAK_HBM_GBPS * 1e9)) / t
+    per_kernel = {k: {"avg_ms": v[0] / v[1], "launches_per_step": v[1] / args.steps} for k, v in kernels.items()}
+    dominant = max(kernels, key=lambda k: kernels[k][0])
+    roof = roofline_for(dominant, kernels, F, B, args.workload)
+    side = {}
+    pre_ms = sum(kernels[k][0] for k in ("qknorm_rope_kv_prefill", "prefill_attn_mfma_bf16") if k in kernels)
+    dec_ms = sum(kernels[k][0] for k in ("qknorm_rope_kv_decode", "decode_attn_split", "decode_attn_combine")
+                 if k in kernels)
+    if F:
+        tf = F / (pre_ms / args.steps / 1e3) / 1e12
+        side["prefill_call"] = {"tflops": tf, "frac_of_mfma_peak": tf / PEAK_MFMA_TFLOPS,
+                                "ms": pre_ms / args.steps, "flops": F}
+        side["prefill_kernel"] = roofline_for("prefill_attn_mfma_bf16", kernels, F, B, args.workload)
+    if B:
+        gbps = B / (dec_ms / args.steps / 1e3) / 1e9
+        side["decode_call"] = {"gbps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS, "ms": dec_ms / args.steps,
+                               "kv_bytes": B}
+        side["decode_kernel"] = roofline_for("decode_attn_split", kernels, F, B, args.workload)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, F, B)
+    del runner, w
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not args.no_extra:
+        for name, steps in (("long_prefill_32k", 5), ("qwen3_4b_decode64", 20)):
+            ew, er, ems, ek, eF, eB = measure(name, steps, 2)
+            key = "prefill_attn_mfma_bf16" if eF else "decode_attn_split"
+            extra[name] = {"ms_per_call": ems, "kernel": roofline_for(key, ek, eF, eB, name),
+                           "call_rate": (eF / (ems / 1e3) / 1e12) if eF else (eB / (ems / 1e3) / 1e9),
+                           "call_rate_unit": "TFLOP/s" if eF else "GB/s"}
+            del er, ew
+            torch.cuda.empty_cache()
+
+    record = {
+        "metric": "prefill attention TFLOP/s + decode KV GB/s, as % of MI355X peak",
+        "value": value,
+        "unit": "% of MI355X peak",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal qkv, norm weights 1+0.1N, cache contents N(0,1))",
+        "config": {"workload": args.workload, "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128,
+                   "prefill_seqlens": [4096] * 4 if args.workload == "mixed_qwen3_8b" else None,
+                   "decode_requests": 128 if args.workload == "mixed_qwen3_8b" else None,
+                   "decode_cache_lens": "U[1,16384], seed 1005" if args.workload == "mixed_qwen3_8b" else None,
+                   "prefill_flops": F, "decode_kv_bytes": B},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parts": side,
+        "kernels": per_kernel,
+        "side_workloads": extra,
+    }
+    print(json.dumps(record), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

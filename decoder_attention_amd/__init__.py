@@ -1,0 +1,85 @@
+"""QK-RMSNorm + RoPE + causal grouped-query attention for MI355X (gfx950).
+
+The computation lives in the HIP library ``libqknorm_rope_attn.so`` (C ABI in
+``include/qknorm_rope_attn.h``); this package binds it and adds two
+conveniences that allocate outputs and workspace with PyTorch before calling
+it.  PyTorch supplies device memory and the current stream only.
+"""
+
+from __future__ import annotations
+
+from .binding import (  # noqa: F401
+    QKRA_BF16,
+    QKRA_FP32,
+    QKRA_OK,
+    QKRA_ERR_INVALID_ARGUMENT,
+    QKRA_ERR_UNSUPPORTED,
+    QKRA_ERR_CAPACITY,
+    QKRA_ERR_WORKSPACE_TOO_SMALL,
+    QKRA_ERR_ALIASING,
+    QKRA_ERR_HIP,
+    QKRA_MODE_PREFILL,
+    QKRA_MODE_DECODE,
+    QkraConfig,
+    QkraError,
+    check,
+    exported_symbols,
+    lib,
+    make_config,
+    qknorm_rope_attn_prefill,
+    qknorm_rope_attn_decode,
+    qknorm_rope_attn_workspace_bytes,
+    qknorm_rope_attn_status_string,
+    qknorm_rope_attn_last_hip_error,
+    qknorm_rope_attn_version,
+    qknorm_rope_attn_set_kernel_timing,
+    qknorm_rope_attn_read_kernel_timing,
+    qknorm_rope_attn_kernel_name,
+)
+
+
+def _require_device(*tensors):
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def prefill(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens, max_seqlen: int,
+            k_cache, v_cache, out=None, workspace=None, stream=None):
+    """Runs ``qknorm_rope_attn_prefill``; returns (out [N, Hq*D], workspace)."""
+    import torch
+
+    _require_device(qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens, k_cache, v_cache)
+    n = qkv.shape[0]
+    b = cu_seqlens.shape[0] - 1
+    if out is None:
+        out = torch.empty((n, cfg.num_q_heads * cfg.head_dim), dtype=qkv.dtype, device=qkv.device)
+    need = qknorm_rope_attn_workspace_bytes(cfg, QKRA_MODE_PREFILL, n, max_seqlen)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=qkv.device)
+    status = qknorm_rope_attn_prefill(cfg, qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens, n, b,
+                                      max_seqlen, k_cache, v_cache, k_cache.shape[2], out, workspace,
+                                      workspace.numel() * workspace.element_size(), stream)
+    check(status, "qknorm_rope_attn_prefill")
+    return out, workspace
+
+
+def decode(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cache_lens, max_cache_len: int,
+           k_cache, v_cache, out=None, workspace=None, stream=None):
+    """Runs ``qknorm_rope_attn_decode``; returns (out [B, Hq*D], workspace)."""
+    import torch
+
+    _require_device(qkv, q_norm_weight, k_norm_weight, positions, cache_lens, k_cache, v_cache)
+    b = qkv.shape[0]
+    if out is None:
+        out = torch.empty((b, cfg.num_q_heads * cfg.head_dim), dtype=qkv.dtype, device=qkv.device)
+    need = qknorm_rope_attn_workspace_bytes(cfg, QKRA_MODE_DECODE, b, max_cache_len)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=qkv.device)
+    status = qknorm_rope_attn_decode(cfg, qkv, q_norm_weight, k_norm_weight, positions, cache_lens, b,
+                                     max_cache_len, k_cache, v_cache, k_cache.shape[2], out, workspace,
+                                     workspace.numel() * workspace.element_size(), stream)
+    check(status, "qknorm_rope_attn_decode")
+    return out, workspace

@@ -1,0 +1,181 @@
+"""ctypes binding of the C ABI declared in ``include/qknorm_rope_attn.h``.
+
+Argument marshalling only: tensors become device pointers, the stream becomes
+a ``hipStream_t``.  Every step of the computation runs in the HIP library; if
+the library is not built, loading it raises instead of falling back to
+anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+from .build import LIB_PATH
+
+QKRA_BF16 = 0
+QKRA_FP32 = 1
+
+QKRA_OK = 0
+QKRA_ERR_INVALID_ARGUMENT = 1
+QKRA_ERR_UNSUPPORTED = 2
+QKRA_ERR_CAPACITY = 3
+QKRA_ERR_WORKSPACE_TOO_SMALL = 4
+QKRA_ERR_ALIASING = 5
+QKRA_ERR_HIP = 6
+
+QKRA_MODE_PREFILL = 0
+QKRA_MODE_DECODE = 1
+
+
+class QkraConfig(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("rms_eps", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+        ("rope_base", ctypes.c_double),
+    ]
+
+
+class QkraError(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        self.status = status
+        msg = f"{where}: " if where else ""
+        msg += f"status {status} ({qknorm_rope_attn_status_string(status)})"
+        if status == QKRA_ERR_HIP:
+            msg += f", hipError {qknorm_rope_attn_last_hip_error()}"
+        super().__init__(msg)
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "qknorm_rope_attn_prefill": (_I32, [ctypes.POINTER(QkraConfig), _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P,
+                                        _I32, _P, _P, _SZ, _P]),
+    "qknorm_rope_attn_decode": (_I32, [ctypes.POINTER(QkraConfig), _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32,
+                                       _P, _P, _SZ, _P]),
+    "qknorm_rope_attn_workspace_bytes": (_SZ, [ctypes.POINTER(QkraConfig), _I32, _I32, _I32]),
+    "qknorm_rope_attn_status_string": (ctypes.c_char_p, [_I32]),
+    "qknorm_rope_attn_last_hip_error": (_I32, []),
+    "qknorm_rope_attn_version": (_I32, []),
+    "qknorm_rope_attn_set_kernel_timing": (_I32, [_I32]),
+    "qknorm_rope_attn_read_kernel_timing": (_I32, [ctypes.POINTER(ctypes.c_double),
+                                                   ctypes.POINTER(ctypes.c_int64), _I32]),
+    "qknorm_rope_attn_kernel_name": (ctypes.c_char_p, [_I32]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"HIP library {LIB_PATH} is missing; build it first "
+                "(python -c 'import __graft_entry__ as g; g.build()' or python decoder_attention_amd/build.py)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def exported_symbols():
+    return sorted(_SIGNATURES)
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_config(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype=QKRA_BF16, rms_eps: float = 1e-6,
+                rope_base: float = 1e6) -> QkraConfig:
+    if not isinstance(dtype, int):
+        import torch
+
+        dtype = {torch.bfloat16: QKRA_BF16, torch.float32: QKRA_FP32}[dtype]
+    return QkraConfig(int(num_q_heads), int(num_kv_heads), int(head_dim), int(dtype), float(rms_eps), 0,
+                      float(rope_base))
+
+
+# ---- the C ABI, one Python function per exported symbol -------------------
+
+def qknorm_rope_attn_prefill(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens,
+                             num_tokens: int, num_seqs: int, max_seqlen: int, k_cache, v_cache,
+                             cache_capacity: int, out, workspace, workspace_bytes: int, stream=None) -> int:
+    return lib().qknorm_rope_attn_prefill(
+        ctypes.byref(cfg), _ptr(qkv), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(positions), _ptr(cu_seqlens),
+        int(num_tokens), int(num_seqs), int(max_seqlen), _ptr(k_cache), _ptr(v_cache), int(cache_capacity),
+        _ptr(out), _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def qknorm_rope_attn_decode(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cache_lens,
+                            num_seqs: int, max_cache_len: int, k_cache, v_cache, cache_capacity: int, out,
+                            workspace, workspace_bytes: int, stream=None) -> int:
+    return lib().qknorm_rope_attn_decode(
+        ctypes.byref(cfg), _ptr(qkv), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(positions), _ptr(cache_lens),
+        int(num_seqs), int(max_cache_len), _ptr(k_cache), _ptr(v_cache), int(cache_capacity), _ptr(out),
+        _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def qknorm_rope_attn_workspace_bytes(cfg: QkraConfig, mode: int, n: int, max_len: int) -> int:
+    return int(lib().qknorm_rope_attn_workspace_bytes(ctypes.byref(cfg), int(mode), int(n), int(max_len)))
+
+
+def qknorm_rope_attn_status_string(status: int) -> str:
+    return lib().qknorm_rope_attn_status_string(int(status)).decode()
+
+
+def qknorm_rope_attn_last_hip_error() -> int:
+    return int(lib().qknorm_rope_attn_last_hip_error())
+
+
+def qknorm_rope_attn_version() -> int:
+    return int(lib().qknorm_rope_attn_version())
+
+
+def qknorm_rope_attn_set_kernel_timing(enable: bool) -> int:
+    return int(lib().qknorm_rope_attn_set_kernel_timing(1 if enable else 0))
+
+
+def qknorm_rope_attn_kernel_name(kernel_id: int) -> str:
+    return lib().qknorm_rope_attn_kernel_name(int(kernel_id)).decode()
+
+
+def qknorm_rope_attn_read_kernel_timing(max_kernels: int = 8):
+    """Returns {kernel name: (total ms, launches)} for kernels launched since the last read."""
+    ms = (ctypes.c_double * max_kernels)()
+    n = (ctypes.c_int64 * max_kernels)()
+    count = lib().qknorm_rope_attn_read_kernel_timing(ms, n, int(max_kernels))
+    if count < 0:
+        raise QkraError(-count, "read_kernel_timing")
+    return {qknorm_rope_attn_kernel_name(k): (ms[k], int(n[k])) for k in range(min(count, max_kernels)) if n[k]}
+
+
+def check(status: int, where: str = "") -> None:
+    if status != QKRA_OK:
+        raise QkraError(status, where)

@@ -1,0 +1,366 @@
+// C ABI of the attention library: host-side argument checks, workspace
+// sizing and the launch sequence of each call.  Nothing here allocates
+// device memory or synchronises the caller's stream.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/qknorm_rope_attn.h"
+#include "launch.h"
+
+namespace qkra {
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+size_t elem_size(int32_t dtype) { return dtype == QKRA_BF16 ? 2 : 4; }
+
+int32_t check_config(const qkra_config* cfg) {
+  if (cfg == nullptr) return QKRA_ERR_INVALID_ARGUMENT;
+  if (cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0) return QKRA_ERR_INVALID_ARGUMENT;
+  if (cfg->num_q_heads % cfg->num_kv_heads != 0) return QKRA_ERR_INVALID_ARGUMENT;
+  if (cfg->reserved != 0) return QKRA_ERR_INVALID_ARGUMENT;
+  if (!(cfg->rms_eps >= 0.0f) || !std::isfinite(cfg->rms_eps)) return QKRA_ERR_INVALID_ARGUMENT;
+  if (!(cfg->rope_base > 0.0) || !std::isfinite(cfg->rope_base)) return QKRA_ERR_INVALID_ARGUMENT;
+  if (cfg->head_dim != 64 && cfg->head_dim != 128) return QKRA_ERR_UNSUPPORTED;
+  if (cfg->dtype != QKRA_BF16 && cfg->dtype != QKRA_FP32) return QKRA_ERR_UNSUPPORTED;
+  // Keep every index inside 32-bit signed arithmetic where the kernels use it.
+  if (static_cast<long long>(cfg->num_q_heads + 2LL * cfg->num_kv_heads) * cfg->head_dim > (1LL << 24))
+    return QKRA_ERR_UNSUPPORTED;
+  return QKRA_OK;
+}
+
+size_t prefill_workspace(const qkra_config* cfg, int64_t num_tokens) {
+  return align_up(static_cast<size_t>(num_tokens) * cfg->num_q_heads * cfg->head_dim * elem_size(cfg->dtype));
+}
+
+size_t decode_q_bytes(const qkra_config* cfg, int64_t num_seqs) {
+  return align_up(static_cast<size_t>(num_seqs) * cfg->num_q_heads * cfg->head_dim * elem_size(cfg->dtype));
+}
+
+size_t decode_workspace(const qkra_config* cfg, int64_t num_seqs, int32_t max_cache_len) {
+  const size_t splits = static_cast<size_t>(decode_num_splits(max_cache_len));
+  return decode_q_bytes(cfg, num_seqs) +
+         align_up(static_cast<size_t>(num_seqs) * cfg->num_q_heads * splits * (cfg->head_dim + 2) * sizeof(float));
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---- per-kernel timing (benchmark instrumentation) ------------------------
+struct TimingRecord {
+  int kernel;
+  hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+bool g_timing_enabled = false;
+std::vector<TimingRecord> g_timing_records;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <typename Launch>
+hipError_t timed(int kernel, hipStream_t stream, Launch&& launch) {
+  bool enabled;
+  {
+    std::lock_guard<std::mutex> lock(g_timing_mu);
+    enabled = g_timing_enabled;
+  }
+  if (!enabled) return launch();
+  hipEvent_t start, stop;
+  {
+    std::lock_guard<std::mutex> lock(g_timing_mu);
+    start = take_event();
+    stop = take_event();
+  }
+  if (start == nullptr || stop == nullptr) return hipErrorOutOfMemory;
+  hipError_t err = hipEventRecord(start, stream);
+  if (err != hipSuccess) return err;
+  err = launch();
+  if (err != hipSuccess) return err;
+  err = hipEventRecord(stop, stream);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  g_timing_records.push_back(TimingRecord{kernel, start, stop});
+  return hipSuccess;
+}
+
+int32_t hip_status(hipError_t err) {
+  if (err == hipSuccess) return QKRA_OK;
+  g_last_hip_error = static_cast<int32_t>(err);
+  return QKRA_ERR_HIP;
+}
+
+double log2_of(double base) { return std::log2(base); }
+
+float softmax_scale_log2(int head_dim) {
+  return static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(head_dim)));
+}
+
+}  // namespace
+}  // namespace qkra
+
+using namespace qkra;
+
+extern "C" {
+
+QKRA_API size_t qknorm_rope_attn_workspace_bytes(const qkra_config* cfg, int32_t mode, int32_t n,
+                                                 int32_t max_len) {
+  if (check_config(cfg) != QKRA_OK || n < 0 || max_len < 0) return 0;
+  if (mode == QKRA_MODE_PREFILL) return prefill_workspace(cfg, n);
+  if (mode == QKRA_MODE_DECODE) return decode_workspace(cfg, n, max_len);
+  return 0;
+}
+
+QKRA_API const char* qknorm_rope_attn_status_string(int32_t status) {
+  switch (status) {
+    case QKRA_OK: return "ok";
+    case QKRA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case QKRA_ERR_UNSUPPORTED: return "unsupported head_dim or dtype";
+    case QKRA_ERR_CAPACITY: return "cache capacity too small";
+    case QKRA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case QKRA_ERR_ALIASING: return "output or cache buffers overlap another buffer";
+    case QKRA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+QKRA_API int32_t qknorm_rope_attn_last_hip_error(void) { return g_last_hip_error; }
+
+QKRA_API int32_t qknorm_rope_attn_version(void) { return 100; }
+
+QKRA_API int32_t qknorm_rope_attn_prefill(const qkra_config* cfg, const void* qkv, const void* q_norm_weight,
+                                          const void* k_norm_weight, const int32_t* positions,
+                                          const int32_t* cu_seqlens, int32_t num_tokens, int32_t num_seqs,
+                                          int32_t max_seqlen, void* k_cache, void* v_cache,
+                                          int32_t cache_capacity, void* out, void* workspace,
+                                          size_t workspace_bytes, void* hip_stream) {
+  const int32_t cs = check_config(cfg);
+  if (cs != QKRA_OK) return cs;
+  if (num_tokens < 0 || num_seqs < 0 || max_seqlen < 0 || cache_capacity < 0) return QKRA_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return QKRA_OK;
+  if (num_seqs == 0 || max_seqlen == 0 || max_seqlen > num_tokens) return QKRA_ERR_INVALID_ARGUMENT;
+  if (static_cast<long long>(max_seqlen) * num_seqs < num_tokens) return QKRA_ERR_INVALID_ARGUMENT;
+  if (cache_capacity < max_seqlen) return QKRA_ERR_CAPACITY;
+  if (!qkv || !q_norm_weight || !k_norm_weight || !positions || !cu_seqlens || !k_cache || !v_cache || !out)
+    return QKRA_ERR_INVALID_ARGUMENT;
+  const size_t need = prefill_workspace(cfg, num_tokens);
+  if (workspace_bytes < need) return QKRA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return QKRA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(qkv) || !aligned16(q_norm_weight) || !aligned16(k_norm_weight) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(out) || !aligned16(workspace))
+    return QKRA_ERR_INVALID_ARGUMENT;
+
+  const size_t es = elem_size(cfg->dtype);
+  const size_t hq = cfg->num_q_heads, hkv = cfg->num_kv_heads, d = cfg->head_dim;
+  const Range r_qkv = range_of(qkv, num_tokens * (hq + 2 * hkv) * d * es);
+  const Range r_out = range_of(out, num_tokens * hq * d * es);
+  const size_t cache_bytes = static_cast<size_t>(num_seqs) * hkv * cache_capacity * d * es;
+  const Range r_k = range_of(k_cache, cache_bytes), r_v = range_of(v_cache, cache_bytes);
+  const Range r_ws = range_of(workspace, need);
+  const Range r_wq = range_of(q_norm_weight, d * es), r_wk = range_of(k_norm_weight, d * es);
+  const Range r_pos = range_of(positions, num_tokens * 4ull), r_cu = range_of(cu_seqlens, (num_seqs + 1ull) * 4);
+  for (Range w : {r_out, r_k, r_v, r_ws})
+    for (Range r : {r_qkv, r_wq, r_wk, r_pos, r_cu})
+      if (overlap(w, r)) return QKRA_ERR_ALIASING;
+  if (overlap(r_out, r_k) || overlap(r_out, r_v) || overlap(r_out, r_ws) || overlap(r_k, r_v) ||
+      overlap(r_k, r_ws) || overlap(r_v, r_ws))
+    return QKRA_ERR_ALIASING;
+
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  QkNormRopeArgs ka{};
+  ka.qkv = qkv;
+  ka.q_norm_weight = q_norm_weight;
+  ka.k_norm_weight = k_norm_weight;
+  ka.positions = positions;
+  ka.seq_info = cu_seqlens;
+  ka.decode_mode = 0;
+  ka.num_rows = num_tokens;
+  ka.num_seqs = num_seqs;
+  ka.num_q_heads = cfg->num_q_heads;
+  ka.num_kv_heads = cfg->num_kv_heads;
+  ka.head_dim = cfg->head_dim;
+  ka.dtype = cfg->dtype;
+  ka.cache_capacity = cache_capacity;
+  ka.rms_eps = cfg->rms_eps;
+  ka.log2_rope_base = log2_of(cfg->rope_base);
+  ka.q_out = workspace;
+  ka.k_cache = k_cache;
+  ka.v_cache = v_cache;
+  hipError_t err = timed(kKernelQkNormRopePrefill, stream, [&] { return launch_qknorm_rope(ka, stream); });
+  if (err != hipSuccess) return hip_status(err);
+
+  PrefillAttnArgs pa{};
+  pa.q = workspace;
+  pa.k_cache = k_cache;
+  pa.v_cache = v_cache;
+  pa.cu_seqlens = cu_seqlens;
+  pa.out = out;
+  pa.num_q_heads = cfg->num_q_heads;
+  pa.num_kv_heads = cfg->num_kv_heads;
+  pa.head_dim = cfg->head_dim;
+  pa.cache_capacity = cache_capacity;
+  pa.num_seqs = num_seqs;
+  pa.max_seqlen = max_seqlen;
+  pa.scale_log2 = softmax_scale_log2(cfg->head_dim);
+  if (cfg->dtype == QKRA_BF16)
+    err = timed(kKernelPrefillMfma, stream, [&] { return launch_prefill_attn_bf16(pa, stream); });
+  else
+    err = timed(kKernelPrefillFp32, stream, [&] { return launch_prefill_attn_fp32(pa, stream); });
+  return hip_status(err);
+}
+
+QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv, const void* q_norm_weight,
+                                         const void* k_norm_weight, const int32_t* positions,
+                                         const int32_t* cache_lens, int32_t num_seqs, int32_t max_cache_len,
+                                         void* k_cache, void* v_cache, int32_t cache_capacity, void* out,
+                                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+  const int32_t cs = check_config(cfg);
+  if (cs != QKRA_OK) return cs;
+  if (num_seqs < 0 || max_cache_len < 0 || cache_capacity < 0) return QKRA_ERR_INVALID_ARGUMENT;
+  if (num_seqs == 0) return QKRA_OK;
+  if (static_cast<long long>(cache_capacity) < static_cast<long long>(max_cache_len) + 1) return QKRA_ERR_CAPACITY;
+  if (!qkv || !q_norm_weight || !k_norm_weight || !positions || !cache_lens || !k_cache || !v_cache || !out)
+    return QKRA_ERR_INVALID_ARGUMENT;
+  const size_t need = decode_workspace(cfg, num_seqs, max_cache_len);
+  if (workspace_bytes < need) return QKRA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return QKRA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(qkv) || !aligned16(q_norm_weight) || !aligned16(k_norm_weight) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(out) || !aligned16(workspace))
+    return QKRA_ERR_INVALID_ARGUMENT;
+
+  const size_t es = elem_size(cfg->dtype);
+  const size_t hq = cfg->num_q_heads, hkv = cfg->num_kv_heads, d = cfg->head_dim;
+  const Range r_qkv = range_of(qkv, num_seqs * (hq + 2 * hkv) * d * es);
+  const Range r_out = range_of(out, num_seqs * hq * d * es);
+  const size_t cache_bytes = static_cast<size_t>(num_seqs) * hkv * cache_capacity * d * es;
+  const Range r_k = range_of(k_cache, cache_bytes), r_v = range_of(v_cache, cache_bytes);
+  const Range r_ws = range_of(workspace, need);
+  const Range r_wq = range_of(q_norm_weight, d * es), r_wk = range_of(k_norm_weight, d * es);
+  const Range r_pos = range_of(positions, num_seqs * 4ull), r_len = range_of(cache_lens, num_seqs * 4ull);
+  for (Range w : {r_out, r_k, r_v, r_ws})
+    for (Range r : {r_qkv, r_wq, r_wk, r_pos, r_len})
+      if (overlap(w, r)) return QKRA_ERR_ALIASING;
+  if (overlap(r_out, r_k) || overlap(r_out, r_v) || overlap(r_out, r_ws) || overlap(r_k, r_v) ||
+      overlap(r_k, r_ws) || overlap(r_v, r_ws))
+    return QKRA_ERR_ALIASING;
+
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  QkNormRopeArgs ka{};
+  ka.qkv = qkv;
+  ka.q_norm_weight = q_norm_weight;
+  ka.k_norm_weight = k_norm_weight;
+  ka.positions = positions;
+  ka.seq_info = cache_lens;
+  ka.decode_mode = 1;
+  ka.num_rows = num_seqs;
+  ka.num_seqs = num_seqs;
+  ka.num_q_heads = cfg->num_q_heads;
+  ka.num_kv_heads = cfg->num_kv_heads;
+  ka.head_dim = cfg->head_dim;
+  ka.dtype = cfg->dtype;
+  ka.cache_capacity = cache_capacity;
+  ka.rms_eps = cfg->rms_eps;
+  ka.log2_rope_base = log2_of(cfg->rope_base);
+  ka.q_out = workspace;
+  ka.k_cache = k_cache;
+  ka.v_cache = v_cache;
+  hipError_t err = timed(kKernelQkNormRopeDecode, stream, [&] { return launch_qknorm_rope(ka, stream); });
+  if (err != hipSuccess) return hip_status(err);
+
+  DecodeAttnArgs da{};
+  da.q = workspace;
+  da.k_cache = k_cache;
+  da.v_cache = v_cache;
+  da.cache_lens = cache_lens;
+  da.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_q_bytes(cfg, num_seqs));
+  da.out = out;
+  da.num_q_heads = cfg->num_q_heads;
+  da.num_kv_heads = cfg->num_kv_heads;
+  da.head_dim = cfg->head_dim;
+  da.dtype = cfg->dtype;
+  da.cache_capacity = cache_capacity;
+  da.num_seqs = num_seqs;
+  da.num_splits = decode_num_splits(max_cache_len);
+  da.scale_log2 = softmax_scale_log2(cfg->head_dim);
+  err = timed(kKernelDecodeSplit, stream, [&] { return launch_decode_split(da, stream); });
+  if (err != hipSuccess) return hip_status(err);
+  err = timed(kKernelDecodeCombine, stream, [&] { return launch_decode_combine(da, stream); });
+  return hip_status(err);
+}
+
+QKRA_API int32_t qknorm_rope_attn_set_kernel_timing(int32_t enable) {
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  g_timing_enabled = enable != 0;
+  return QKRA_OK;
+}
+
+QKRA_API int32_t qknorm_rope_attn_read_kernel_timing(double* ms_total, int64_t* launches, int32_t max_kernels) {
+  std::vector<TimingRecord> records;
+  {
+    std::lock_guard<std::mutex> lock(g_timing_mu);
+    records.swap(g_timing_records);
+  }
+  for (int k = 0; k < max_kernels; ++k) {
+    if (ms_total) ms_total[k] = 0.0;
+    if (launches) launches[k] = 0;
+  }
+  int32_t status = kNumKernels;
+  for (const TimingRecord& r : records) {
+    float ms = 0.f;
+    hipError_t err = hipEventSynchronize(r.stop);
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (err != hipSuccess) {
+      g_last_hip_error = static_cast<int32_t>(err);
+      status = -QKRA_ERR_HIP;
+    } else if (r.kernel < max_kernels) {
+      if (ms_total) ms_total[r.kernel] += ms;
+      if (launches) launches[r.kernel] += 1;
+    }
+  }
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  for (const TimingRecord& r : records) {
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  return status;
+}
+
+QKRA_API const char* qknorm_rope_attn_kernel_name(int32_t kernel_id) {
+  switch (kernel_id) {
+    case kKernelQkNormRopePrefill: return "qknorm_rope_kv_prefill";
+    case kKernelQkNormRopeDecode: return "qknorm_rope_kv_decode";
+    case kKernelPrefillMfma: return "prefill_attn_mfma_bf16";
+    case kKernelPrefillFp32: return "prefill_attn_fp32";
+    case kKernelDecodeSplit: return "decode_attn_split";
+    case kKernelDecodeCombine: return "decode_attn_combine";
+    default: return "unknown";
+  }
+}
+
+}  // extern "C"

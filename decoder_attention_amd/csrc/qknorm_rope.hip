@@ -1,0 +1,177 @@
+// Kernel 1: fused per-head Q/K RMSNorm + rotate-half RoPE + K/V cache write.
+//
+// Follows zero-to-sglang "Chapter 3 Forward Pass and Generation (Code
+// Walkthrough)", section 3.3: the packed projection is split into Q, K and V
+// heads, each Q and K head is RMS-normalised over its last dimension with a
+// learned weight, Q and K are rotated at the token's position, V is left as it
+// is.  The cache write follows the concept chapter, section 4.1 (prefill keeps
+// every prompt token's K and V) and jq-wei "transformer basics", "Prefill vs
+// Decode" (a decode step appends one entry).
+//
+// Layout of the work: one workgroup per token row.  The D/2 rotation angles
+// of the row are formed once in fp64 (position * base^(-2i/D), then sin/cos)
+// and kept in LDS, so positions up to tens of thousands keep full fp32
+// accuracy in cos/sin.  Each head row is handled by D/8 lanes: a lane holds 4
+// elements of the first half and the 4 matching elements of the second half,
+// so every rotate-half pair stays inside one lane and the rotation needs no
+// cross-lane traffic; only the sum of squares is reduced across the D/8 lanes.
+// Loads and stores are 8 B (bf16) or 16 B (fp32) per lane, contiguous across
+// the lanes of a head.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace qkra {
+namespace {
+
+template <typename T> struct Raw4;
+template <> struct Raw4<bf16> { typedef uint2 type; };
+template <> struct Raw4<float> { typedef uint4 type; };
+
+__device__ __forceinline__ void unpack4(uint2 r, float x[4]) {
+  x[0] = bf16_lo_to_f32(r.x); x[1] = bf16_hi_to_f32(r.x);
+  x[2] = bf16_lo_to_f32(r.y); x[3] = bf16_hi_to_f32(r.y);
+}
+__device__ __forceinline__ void unpack4(uint4 r, float x[4]) {
+  x[0] = __uint_as_float(r.x); x[1] = __uint_as_float(r.y);
+  x[2] = __uint_as_float(r.z); x[3] = __uint_as_float(r.w);
+}
+__device__ __forceinline__ void pack4(const float y[4], uint2* r) {
+  r->x = pack_bf16x2(y[0], y[1]);
+  r->y = pack_bf16x2(y[2], y[3]);
+}
+__device__ __forceinline__ void pack4(const float y[4], uint4* r) {
+  r->x = __float_as_uint(y[0]); r->y = __float_as_uint(y[1]);
+  r->z = __float_as_uint(y[2]); r->w = __float_as_uint(y[3]);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
+    const T* __restrict__ qkv, const T* __restrict__ q_weight, const T* __restrict__ k_weight,
+    const int32_t* __restrict__ positions, const int32_t* __restrict__ seq_info, int decode_mode,
+    int num_seqs, int num_q_heads, int num_kv_heads, int cache_capacity, float eps,
+    double log2_base, T* __restrict__ q_out, T* __restrict__ k_cache, T* __restrict__ v_cache) {
+  using Raw = typename Raw4<T>::type;
+  constexpr int HALF = D / 2;
+  constexpr int LPH = HALF / 4;  // lanes per head row
+  constexpr int HPW = 64 / LPH;  // head rows per wavefront pass
+  __shared__ float s_cos[HALF];
+  __shared__ float s_sin[HALF];
+
+  const int row_id = blockIdx.x;
+  int req, slot;
+  if (decode_mode) {
+    req = row_id;
+    slot = seq_info[row_id];
+  } else {
+    // Request r with cu[r] <= row < cu[r+1]; empty requests are skipped over.
+    int lo = 0, hi = num_seqs;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (seq_info[mid] <= row_id) lo = mid; else hi = mid;
+    }
+    req = lo;
+    slot = row_id - seq_info[lo];
+  }
+  // Rows outside the caller's contract (slot past the cache) write no cache entry.
+  const bool slot_ok = slot >= 0 && slot < cache_capacity;
+
+  const double pos = static_cast<double>(positions[row_id]);
+  for (int i = threadIdx.x; i < HALF; i += blockDim.x) {
+    const double theta = exp2(-static_cast<double>(2 * i) / static_cast<double>(D) * log2_base);
+    double sn, cs;
+    sincos(pos * theta, &sn, &cs);
+    s_cos[i] = static_cast<float>(cs);
+    s_sin[i] = static_cast<float>(sn);
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int sub = lane % LPH;
+  const int hslot = lane / LPH;
+  const int i0 = sub * 4;
+
+  float cs[4], sn[4], wq1[4], wq2[4], wk1[4], wk2[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    cs[e] = s_cos[i0 + e];
+    sn[e] = s_sin[i0 + e];
+  }
+  unpack4(*reinterpret_cast<const Raw*>(q_weight + i0), wq1);
+  unpack4(*reinterpret_cast<const Raw*>(q_weight + HALF + i0), wq2);
+  unpack4(*reinterpret_cast<const Raw*>(k_weight + i0), wk1);
+  unpack4(*reinterpret_cast<const Raw*>(k_weight + HALF + i0), wk2);
+
+  const int heads = num_q_heads + 2 * num_kv_heads;
+  const T* row = qkv + static_cast<size_t>(row_id) * heads * D;
+  for (int hb = wave * HPW; hb < heads; hb += nwaves * HPW) {
+    const int head = hb + hslot;
+    const bool active = head < heads;
+    Raw r1 = {}, r2 = {};
+    if (active) {
+      r1 = *reinterpret_cast<const Raw*>(row + head * D + i0);
+      r2 = *reinterpret_cast<const Raw*>(row + head * D + HALF + i0);
+    }
+    float x1[4], x2[4];
+    unpack4(r1, x1);
+    unpack4(r2, x2);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
+#pragma unroll
+    for (int m = 1; m < LPH; m <<= 1) ss += xor_shuffle(ss, m);
+    if (!active) continue;
+
+    if (head >= num_q_heads + num_kv_heads) {  // V head: bit copy into the cache
+      if (!slot_ok) continue;
+      const int g = head - num_q_heads - num_kv_heads;
+      T* dst = v_cache + ((static_cast<size_t>(req) * num_kv_heads + g) * cache_capacity + slot) * D;
+      *reinterpret_cast<Raw*>(dst + i0) = r1;
+      *reinterpret_cast<Raw*>(dst + HALF + i0) = r2;
+      continue;
+    }
+    const bool is_q = head < num_q_heads;
+    if (!is_q && !slot_ok) continue;
+    const float inv_rms = rsqrtf(ss * (1.0f / D) + eps);
+    float y1[4], y2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = x1[e] * inv_rms * (is_q ? wq1[e] : wk1[e]);
+      const float b = x2[e] * inv_rms * (is_q ? wq2[e] : wk2[e]);
+      y1[e] = a * cs[e] - b * sn[e];
+      y2[e] = b * cs[e] + a * sn[e];
+    }
+    T* dst = is_q ? q_out + (static_cast<size_t>(row_id) * num_q_heads + head) * D
+                  : k_cache + ((static_cast<size_t>(req) * num_kv_heads + (head - num_q_heads)) *
+                                   cache_capacity + slot) * D;
+    Raw o1, o2;
+    pack4(y1, &o1);
+    pack4(y2, &o2);
+    *reinterpret_cast<Raw*>(dst + i0) = o1;
+    *reinterpret_cast<Raw*>(dst + HALF + i0) = o2;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const QkNormRopeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((qknorm_rope_kv_kernel<T, D>), dim3(a.num_rows), dim3(256), 0, stream,
+                     static_cast<const T*>(a.qkv), static_cast<const T*>(a.q_norm_weight),
+                     static_cast<const T*>(a.k_norm_weight), a.positions, a.seq_info, a.decode_mode,
+                     a.num_seqs, a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.rms_eps,
+                     a.log2_rope_base, static_cast<T*>(a.q_out), static_cast<T*>(a.k_cache),
+                     static_cast<T*>(a.v_cache));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qknorm_rope(const QkNormRopeArgs& a, hipStream_t stream) {
+  const bool bf = a.dtype == 0;
+  if (a.head_dim == 128) return bf ? launch_typed<bf16, 128>(a, stream) : launch_typed<float, 128>(a, stream);
+  if (a.head_dim == 64) return bf ? launch_typed<bf16, 64>(a, stream) : launch_typed<float, 64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qkra

@@ -1,0 +1,181 @@
+/*
+ * qknorm_rope_attn -- QK-RMSNorm + RoPE + causal grouped-query attention for
+ * one decoder layer, prefill and decode, on AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute (zero-to-sglang, "Chapter 3 Forward Pass and
+ * Generation (Code Walkthrough)", section 3.3 "QKV, RoPE, and causal
+ * attention"; jq-wei, "transformer basics", "Attention calculation: part 1"):
+ *
+ *   for every token row n of the packed projection qkv[N, (Hq + 2*Hkv) * D]
+ *     q_h  = columns [h*D, (h+1)*D)                     (h < Hq)
+ *     k_g  = columns [(Hq+g)*D, (Hq+g+1)*D)             (g < Hkv)
+ *     v_g  = columns [(Hq+Hkv+g)*D, (Hq+Hkv+g+1)*D)
+ *     q~_h = RoPE(RMSNorm(q_h) * w_q, pos[n]);  k~_g = RoPE(RMSNorm(k_g) * w_k, pos[n])
+ *       RMSNorm(x) = x / sqrt(mean(x^2) + eps)
+ *       RoPE pairs element i with i + D/2 and turns it by pos * base^(-2i/D)
+ *     out[n, h*D:(h+1)*D] = sum_t softmax_t(q~_h . k~_{h/G}(t) / sqrt(D)) v_{h/G}(t)
+ *       over the request's keys t = 0..i (i = the token's index in its request),
+ *       G = Hq / Hkv (query head h reads KV head floor(h / G)).
+ *
+ * Prefill processes whole requests packed back to back and writes every
+ * token's K~ and V to the request's cache (concept chapter "Chapter 3 Forward
+ * Pass and Generation", section 4.1).  Decode takes one new token per request,
+ * appends its K~ and V at slot L_b, then attends over slots 0..L_b (section 4.2;
+ * "transformer basics", "Prefill vs Decode": the cache grows from 12 to 13
+ * entries before attention runs).
+ *
+ * Conventions for every call
+ *   - Every pointer argument except `cfg` and `workspace_bytes`-style scalars is
+ *     a DEVICE pointer; all device buffers are owned by the caller, must stay
+ *     alive until the enqueued work completes, and are never freed or kept by
+ *     the library.
+ *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the default
+ *     stream).  Calls return without synchronising.  They allocate no device
+ *     memory and are reentrant.
+ *   - Element type of qkv, both norm weights, both caches, out and the Q~ part
+ *     of the workspace is `cfg->dtype` (bf16 or fp32).  Accumulation is fp32.
+ *   - Cache layout (exact): element (b, g, s, d) of a cache lives at
+ *       ((b * Hkv + g) * cache_capacity + s) * D + d
+ *     K holds post-norm post-RoPE values rounded to the dtype, V holds the
+ *     input bits unchanged.  Slots a call does not write keep their contents.
+ *   - Errors: the return value is QKRA_OK or one of the QKRA_ERR_* codes below;
+ *     argument checks happen on the host before anything is enqueued, so an
+ *     error return means nothing was launched (except QKRA_ERR_HIP, where a
+ *     launch failed; qknorm_rope_attn_last_hip_error() then gives the hipError_t).
+ *     No C++ exception crosses this interface.
+ *   - Contents of device arrays (monotone cu_seqlens, positions >= 0,
+ *     cache_lens[b] + 1 <= cache_capacity) are the caller's contract; they are
+ *     not checked, and violating them is undefined behaviour.
+ */
+#ifndef QKNORM_ROPE_ATTN_H
+#define QKNORM_ROPE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QKRA_API __attribute__((visibility("default")))
+
+/* Element types. */
+#define QKRA_BF16 0
+#define QKRA_FP32 1
+
+/* Status codes. */
+#define QKRA_OK 0
+#define QKRA_ERR_INVALID_ARGUMENT 1   /* Hq % Hkv != 0, negative size, null pointer with work to do, bad eps/base */
+#define QKRA_ERR_UNSUPPORTED 2        /* head_dim not 64 or 128, unknown dtype */
+#define QKRA_ERR_CAPACITY 3           /* cache_capacity too small for the longest request / new token */
+#define QKRA_ERR_WORKSPACE_TOO_SMALL 4
+#define QKRA_ERR_ALIASING 5           /* out overlaps an input, a cache or the workspace, or buffers overlap each other */
+#define QKRA_ERR_HIP 6                /* a HIP launch or runtime call failed */
+
+/* Workspace query modes. */
+#define QKRA_MODE_PREFILL 0
+#define QKRA_MODE_DECODE 1
+
+/* Layer configuration, passed by pointer (host memory) to every call. */
+typedef struct qkra_config {
+  int32_t num_q_heads;   /* Hq > 0 */
+  int32_t num_kv_heads;  /* Hkv > 0, Hq % Hkv == 0 (whole groups of query heads share a KV head) */
+  int32_t head_dim;      /* D: 64 or 128; independent of the hidden size */
+  int32_t dtype;         /* QKRA_BF16 or QKRA_FP32 */
+  float rms_eps;         /* >= 0, added to mean(x^2) inside the square root */
+  int32_t reserved;      /* must be 0 */
+  double rope_base;      /* > 0, e.g. 1e4 or 1e6 */
+} qkra_config;
+
+/*
+ * Prefill of `num_seqs` requests packed into `num_tokens` rows.
+ *
+ *   qkv            [num_tokens, (Hq+2Hkv)*D], row-major, read-only.
+ *   q_norm_weight  [D], k_norm_weight [D], read-only.
+ *   positions      int32 [num_tokens]: RoPE position of each row (only the angle
+ *                  depends on it; the cache slot is the in-request index).
+ *   cu_seqlens     int32 [num_seqs+1]: cu[0] = 0, non-decreasing, cu[num_seqs] =
+ *                  num_tokens; request r owns rows cu[r] .. cu[r+1]-1.  Zero-length
+ *                  requests are allowed and produce nothing.
+ *   max_seqlen     host copy of max_r (cu[r+1]-cu[r]); used to size the launch.
+ *   k_cache, v_cache [num_seqs, Hkv, cache_capacity, D]; token j of request r
+ *                  is written to slot j; slots >= the request's length are not
+ *                  touched.  cache_capacity >= max_seqlen.
+ *   out            [num_tokens, Hq*D], write-only; must not overlap any other buffer.
+ *   workspace      device scratch of at least
+ *                  qknorm_rope_attn_workspace_bytes(cfg, QKRA_MODE_PREFILL,
+ *                  num_tokens, max_seqlen) bytes.  On return (after the stream
+ *                  work completes) its first num_tokens*Hq*D elements hold
+ *                  q~ as [num_tokens, Hq, D] in the dtype.
+ * num_tokens == 0 is a no-op returning QKRA_OK.
+ */
+QKRA_API int32_t qknorm_rope_attn_prefill(const qkra_config* cfg, const void* qkv,
+                                          const void* q_norm_weight, const void* k_norm_weight,
+                                          const int32_t* positions, const int32_t* cu_seqlens,
+                                          int32_t num_tokens, int32_t num_seqs, int32_t max_seqlen,
+                                          void* k_cache, void* v_cache, int32_t cache_capacity,
+                                          void* out, void* workspace, size_t workspace_bytes,
+                                          void* hip_stream);
+
+/*
+ * Decode step: one new token per request.
+ *
+ *   qkv            [num_seqs, (Hq+2Hkv)*D]: the new token's projection row.
+ *   positions      int32 [num_seqs]: RoPE position of the new token.
+ *   cache_lens     int32 [num_seqs]: L_b, the number of valid cache entries
+ *                  before this step.  The new token's k~ and v are written to
+ *                  slot L_b, then its query attends over slots 0..L_b.  The
+ *                  library does not update cache_lens.
+ *   max_cache_len  host copy of max_b L_b; cache_capacity >= max_cache_len + 1.
+ *   k_cache, v_cache [num_seqs, Hkv, cache_capacity, D], read and written.
+ *   out            [num_seqs, Hq*D], write-only.
+ *   workspace      at least qknorm_rope_attn_workspace_bytes(cfg,
+ *                  QKRA_MODE_DECODE, num_seqs, max_cache_len) bytes: q~ as
+ *                  [num_seqs, Hq, D] in the dtype, then fp32 split partials.
+ * num_seqs == 0 is a no-op returning QKRA_OK.
+ */
+QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv,
+                                         const void* q_norm_weight, const void* k_norm_weight,
+                                         const int32_t* positions, const int32_t* cache_lens,
+                                         int32_t num_seqs, int32_t max_cache_len,
+                                         void* k_cache, void* v_cache, int32_t cache_capacity,
+                                         void* out, void* workspace, size_t workspace_bytes,
+                                         void* hip_stream);
+
+/*
+ * Workspace size in bytes for a call (0 when the configuration is invalid).
+ * mode QKRA_MODE_PREFILL: n = num_tokens, max_len = max_seqlen.
+ * mode QKRA_MODE_DECODE:  n = num_seqs,   max_len = max_cache_len.
+ * Pure host computation; needs no GPU.
+ */
+QKRA_API size_t qknorm_rope_attn_workspace_bytes(const qkra_config* cfg, int32_t mode, int32_t n,
+                                                 int32_t max_len);
+
+/* Static string naming a status code (never NULL). */
+QKRA_API const char* qknorm_rope_attn_status_string(int32_t status);
+
+/* hipError_t of the most recent QKRA_ERR_HIP on the calling thread (0 if none). */
+QKRA_API int32_t qknorm_rope_attn_last_hip_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+QKRA_API int32_t qknorm_rope_attn_version(void);
+
+/*
+ * Per-kernel timing, for benchmarks.  While enabled, every kernel launch is
+ * bracketed by two hipEvents recorded on the launch stream.
+ * qknorm_rope_attn_read_kernel_timing() waits for those events, writes for each
+ * kernel id k < max_kernels the summed duration in milliseconds (ms_total[k])
+ * and the number of launches (launches[k]), clears the record and returns the
+ * number of kernel ids (or a negative QKRA_ERR_* on failure).  Kernel ids are
+ * named by qknorm_rope_attn_kernel_name().  Enabling/disabling is process-wide.
+ */
+QKRA_API int32_t qknorm_rope_attn_set_kernel_timing(int32_t enable);
+QKRA_API int32_t qknorm_rope_attn_read_kernel_timing(double* ms_total, int64_t* launches,
+                                                     int32_t max_kernels);
+QKRA_API const char* qknorm_rope_attn_kernel_name(int32_t kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QKNORM_ROPE_ATTN_H */

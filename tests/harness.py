@@ -1,0 +1,130 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C ABI,
+run the oracle on the same seeded inputs, compare."""
+
+from __future__ import annotations
+
+import sys
+from typing import Dict, Iterable, Optional
+
+import numpy as np
+import torch
+
+import decoder_attention_amd as da
+import oracle
+
+BF16_TOL = 2e-2   # max-abs error bound for bf16 inputs/outputs (fp32 accumulation)
+FP32_TOL = 1e-4   # max-abs error bound in fp32 mode
+
+
+def tol_for(dtype) -> float:
+    return BF16_TOL if dtype == torch.bfloat16 else FP32_TOL
+
+
+def note(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def cfg_of(heads, dtype) -> da.QkraConfig:
+    return da.make_config(heads.num_q_heads, heads.num_kv_heads, heads.head_dim, dtype, heads.rms_eps,
+                          heads.rope_base)
+
+
+def layer_kw(heads) -> dict:
+    return dict(num_q_heads=heads.num_q_heads, num_kv_heads=heads.num_kv_heads, head_dim=heads.head_dim,
+                rms_eps=heads.rms_eps, rope_base=heads.rope_base)
+
+
+def run_prefill(p) -> Dict[str, torch.Tensor]:
+    """HIP prefill on PrefillInputs (device tensors); caches are updated in place."""
+    cfg = cfg_of(p.heads, p.qkv.dtype)
+    out, ws = da.prefill(cfg, p.qkv, p.q_norm_weight, p.k_norm_weight, p.positions, p.cu_seqlens,
+                         p.max_seqlen, p.k_cache, p.v_cache)
+    torch.cuda.synchronize()
+    n, h = p.num_tokens, p.heads
+    q_tilde = ws[: n * h.num_q_heads * h.head_dim * p.qkv.element_size()].view(p.qkv.dtype)
+    return {"out": out, "q_tilde": q_tilde.view(n, h.num_q_heads, h.head_dim)}
+
+
+def run_decode(d, k_cache=None, v_cache=None) -> Dict[str, torch.Tensor]:
+    cfg = cfg_of(d.heads, d.qkv.dtype)
+    kc = d.k_cache if k_cache is None else k_cache
+    vc = d.v_cache if v_cache is None else v_cache
+    out, ws = da.decode(cfg, d.qkv, d.q_norm_weight, d.k_norm_weight, d.positions, d.cache_lens,
+                        d.max_cache_len, kc, vc)
+    torch.cuda.synchronize()
+    return {"out": out}
+
+
+def oracle_prefill(p, init_k=None, init_v=None):
+    return oracle.prefill(f64(p.qkv), f64(p.q_norm_weight), f64(p.k_norm_weight), p.positions.cpu().numpy(),
+                          p.cu_seqlens.cpu().numpy(), cache_capacity=p.cache_capacity,
+                          k_cache=init_k, v_cache=init_v, **layer_kw(p.heads))
+
+
+def max_abs(got: np.ndarray, want: np.ndarray) -> float:
+    if got.size == 0:
+        return 0.0
+    return float(np.max(np.abs(got - want)))
+
+
+def assert_close(got: np.ndarray, want: np.ndarray, tol: float, what: str) -> float:
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values in the HIP result"
+    err = max_abs(got, want)
+    if err > tol:
+        idx = np.unravel_index(np.argmax(np.abs(got - want)), got.shape)
+        raise AssertionError(f"{what}: max-abs error {err:.3e} > {tol:.1e} at {idx}: "
+                             f"got {got[idx]!r} want {want[idx]!r}")
+    return err
+
+
+def bits(t: torch.Tensor) -> torch.Tensor:
+    """Raw bit patterns of a tensor (exact comparisons, NaN payloads included)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16)
+    if t.dtype == torch.float32:
+        return t.view(torch.int32)
+    raise TypeError(t.dtype)
+
+
+def check_prefill_caches(p, k_before: torch.Tensor, v_before: torch.Tensor, ref: dict, tol: float) -> None:
+    """V cache equals the input V bits; K cache matches the oracle's k~; untouched slots keep their bits."""
+    h = p.heads
+    hq, hkv, d = h.num_q_heads, h.num_kv_heads, h.head_dim
+    cu = p.cu_seqlens.cpu().tolist()
+    v_in = p.qkv[:, (hq + hkv) * d:].reshape(-1, hkv, d)
+    kb, vb = bits(p.k_cache), bits(p.v_cache)
+    kb0, vb0 = bits(k_before), bits(v_before)
+    for r in range(p.num_seqs):
+        lo, hi = cu[r], cu[r + 1]
+        t = hi - lo
+        if t:
+            assert torch.equal(vb[r, :, :t], bits(v_in[lo:hi].permute(1, 0, 2).contiguous())), f"V cache request {r}"
+            got = f64(p.k_cache[r, :, :t])
+            assert_close(got, np.transpose(ref["k_tilde"][lo:hi], (1, 0, 2)), tol, f"K cache request {r}")
+        assert torch.equal(kb[r, :, t:], kb0[r, :, t:]), f"K cache slots >= {t} of request {r} were written"
+        assert torch.equal(vb[r, :, t:], vb0[r, :, t:]), f"V cache slots >= {t} of request {r} were written"
+
+
+def sample_tokens(cu: Iterable[int], per_request: int, seed: int, tile: int = 64) -> list:
+    """Rows 0, 1, the last, tile edges and random ones of every request."""
+    rng = np.random.default_rng(seed)
+    cu = list(cu)
+    rows = set()
+    for r in range(len(cu) - 1):
+        lo, hi = cu[r], cu[r + 1]
+        t = hi - lo
+        if t == 0:
+            continue
+        for i in (0, 1, t - 1, t - 2):
+            if 0 <= i < t:
+                rows.add(lo + i)
+        for e in range(tile, t, tile * max(1, t // (tile * 8))):
+            rows.update(x for x in (lo + e - 1, lo + e) if lo <= x < hi)
+        rows.update(int(lo + x) for x in rng.integers(0, t, size=per_request))
+    return sorted(rows)

@@ -1,0 +1,159 @@
+"""The C ABI on the host: exported symbols, status strings, workspace sizes and
+argument checks.  Every call here is rejected (or is a no-op) before any HIP
+work is enqueued, so these run without a GPU; the pointers are placeholders
+that are never dereferenced."""
+
+import ctypes
+import pathlib
+import re
+
+import pytest
+
+import decoder_attention_amd as da
+
+HEADER = pathlib.Path(__file__).resolve().parents[1] / "include" / "qknorm_rope_attn.h"
+
+
+def declared_symbols():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"QKRA_API\s+[\w\s\*]*?\b(qknorm_rope_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_two_entry_points():
+    names = declared_symbols()
+    assert "qknorm_rope_attn_prefill" in names and "qknorm_rope_attn_decode" in names
+    assert len(names) >= 8
+
+
+def test_library_exports_every_declared_symbol():
+    lib = da.lib()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+    assert sorted(da.exported_symbols()) == declared_symbols()
+
+
+def test_status_strings_and_version():
+    for code in range(7):
+        assert da.qknorm_rope_attn_status_string(code)
+    assert da.qknorm_rope_attn_status_string(99) == "unknown status"
+    assert da.qknorm_rope_attn_version() == 100
+    assert da.qknorm_rope_attn_last_hip_error() == 0
+    assert da.qknorm_rope_attn_kernel_name(1) == "prefill_attn_mfma_bf16"
+
+
+def test_workspace_bytes():
+    cfg = da.make_config(32, 8, 128, da.QKRA_BF16)
+    # prefill: q~ [N, Hq, D] bf16, rounded up to 256 bytes
+    assert da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_PREFILL, 100, 100) == 100 * 32 * 128 * 2
+    assert da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_PREFILL, 1, 1) == 8192
+    # decode: q~ then fp32 (m, l, o[D]) per (request, head, 512-key split)
+    b, L = 3, 1023
+    splits = (L + 1 + 511) // 512
+    q_bytes = -(-(b * 32 * 128 * 2) // 256) * 256
+    p_bytes = -(-(b * 32 * splits * 130 * 4) // 256) * 256
+    assert da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_DECODE, b, L) == q_bytes + p_bytes
+    bad = da.make_config(5, 2, 128)
+    assert da.qknorm_rope_attn_workspace_bytes(bad, da.QKRA_MODE_PREFILL, 10, 10) == 0
+    assert da.qknorm_rope_attn_workspace_bytes(cfg, 7, 10, 10) == 0
+
+
+BASE = 1 << 32
+MB = 1 << 20
+
+
+def prefill_args(**over):
+    cfg = over.pop("cfg", da.make_config(4, 2, 64, da.QKRA_BF16, 1e-6, 1e4))
+    a = dict(qkv=BASE, q_norm_weight=BASE + 64 * MB, k_norm_weight=BASE + 65 * MB, positions=BASE + 66 * MB,
+             cu_seqlens=BASE + 67 * MB, num_tokens=64, num_seqs=1, max_seqlen=64, k_cache=BASE + 100 * MB,
+             v_cache=BASE + 200 * MB, cache_capacity=64, out=BASE + 300 * MB, workspace=BASE + 400 * MB,
+             workspace_bytes=1 << 20, stream=0)
+    a.update(over)
+    return cfg, a
+
+
+def call_prefill(cfg, a):
+    return da.qknorm_rope_attn_prefill(cfg, a["qkv"], a["q_norm_weight"], a["k_norm_weight"], a["positions"],
+                                       a["cu_seqlens"], a["num_tokens"], a["num_seqs"], a["max_seqlen"],
+                                       a["k_cache"], a["v_cache"], a["cache_capacity"], a["out"], a["workspace"],
+                                       a["workspace_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(cfg=da.make_config(5, 2, 64)), da.QKRA_ERR_INVALID_ARGUMENT),          # Hq % Hkv != 0
+    (dict(cfg=da.make_config(4, 0, 64)), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(cfg=da.make_config(4, 2, 96)), da.QKRA_ERR_UNSUPPORTED),               # head_dim
+    (dict(cfg=da.make_config(4, 2, 64, 7)), da.QKRA_ERR_UNSUPPORTED),            # dtype
+    (dict(cfg=da.make_config(4, 2, 64, 0, -1.0)), da.QKRA_ERR_INVALID_ARGUMENT),  # eps < 0
+    (dict(cfg=da.make_config(4, 2, 64, 0, 1e-6, 0.0)), da.QKRA_ERR_INVALID_ARGUMENT),  # base <= 0
+    (dict(num_tokens=-1), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(max_seqlen=65), da.QKRA_ERR_INVALID_ARGUMENT),                        # longer than N
+    (dict(num_tokens=64, num_seqs=2, max_seqlen=16), da.QKRA_ERR_INVALID_ARGUMENT),  # B * max < N
+    (dict(num_seqs=0), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(cache_capacity=63), da.QKRA_ERR_CAPACITY),
+    (dict(qkv=None), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(cu_seqlens=None), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(workspace_bytes=64 * 4 * 64 * 2 - 1), da.QKRA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(workspace=None), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(out=BASE + 8), da.QKRA_ERR_INVALID_ARGUMENT),                          # misaligned
+    (dict(out=BASE), da.QKRA_ERR_ALIASING),                                      # out over qkv
+    (dict(v_cache=BASE + 100 * MB + 4096), da.QKRA_ERR_ALIASING),                # caches overlap
+    (dict(workspace=BASE + 300 * MB + 256), da.QKRA_ERR_ALIASING),               # workspace over out
+    (dict(k_cache=BASE + 64 * MB), da.QKRA_ERR_ALIASING),                        # cache over a weight
+])
+def test_prefill_argument_checks(over, status):
+    cfg, a = prefill_args(**over)
+    assert call_prefill(cfg, a) == status
+    assert da.qknorm_rope_attn_last_hip_error() == 0  # rejected before any launch
+
+
+def test_prefill_empty_batch_is_noop():
+    cfg, a = prefill_args(num_tokens=0, num_seqs=0, max_seqlen=0, qkv=None, out=None, workspace=None,
+                          workspace_bytes=0)
+    assert call_prefill(cfg, a) == da.QKRA_OK
+
+
+def decode_args(**over):
+    cfg = over.pop("cfg", da.make_config(32, 8, 128, da.QKRA_BF16))
+    a = dict(qkv=BASE, q_norm_weight=BASE + 64 * MB, k_norm_weight=BASE + 65 * MB, positions=BASE + 66 * MB,
+             cache_lens=BASE + 67 * MB, num_seqs=4, max_cache_len=100, k_cache=BASE + 100 * MB,
+             v_cache=BASE + 200 * MB, cache_capacity=101, out=BASE + 300 * MB, workspace=BASE + 400 * MB,
+             workspace_bytes=1 << 20, stream=0)
+    a.update(over)
+    return cfg, a
+
+
+def call_decode(cfg, a):
+    return da.qknorm_rope_attn_decode(cfg, a["qkv"], a["q_norm_weight"], a["k_norm_weight"], a["positions"],
+                                      a["cache_lens"], a["num_seqs"], a["max_cache_len"], a["k_cache"],
+                                      a["v_cache"], a["cache_capacity"], a["out"], a["workspace"],
+                                      a["workspace_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(cfg=da.make_config(32, 7, 128)), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(cfg=da.make_config(32, 8, 256)), da.QKRA_ERR_UNSUPPORTED),
+    (dict(num_seqs=-2), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(max_cache_len=-1), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(cache_capacity=100), da.QKRA_ERR_CAPACITY),                            # no room for the new token
+    (dict(cache_lens=None), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(workspace_bytes=1024), da.QKRA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(k_cache=BASE + 16 * 1024), da.QKRA_ERR_ALIASING),                     # cache over qkv [B, 48*128] bf16
+    (dict(out=BASE + 200 * MB + 4096), da.QKRA_ERR_ALIASING),                    # out over the V cache
+    (dict(workspace=BASE + 67 * MB), da.QKRA_ERR_ALIASING),                      # workspace over cache_lens
+])
+def test_decode_argument_checks(over, status):
+    cfg, a = decode_args(**over)
+    assert call_decode(cfg, a) == status
+    assert da.qknorm_rope_attn_last_hip_error() == 0  # rejected before any launch
+
+
+def test_decode_empty_batch_is_noop():
+    cfg, a = decode_args(num_seqs=0, qkv=None, out=None, workspace=None, workspace_bytes=0)
+    assert call_decode(cfg, a) == da.QKRA_OK
+
+
+def test_kernel_timing_toggle_without_launches():
+    assert da.qknorm_rope_attn_set_kernel_timing(True) == 0
+    assert da.qknorm_rope_attn_read_kernel_timing() == {}
+    assert da.qknorm_rope_attn_set_kernel_timing(False) == 0

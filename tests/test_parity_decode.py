@@ -1,0 +1,180 @@
+"""Decode on the GPU, through the C ABI, against the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from harness import (BF16_TOL, assert_close, bits, f64, layer_kw, note, oracle_prefill, run_decode, run_prefill,
+                     tol_for)
+from workloads import HeadConfig, build_workload, make_decode_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _check_decode(d, subset=None, tol=None):
+    """Runs the HIP decode on all requests and checks `subset` of them (all if None)."""
+    tol = tol if tol is not None else tol_for(d.qkv.dtype)
+    b_all = d.num_seqs
+    subset = list(range(b_all)) if subset is None else list(subset)
+    lens = d.cache_lens.cpu().tolist()
+    k_before, v_before = d.k_cache.clone(), d.v_cache.clone()
+    got = run_decode(d)
+    h = d.heads
+    hq, hkv, dim = h.num_q_heads, h.num_kv_heads, h.head_dim
+    top = max(lens[b] for b in subset) + 1
+    idx = torch.tensor(subset, device=d.k_cache.device)
+    kc = f64(k_before.index_select(0, idx)[:, :, :top])
+    vc = f64(v_before.index_select(0, idx)[:, :, :top])
+    ref = oracle.decode(f64(d.qkv.index_select(0, idx)), f64(d.q_norm_weight), f64(d.k_norm_weight),
+                        d.positions.cpu().numpy()[subset], np.array(lens)[subset], kc, vc, **layer_kw(h))
+    err = assert_close(f64(got["out"].index_select(0, idx)), ref["out"], tol, "decode out")
+    v_new = d.qkv[:, (hq + hkv) * dim:].reshape(b_all, hkv, dim)
+    kb, vb = bits(d.k_cache), bits(d.v_cache)
+    kb0, vb0 = bits(k_before), bits(v_before)
+    for i, b in enumerate(subset):
+        L = lens[b]
+        assert torch.equal(vb[b, :, L], bits(v_new[b])), f"new V slot of request {b}"
+        assert_close(f64(d.k_cache[b, :, L]), ref["k_tilde"][i], tol, f"new K slot of request {b}")
+    # Every slot other than L_b, of every request, keeps its bits.
+    mask = torch.ones(d.k_cache.shape[:3], dtype=torch.bool, device=d.k_cache.device)
+    mask[torch.arange(b_all, device=mask.device), :, d.cache_lens.long()] = False
+    assert torch.equal(kb[mask], kb0[mask]) and torch.equal(vb[mask], vb0[mask]), "a slot other than L_b changed"
+    return err
+
+
+# (Hq, Hkv, D, cache lengths): split edges (512 keys per split), 16-key step
+# edges, empty caches (the token attends to itself only), every GQA width.
+CASES = [
+    (4, 2, 64, [0, 1, 5, 64]),
+    (32, 8, 128, [0, 1, 15, 16, 17, 511, 512, 513, 1000, 2047]),
+    (16, 8, 128, [100, 3000]),
+    (8, 8, 64, [700, 1]),
+    (16, 2, 128, [33, 1025]),
+    (12, 4, 64, [50, 600]),
+]
+
+
+def _ids(case):
+    hq, hkv, d, lens = case
+    return f"hq{hq}-hkv{hkv}-d{d}-L{'_'.join(map(str, lens))}"
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_decode_matches_oracle(case, dtype):
+    hq, hkv, d, lens = case
+    h = HeadConfig(hq, hkv, d, 1e-6, 1e6)
+    note(f"decode {_ids(case)} {dtype}")
+    dec = make_decode_inputs(h, lens, seed=sum(lens) % 9973, dtype=dtype, device=DEV, capacity=max(lens) + 4)
+    _check_decode(dec)
+
+
+def test_decode_is_deterministic():
+    h = HeadConfig(32, 8, 128, 1e-6, 1e6)
+    outs = []
+    for _ in range(2):
+        dec = make_decode_inputs(h, [3000, 10, 700], seed=3, device=DEV)
+        outs.append(run_decode(dec)["out"])
+    assert torch.equal(bits(outs[0]), bits(outs[1]))
+
+
+def _chained(name):
+    """Prefill, then decode steps on the cache the prefill wrote, against the oracle doing the same."""
+    w = build_workload(name, device=DEV)
+    p = w.prefill
+    h = p.heads
+    run_prefill(p)
+    ref = oracle_prefill(p)
+    kc, vc = ref["k_cache"], ref["v_cache"]
+    t = p.seqlens[0]
+    errs = []
+    for s, row in enumerate(w.chained_decode_qkv):
+        L = t + s
+        lens = torch.tensor([L], dtype=torch.int32, device=DEV)
+
+        class Step:  # the decode arguments for this step
+            heads = h
+            qkv = row
+            q_norm_weight = p.q_norm_weight
+            k_norm_weight = p.k_norm_weight
+            positions = lens.clone()
+            cache_lens = lens
+            cache_capacity = p.cache_capacity
+            k_cache = p.k_cache
+            v_cache = p.v_cache
+            num_seqs = 1
+            max_cache_len = L
+
+        got = run_decode(Step)["out"]
+        r = oracle.decode(f64(row), f64(p.q_norm_weight), f64(p.k_norm_weight), [L], [L], kc, vc, **layer_kw(h))
+        kc, vc = r["k_cache"], r["v_cache"]
+        errs.append(assert_close(f64(got), r["out"], BF16_TOL, f"{name} decode step {s}"))
+        assert torch.equal(bits(p.v_cache[0, :, L]), bits(row[0, (h.num_q_heads + h.num_kv_heads) * h.head_dim:]
+                                                          .reshape(h.num_kv_heads, h.head_dim)))
+    note(f"{name}: chained decode max-abs errors {['%.2e' % e for e in errs]}")
+
+
+def test_chained_decode_single_t64():
+    _chained("single_t64_hq4_hkv2_d64")
+
+
+def test_chained_decode_pages_t12_9_steps():
+    _chained("pages_t12_decode9")
+
+
+def test_decode_equals_last_prefill_row_on_gpu():
+    # A decode step over L cached tokens and a prefill over the same L+1 tokens
+    # compute the same row (different kernels, so compared to the tolerance).
+    from workloads import make_prefill_inputs
+
+    h = HeadConfig(32, 8, 128, 1e-6, 1e6)
+    for L in (0, 37, 600):
+        p = make_prefill_inputs(h, [L + 1], seed=L, device=DEV, capacity=L + 1)
+        full = run_prefill(p)["out"]
+        k = p.k_cache.clone()
+        v = p.v_cache.clone()
+        k[:, :, L:] = float("nan")
+        v[:, :, L:] = float("nan")
+
+        class Step:
+            heads = h
+            qkv = p.qkv[L:L + 1]
+            q_norm_weight = p.q_norm_weight
+            k_norm_weight = p.k_norm_weight
+            positions = torch.tensor([L], dtype=torch.int32, device=DEV)
+            cache_lens = torch.tensor([L], dtype=torch.int32, device=DEV)
+            cache_capacity = L + 1
+            k_cache = k
+            v_cache = v
+            num_seqs = 1
+            max_cache_len = L
+
+        got = run_decode(Step)["out"]
+        assert_close(f64(got), f64(full[L:L + 1]), BF16_TOL, f"decode vs prefill row at L={L}")
+        # The decode wrote the same K~/V the prefill wrote for that token.
+        assert torch.equal(bits(v), bits(p.v_cache))
+        assert torch.equal(bits(k), bits(p.k_cache))
+
+
+def test_decode_qwen3_4b_64_requests_sampled():
+    # 64 requests, cache lengths U[512, 8192], Hq=32 Hkv=8 D=128 -- the launch shape the benchmark times.
+    w = build_workload("qwen3_4b_decode64", device=DEV)
+    lens = w.decode.cache_lens.cpu().tolist()
+    order = np.argsort(lens)
+    subset = sorted({int(order[0]), int(order[-1])} | set(int(x) for x in np.random.default_rng(3).choice(64, 6,
+                                                                                                        replace=False)))
+    err = _check_decode(w.decode, subset)
+    note(f"decode64: requests {subset} max-abs error {err:.3e}")
+
+
+def test_decode_mixed_step_part_sampled():
+    w = build_workload("mixed_qwen3_8b", device=DEV)
+    lens = w.decode.cache_lens.cpu().tolist()
+    order = np.argsort(lens)
+    subset = sorted({int(order[0]), int(order[-1])} | set(int(x) for x in np.random.default_rng(5).choice(128, 6,
+                                                                                                         replace=False)))
+    err = _check_decode(w.decode, subset)
+    note(f"mixed decode: requests {subset} (lengths {[lens[b] for b in subset]}) max-abs error {err:.3e}")
