@@ -48,25 +48,28 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
-def build_library(verbose: bool = False, jobs: int | None = None, extra_flags=None) -> str:
+def build_library(verbose: bool = False, jobs: int | None = None, extra_flags=None, out_path: str | None = None,
+                  build_dir: str | None = None) -> str:
     """Compile every HIP source for gfx950 and link the shared library; returns its path."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    build_dir = build_dir or BUILD_DIR
+    out_path = out_path or LIB_PATH
+    os.makedirs(build_dir, exist_ok=True)
     flags = CFLAGS + list(extra_flags or [])
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmds.append([hipcc] + flags + ["-c", os.path.join(CSRC, src), "-o", obj])
     workers = jobs or min(len(cmds), max(1, (os.cpu_count() or 4) // 2), 8)
     with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as pool:
         for fut in [pool.submit(_run, c, verbose) for c in cmds]:
             fut.result()
-    tmp = LIB_PATH + ".tmp"
+    tmp = out_path + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out_path)
+    return out_path
 
 
 if __name__ == "__main__":

@@ -52,7 +52,7 @@ hipError_t launch_prefill_attn_bf16(const PrefillAttnArgs& a, hipStream_t stream
 hipError_t launch_prefill_attn_fp32(const PrefillAttnArgs& a, hipStream_t stream);
 
 // Kernels 3a/3b: split-KV decode attention and the log-sum-exp combine.
-constexpr int kDecodeKeysPerSplit = 512;  // keys handled by one wavefront
+constexpr int kDecodeKeysPerSplit = 1024;  // keys per workgroup (4 wavefronts x 256)
 
 inline int decode_num_splits(int max_cache_len) {
   return (max_cache_len + 1 + kDecodeKeysPerSplit - 1) / kDecodeKeysPerSplit;

@@ -26,7 +26,8 @@
 //    accumulator is again one query per lane, so the online-softmax rescale
 //    is a per-lane multiply.
 //  * fp32 online softmax in the log2 domain (scale log2(e)/sqrt(D) folded into
-//    one multiply).  K/V tiles run only up to the causal diagonal of the
+//    the exponent's FMA); the running max is raised lazily (only when a tile
+//    max exceeds it by more than 2^8), so the O rescale is rare.  K/V tiles run only up to the causal diagonal of the
 //    workgroup's last token; tiles entirely above a wavefront's rows are
 //    skipped by that wavefront; only tiles that cross the diagonal are masked.
 //  * Keys at or past the request's length are zero-filled on load so that
@@ -44,8 +45,30 @@
 namespace qkra {
 namespace {
 
-constexpr int BN = 64;        // keys per K/V tile
-constexpr int NTHREADS = 256;
+// Launch shape.  QB query blocks (of 32 rows) per wavefront and 8/QB
+// wavefronts per workgroup, so a workgroup always owns 8 query blocks; BN keys
+// per K/V tile.  QB = 1 gives two wavefronts per SIMD (their matrix and vector
+// work interleave); QB = 2 halves the LDS reads per MFMA but leaves one
+// wavefront per SIMD.
+#ifndef QKRA_PREFILL_QB
+#define QKRA_PREFILL_QB 1
+#endif
+#ifndef QKRA_PREFILL_BN
+#define QKRA_PREFILL_BN 64
+#endif
+constexpr int QB = QKRA_PREFILL_QB;
+constexpr int BN = QKRA_PREFILL_BN;
+constexpr int NWAVES = 8 / QB;
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr float TAU = 8.0f;   // lazy-rescale threshold (log2 units)
+static_assert(QB == 1 || QB == 2, "QB");
+static_assert(BN == 32 || BN == 64, "BN");
+
+// Max of a value held by lanes l and l ^ 32 (gfx950 v_permlane32_swap).
+__device__ __forceinline__ float half_wave_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 template <int D, int HC>
 __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
@@ -57,13 +80,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   constexpr int TM = 32 * TBN;      // tokens per workgroup
   constexpr int DS = D / 16;        // k-steps over D for the scores
   constexpr int DB = D / 32;        // 32-wide blocks of D in the output
+  constexpr int KB = BN / 32;       // 32-key blocks per tile
+  constexpr int KSTEPS = BN / 16;   // 16-key steps per tile
   constexpr int KST = D + 8;        // LDS row stride of K (elements)
   constexpr int VST = BN + 8;       // LDS row stride of V^T (elements)
-  constexpr int KCHUNKS = BN * D / 8 / NTHREADS;  // 16-byte K loads per thread per tile
-  constexpr int VITEMS = 16 * (D / 8);             // (4 keys x 8 d) V items per tile
+  constexpr int KCH = BN * D / 8;   // 16-byte K chunks per tile
+  constexpr int KCHUNKS = (KCH + NTHREADS - 1) / NTHREADS;
+  constexpr int VITEMS = (BN / 4) * (D / 8);  // (4 keys x 8 d) V items per tile
+  constexpr int NSLOT = 3;          // LDS tile slots
 
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][BN * KST];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][D * VST];
+  __shared__ __attribute__((aligned(16))) bf16 sK[NSLOT][BN * KST];
+  __shared__ __attribute__((aligned(16))) bf16 sV[NSLOT][D * VST];
 
   // ---- work item (XCD-aware remap, heaviest tiles first) -------------------
   const int nb = gridDim.x;  // a multiple of 8
@@ -89,19 +116,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  int qtok[2], qhead[2], qfirst[2];
+  int qtok[QB], qhead[QB], qfirst[QB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int bi = 2 * wave + qb;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int bi = QB * wave + qb;
     qfirst[qb] = t0 + 32 * (bi / HC);
     qtok[qb] = qfirst[qb] + l32;
     qhead[qb] = h0 + bi % HC;
   }
 
   // Q^T fragments (B operand): lane holds query l32, d = 16*ds + 8*hi .. +7.
-  bf16x8 qf[2][DS];
+  bf16x8 qf[QB][DS];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const bool valid = qtok[qb] < seqlen;
     const bf16* src = q + (static_cast<size_t>(cu0 + (valid ? qtok[qb] : 0)) * num_q_heads + qhead[qb]) * D + 8 * hi;
 #pragma unroll
@@ -112,55 +139,62 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     }
   }
 
-  f32x16 acc[2][DB];
+  f32x16 acc[QB][DB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
-  float m_run[2] = {kNegInf, kNegInf};
-  float l_run[2] = {0.f, 0.f};
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = kNegInf;
+    l_run[qb] = 0.f;
+  }
 
   const int kv_end = min(seqlen, t0 + TM);
   const int ntiles = (kv_end + BN - 1) / BN;
+  int qlast = qfirst[0];
+#pragma unroll
+  for (int qb = 1; qb < QB; ++qb) qlast = max(qlast, qfirst[qb]);
+  // Tiles holding a key visible to this wavefront's rows (the rest are only loaded).
+  const int wtiles = min(kv_end - 1, qlast + 31) / BN + 1;
   const size_t head_off = (static_cast<size_t>(seq) * num_kv_heads + g) * cache_capacity * D;
   const bf16* kbase = k_cache + head_off;
   const bf16* vbase = v_cache + head_off;
 
-  uint4 kreg[KCHUNKS];
-  uint4 vreg[4];
-  const int v_kq = tid & 15;   // which 4-key quad of the tile
-  const int v_dq = tid >> 4;   // which 8-wide slice of D
+  // ---- global -> registers -> LDS staging -------------------------------------
+  // Rows past kv_end are read from row kv_end-1 instead (a valid row, so the
+  // values are finite); every such key lies after every stored query row and
+  // is removed by the causal mask.
+  u32x4 kreg[KCHUNKS];
+  u32x4 vreg[4];
+  const int v_kq = tid % (BN / 4);   // which 4-key quad of the tile
+  const int v_dq = tid / (BN / 4);   // which 8-wide slice of D
   const bool v_loader = tid < VITEMS;
 
   auto load_tile = [&](int kt) {
     const int k0 = kt * BN;
-#pragma unroll
-    for (int i = 0; i < KCHUNKS; ++i) {
+    static_for<KCHUNKS>([&](auto i) {
       const int c = tid + NTHREADS * i;
-      const int r = c / (D / 8);
-      const int col = c % (D / 8);
-      const int key = k0 + r;
-      kreg[i] = key < kv_end ? *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(key) * D + col * 8)
-                             : make_uint4(0, 0, 0, 0);
-    }
-    if (v_loader) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 4 * v_kq + r;
-        vreg[r] = key < kv_end ? *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(key) * D + v_dq * 8)
-                               : make_uint4(0, 0, 0, 0);
+      if (KCH % NTHREADS == 0 || c < KCH) {
+        const int key = min(k0 + c / (D / 8), kv_end - 1);
+        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(key) * D + (c % (D / 8)) * 8);
       }
+    });
+    if (v_loader) {
+      static_for<4>([&](auto r) {
+        const int key = min(k0 + 4 * v_kq + r, kv_end - 1);
+        vreg[r] = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(key) * D + v_dq * 8);
+      });
     }
   };
 
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KCHUNKS; ++i) {
+  auto store_tile = [&](int slot) {
+    static_for<KCHUNKS>([&](auto i) {
       const int c = tid + NTHREADS * i;
-      const int r = c / (D / 8);
-      const int col = c % (D / 8);
-      *reinterpret_cast<uint4*>(&sK[buf][r * KST + col * 8]) = kreg[i];
-    }
+      if (KCH % NTHREADS == 0 || c < KCH)
+        *reinterpret_cast<u32x4*>(&sK[slot][(c / (D / 8)) * KST + (c % (D / 8)) * 8]) = kreg[i];
+    });
     if (v_loader) {
       // Keys 4*kq..4*kq+3 of one 8-wide d slice, written transposed.  Within
       // each 16-key step the key quads are stored in the order 0, 2, 1, 3, so
@@ -169,117 +203,168 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
       const int step = v_kq >> 2;
       const int quad = v_kq & 3;
       const int pos = 16 * step + 4 * ((quad & 1) * 2 + (quad >> 1));
-      const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-      const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-      const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
-      const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
+      const u32x4 w0 = vreg[0], w1 = vreg[1], w2 = vreg[2], w3 = vreg[3];
+      static_for<4>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        const u32x2 lo = {__builtin_amdgcn_perm(w1[p], w0[p], 0x05040100u),
+                          __builtin_amdgcn_perm(w3[p], w2[p], 0x05040100u)};
+        const u32x2 hv = {__builtin_amdgcn_perm(w1[p], w0[p], 0x07060302u),
+                          __builtin_amdgcn_perm(w3[p], w2[p], 0x07060302u)};
+        *reinterpret_cast<u32x2*>(&sV[slot][(v_dq * 8 + 2 * p) * VST + pos]) = lo;
+        *reinterpret_cast<u32x2*>(&sV[slot][(v_dq * 8 + 2 * p + 1) * VST + pos]) = hv;
+      });
+    }
+  };
+
+  // ---- the matrix and softmax pieces ----------------------------------------
+  // S^T = K Q^T for the tile in `slot`: lane holds query l32 and, per 32-key
+  // block kb, keys 32kb + 8(j/4) + 4hi + j%4 in register j.
+  auto scores = [&](int slot, f32x16 (&S)[QB][KB]) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint2 lo = make_uint2((w0[p] & 0xffffu) | (w1[p] << 16), (w2[p] & 0xffffu) | (w3[p] << 16));
-        const uint2 hi2 = make_uint2((w0[p] >> 16) | (w1[p] & 0xffff0000u), (w2[p] >> 16) | (w3[p] & 0xffff0000u));
-        *reinterpret_cast<uint2*>(&sV[buf][(v_dq * 8 + 2 * p) * VST + pos]) = lo;
-        *reinterpret_cast<uint2*>(&sV[buf][(v_dq * 8 + 2 * p + 1) * VST + pos]) = hi2;
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) S[qb][kb] = f32x16{};
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[slot][(kb * 32 + l32) * KST + 16 * ds + 8 * hi]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          S[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ds], S[qb][kb], 0, 0, 0);
       }
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ntiles) load_tile(kt + 1);
+  // Causal mask (tiles that cross the diagonal only) and the tile's row max,
+  // taken on raw scores (the scale is positive).
+  auto tile_max = [&](int kt, f32x16 (&S)[QB][KB], float (&mx)[QB]) {
     const int k0 = kt * BN;
-
-    // A wavefront whose rows all precede this tile's first key skips it.
-    const bool live0 = k0 <= qfirst[0] + 31;
-    const bool live1 = k0 <= qfirst[1] + 31;
-    if (live0 || live1) {
-      // ---- S^T = K Q^T ------------------------------------------------------
-      f32x16 s[2][2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb) {
+      if (k0 + BN - 1 > qfirst[qb]) {
+        const int lim = qtok[qb] - k0 - 4 * hi;  // register j of block kb holds key k0 + 32kb + 8(j/4) + 4hi + j%4
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[qb][kb] = f32x16{};
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][(kb * 32 + l32) * KST + 16 * ds + 8 * hi]);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ds], s[qb][kb], 0, 0, 0);
-        }
+          for (int j = 0; j < 16; ++j)
+            if (32 * kb + 8 * (j >> 2) + (j & 3) > lim) S[qb][kb][j] = kNegInf;
       }
+      float m = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) m = fmaxf(m, S[qb][kb][j]);
+      mx[qb] = half_wave_max(m) * scale_log2;
+    }
+  };
 
-      // ---- online softmax (lane = query l32) --------------------------------
-      bf16x8 pf[2][4];
+  // Lazy rescale: the running max is raised only when a tile max exceeds it
+  // by more than 2^TAU; the stale max is used consistently for p and the row
+  // sum, so the result is exact.
+  auto raise_max = [&](const float (&mx)[QB]) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const bool diag = k0 + BN - 1 > qfirst[qb];
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            float x = s[qb][kb][j] * scale_log2;
-            if (diag) {
-              const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
-              if (key > qtok[qb]) x = kNegInf;
-            }
-            s[qb][kb][j] = x;
-            mx = fmaxf(mx, x);
-          }
-        mx = fmaxf(mx, xor_shuffle(mx, 32));
-        const float m_new = fmaxf(m_run[qb], mx);
-        const float m_use = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[qb] - m_use);
-        m_run[qb] = m_new;
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const float p = fast_exp2(s[qb][kb][j] - m_use);
-            s[qb][kb][j] = p;
-            rs += p;
-          }
-        l_run[qb] = l_run[qb] * alpha + rs;
+    for (int qb = 0; qb < QB; ++qb) {
+      const bool need = mx[qb] > m_run[qb] + TAU;
+      if (__any(need)) {
+        const float m_new = need ? mx[qb] : m_run[qb];
+        const float alpha = fast_exp2(m_run[qb] - m_new);
+        l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
-        // P^T as the B operand: 16-key step ks = 2*kb + half uses the
-        // accumulator registers 8*half .. 8*half+7 of key block kb.
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int kb = ks >> 1, base = 8 * (ks & 1);
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[qb][kb][base + 2 * e], s[qb][kb][base + 2 * e + 1]);
-          pf[qb][ks] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-        }
-      }
-
-      // ---- O^T += V^T P^T ----------------------------------------------------
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[buf][(db * 32 + l32) * VST + 16 * ks + 8 * hi]);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][ks], acc[qb][db], 0, 0, 0);
-        }
+        m_run[qb] = m_new;
       }
     }
+  };
 
-    if (kt + 1 < ntiles) store_tile(buf ^ 1);
+  // p = 2^(s*scale - m), rounded to bf16 as the B operand of the P.V product;
+  // the row sum accumulates the same rounded values (dot with (1, 1)).
+  // 16-key step ks uses registers 8*(ks%2) .. +7 of key block ks/2.
+  const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
+  auto probs = [&](f32x16 (&S)[QB][KB], bf16x8 (&pf)[QB][KSTEPS]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float nm = -m_run[qb];
+      float rs = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int kb = ks >> 1, base = 8 * (ks & 1);
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(__builtin_fmaf(S[qb][kb][base + 2 * e], scale_log2, nm));
+          const float p1 = fast_exp2(__builtin_fmaf(S[qb][kb][base + 2 * e + 1], scale_log2, nm));
+          w[e] = pack_bf16x2(p0, p1);
+          rs = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[e]), ones, rs, false);
+        }
+        pf[qb][ks] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+      }
+      l_run[qb] += rs;
+    }
+  };
+
+  // O^T += V^T P^T for the tile in `slot`.
+  auto pv = [&](int slot, const bf16x8 (&pf)[QB][KSTEPS]) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[slot][(db * 32 + l32) * VST + 16 * ks + 8 * hi]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][ks], acc[qb][db], 0, 0, 0);
+      }
+  };
+
+  // ---- software pipeline.  Entering step kt, S holds tile kt's masked
+  // scores and m_run already covers them.  Step kt forms tile kt+1's scores
+  // on the matrix cores while the vector units turn tile kt into
+  // probabilities, then issues tile kt's P.V while the vector units mask and
+  // reduce tile kt+1.  Tile kt+2 is fetched from global memory meanwhile and
+  // written to the third LDS slot.
+  auto step = [&](int kt, f32x16 (&Scur)[QB][KB], f32x16 (&Snext)[QB][KB]) {
+    const bool prefetch = kt + 2 < ntiles;
+    if (prefetch) load_tile(kt + 2);
+    if (kt < wtiles) {
+      bf16x8 pf[QB][KSTEPS];
+      if (kt + 1 < wtiles) {
+        float mx[QB];
+        scores((kt + 1) % NSLOT, Snext);
+        probs(Scur, pf);
+        pv(kt % NSLOT, pf);
+        tile_max(kt + 1, Snext, mx);
+        raise_max(mx);
+      } else {
+        probs(Scur, pf);
+        pv(kt % NSLOT, pf);
+      }
+    }
+    if (prefetch) store_tile((kt + 2) % NSLOT);
     __syncthreads();
+  };
+
+  load_tile(0);
+  store_tile(0);
+  if (ntiles > 1) {
+    load_tile(1);
+    store_tile(1);
+  }
+  __syncthreads();
+  f32x16 sA[QB][KB], sB[QB][KB];
+  {
+    float mx[QB];
+    scores(0, sA);
+    tile_max(0, sA, mx);
+    raise_max(mx);
+  }
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    step(kt, sA, sB);
+    if (kt + 1 < ntiles) step(kt + 1, sB, sA);
   }
 
   // ---- normalise and store: lane holds query l32, d = 32*db + 8*(j/4) + 4*hi + j%4
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + xor_shuffle(l_run[qb], 32);
     const float inv = 1.0f / l_tot;
     if (qtok[qb] < seqlen) {
@@ -289,9 +374,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq) {
           const f32x16& a = acc[qb][db];
-          const uint2 w = make_uint2(pack_bf16x2(a[4 * jq] * inv, a[4 * jq + 1] * inv),
-                                     pack_bf16x2(a[4 * jq + 2] * inv, a[4 * jq + 3] * inv));
-          *reinterpret_cast<uint2*>(dst + 32 * db + 8 * jq) = w;
+          const u32x2 w = {pack_bf16x2(a[4 * jq] * inv, a[4 * jq + 1] * inv),
+                           pack_bf16x2(a[4 * jq + 2] * inv, a[4 * jq + 3] * inv)};
+          *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * jq) = w;
         }
     }
   }

@@ -25,22 +25,22 @@ namespace qkra {
 namespace {
 
 template <typename T> struct Raw4;
-template <> struct Raw4<bf16> { typedef uint2 type; };
-template <> struct Raw4<float> { typedef uint4 type; };
+template <> struct Raw4<bf16> { typedef u32x2 type; };
+template <> struct Raw4<float> { typedef u32x4 type; };
 
-__device__ __forceinline__ void unpack4(uint2 r, float x[4]) {
+__device__ __forceinline__ void unpack4(u32x2 r, float x[4]) {
   x[0] = bf16_lo_to_f32(r.x); x[1] = bf16_hi_to_f32(r.x);
   x[2] = bf16_lo_to_f32(r.y); x[3] = bf16_hi_to_f32(r.y);
 }
-__device__ __forceinline__ void unpack4(uint4 r, float x[4]) {
+__device__ __forceinline__ void unpack4(u32x4 r, float x[4]) {
   x[0] = __uint_as_float(r.x); x[1] = __uint_as_float(r.y);
   x[2] = __uint_as_float(r.z); x[3] = __uint_as_float(r.w);
 }
-__device__ __forceinline__ void pack4(const float y[4], uint2* r) {
+__device__ __forceinline__ void pack4(const float y[4], u32x2* r) {
   r->x = pack_bf16x2(y[0], y[1]);
   r->y = pack_bf16x2(y[2], y[3]);
 }
-__device__ __forceinline__ void pack4(const float y[4], uint4* r) {
+__device__ __forceinline__ void pack4(const float y[4], u32x4* r) {
   r->x = __float_as_uint(y[0]); r->y = __float_as_uint(y[1]);
   r->z = __float_as_uint(y[2]); r->w = __float_as_uint(y[3]);
 }

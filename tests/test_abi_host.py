@@ -47,9 +47,9 @@ def test_workspace_bytes():
     # prefill: q~ [N, Hq, D] bf16, rounded up to 256 bytes
     assert da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_PREFILL, 100, 100) == 100 * 32 * 128 * 2
     assert da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_PREFILL, 1, 1) == 8192
-    # decode: q~ then fp32 (m, l, o[D]) per (request, head, 512-key split)
-    b, L = 3, 1023
-    splits = (L + 1 + 511) // 512
+    # decode: q~ then fp32 (m, l, o[D]) per (request, head, 1024-key split)
+    b, L = 3, 2047
+    splits = (L + 1 + 1023) // 1024
     q_bytes = -(-(b * 32 * 128 * 2) // 256) * 256
     p_bytes = -(-(b * 32 * splits * 130 * 4) // 256) * 256
     assert da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_DECODE, b, L) == q_bytes + p_bytes
