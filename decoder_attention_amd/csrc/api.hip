@@ -47,7 +47,23 @@ size_t decode_q_bytes(const qkra_config* cfg, int64_t num_seqs) {
   return align_up(static_cast<size_t>(num_seqs) * cfg->num_q_heads * cfg->head_dim * elem_size(cfg->dtype));
 }
 
+// bf16: units of (request, KV head, chunk of GW query heads).
+int64_t decode_units(const qkra_config* cfg, int64_t num_seqs) {
+  const int group = cfg->num_q_heads / cfg->num_kv_heads;
+  return num_seqs * cfg->num_kv_heads * (group / decode_heads_per_wave(group));
+}
+
+size_t decode_plan_bytes(const qkra_config* cfg, int64_t num_seqs) {
+  return align_up(decode_plan_ints(decode_units(cfg, num_seqs)) * sizeof(int32_t));
+}
+
 size_t decode_workspace(const qkra_config* cfg, int64_t num_seqs, int32_t max_cache_len) {
+  if (cfg->dtype == QKRA_BF16) {
+    const int gw = decode_heads_per_wave(cfg->num_q_heads / cfg->num_kv_heads);
+    const size_t records = static_cast<size_t>(decode_units(cfg, num_seqs) + kDecodeWaves) * gw;
+    return decode_q_bytes(cfg, num_seqs) + decode_plan_bytes(cfg, num_seqs) +
+           align_up(records * (cfg->head_dim + 4) * sizeof(float));
+  }
   const size_t splits = static_cast<size_t>(decode_num_splits(max_cache_len));
   return decode_q_bytes(cfg, num_seqs) +
          align_up(static_cast<size_t>(num_seqs) * cfg->num_q_heads * splits * (cfg->head_dim + 2) * sizeof(float));
@@ -247,6 +263,10 @@ QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv
   if (static_cast<long long>(cache_capacity) < static_cast<long long>(max_cache_len) + 1) return QKRA_ERR_CAPACITY;
   if (!qkv || !q_norm_weight || !k_norm_weight || !positions || !cache_lens || !k_cache || !v_cache || !out)
     return QKRA_ERR_INVALID_ARGUMENT;
+  if (cfg->dtype == QKRA_BF16) {  // the step plan counts in int32
+    const long long steps = decode_units(cfg, num_seqs) * ((cache_capacity + kDecodeStepKeys - 1LL) / kDecodeStepKeys);
+    if (steps + 2LL * kDecodeWaves * kDecodeMinStepsPerWave >= (1LL << 31)) return QKRA_ERR_UNSUPPORTED;
+  }
   const size_t need = decode_workspace(cfg, num_seqs, max_cache_len);
   if (workspace_bytes < need) return QKRA_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace) return QKRA_ERR_INVALID_ARGUMENT;
@@ -298,7 +318,6 @@ QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv
   da.k_cache = k_cache;
   da.v_cache = v_cache;
   da.cache_lens = cache_lens;
-  da.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_q_bytes(cfg, num_seqs));
   da.out = out;
   da.num_q_heads = cfg->num_q_heads;
   da.num_kv_heads = cfg->num_kv_heads;
@@ -306,8 +325,22 @@ QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv
   da.dtype = cfg->dtype;
   da.cache_capacity = cache_capacity;
   da.num_seqs = num_seqs;
-  da.num_splits = decode_num_splits(max_cache_len);
   da.scale_log2 = softmax_scale_log2(cfg->head_dim);
+  char* ws = static_cast<char*>(workspace) + decode_q_bytes(cfg, num_seqs);
+  if (cfg->dtype == QKRA_BF16) {
+    da.plan = reinterpret_cast<int32_t*>(ws);
+    da.partials = reinterpret_cast<float*>(ws + decode_plan_bytes(cfg, num_seqs));
+    da.num_units = static_cast<int>(decode_units(cfg, num_seqs));
+    da.heads_per_wave = decode_heads_per_wave(cfg->num_q_heads / cfg->num_kv_heads);
+    err = timed(kKernelDecodePlan, stream, [&] { return launch_decode_plan(da, stream); });
+    if (err != hipSuccess) return hip_status(err);
+    err = timed(kKernelDecodeSplit, stream, [&] { return launch_decode_mfma(da, stream); });
+    if (err != hipSuccess) return hip_status(err);
+    err = timed(kKernelDecodeCombine, stream, [&] { return launch_decode_mfma_combine(da, stream); });
+    return hip_status(err);
+  }
+  da.partials = reinterpret_cast<float*>(ws);
+  da.num_splits = decode_num_splits(max_cache_len);
   err = timed(kKernelDecodeSplit, stream, [&] { return launch_decode_split(da, stream); });
   if (err != hipSuccess) return hip_status(err);
   err = timed(kKernelDecodeCombine, stream, [&] { return launch_decode_combine(da, stream); });
@@ -359,6 +392,7 @@ QKRA_API const char* qknorm_rope_attn_kernel_name(int32_t kernel_id) {
     case kKernelPrefillFp32: return "prefill_attn_fp32";
     case kKernelDecodeSplit: return "decode_attn_split";
     case kKernelDecodeCombine: return "decode_attn_combine";
+    case kKernelDecodePlan: return "decode_plan";
     default: return "unknown";
   }
 }

@@ -1,5 +1,6 @@
-// Kernels 3a/3b: decode attention, one new token per request, split over the
-// cached keys and merged with a log-sum-exp combine.
+// Kernels 3a/3b for fp32: decode attention, one new token per request, split
+// over the cached keys and merged with a log-sum-exp combine.  (bf16 runs on
+// the matrix cores with an evenly balanced split; see decode_mfma.hip.)
 //
 // The new token's query attends over cache slots 0..L_b of its request, the
 // L_b cached entries plus its own K/V that kernel 1 has just appended (concept
@@ -7,21 +8,18 @@
 // "transformer basics", "Prefill vs Decode": one more row of the causal
 // triangle).  Query head h reads KV head floor(h / G).
 //
-// Decode reads every cached K/V byte once and does only ~G multiply-adds per
-// byte, so it is bound by HBM bandwidth.  The kernel is laid out for that:
-//  * 3a: one workgroup per (request, KV head, split of 1024 keys), four
-//    wavefronts of 256 keys each; a wavefront serves the GW query heads of its
-//    group that share the KV head (GW = 4 for Qwen3's G = 4), so every K/V
-//    byte is fetched once for all of them.
+//  * 3a: one workgroup per (request, KV-head chunk, split of 1024 keys), four
+//    wavefronts of 256 keys each; a wavefront serves the GW (<= 2) query heads
+//    of its chunk that share the KV head, so every K/V byte is fetched once
+//    for all of them.
 //  * Eight lanes share one key row: each lane owns D/8 of it and issues
 //    16-byte loads, the eight lanes of a key reading 128 contiguous bytes per
-//    instruction; 8 keys per wavefront step, the next step's loads in flight
-//    while the current one is consumed.  Few registers per lane, so several
-//    wavefronts per SIMD hide HBM latency.
-//  * Scores via v_dot2_f32_bf16 (bf16) or fp32 FMA, summed over the 8 lanes
-//    of a key with DPP permutes.  Each lane octet keeps its own online-softmax
-//    state (running max, sum, partial output), so no cross-octet traffic is
-//    needed per step; the running max is only raised when a score exceeds it
+//    instruction; 8 keys per wavefront step, with three further steps' loads
+//    in flight (a ring of four register buffers) while one is consumed.  K/V
+//    are read exactly once, so the loads are non-temporal.
+//  * Scores by fp32 FMA, summed over the 8 lanes of a key with DPP permutes.
+//    Each lane octet keeps its own online-softmax state (running max, sum,
+//    partial output); the running max is only raised when a score exceeds it
 //    by more than 2^8, which keeps the arithmetic exact (every p and the sum
 //    use the same stale max) and makes rescaling rare.
 //  * The octets, then the four wavefronts (through LDS), are merged with the
@@ -37,21 +35,10 @@ namespace qkra {
 namespace {
 
 constexpr int SPLIT = kDecodeKeysPerSplit;
-constexpr int CHUNK = 16;
+constexpr float TAU = 8.0f;  // lazy-rescale threshold (log2 units)
 
-template <typename T> __device__ __forceinline__ void store_elem(T* p, float v);
-template <> __device__ __forceinline__ void store_elem<float>(float* p, float v) { *p = v; }
-template <> __device__ __forceinline__ void store_elem<bf16>(bf16* p, float v) { *p = static_cast<bf16>(v); }
-
-// Partial dot product of 16 bytes of q and k.
-__device__ __forceinline__ float dot16(u32x4 q, u32x4 k, float acc, bf16*) {
-  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.x), as_bf16x2(k.x), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.y), as_bf16x2(k.y), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.z), as_bf16x2(k.z), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.w), as_bf16x2(k.w), acc, false);
-  return acc;
-}
-__device__ __forceinline__ float dot16(u32x4 q, u32x4 k, float acc, float*) {
+// Partial dot product of 16 bytes (four fp32) of q and k.
+__device__ __forceinline__ float dot16(u32x4 q, u32x4 k, float acc) {
   acc += __uint_as_float(q.x) * __uint_as_float(k.x);
   acc += __uint_as_float(q.y) * __uint_as_float(k.y);
   acc += __uint_as_float(q.z) * __uint_as_float(k.z);
@@ -59,36 +46,24 @@ __device__ __forceinline__ float dot16(u32x4 q, u32x4 k, float acc, float*) {
   return acc;
 }
 
-// acc[0..n) += p * v for the elements of 16 bytes of v.
-__device__ __forceinline__ void axpy16(float* acc, float p, u32x4 v, bf16*) {
-  const u32x4 w = v;
+// acc[hh][off + e] += p[hh] * v[e] for the four fp32 of 16 bytes of v, all
+// heads at once.
+template <int GW, int EPL>
+__device__ __forceinline__ void axpy16_heads(float (&acc)[GW][EPL], int off, const float (&p)[GW], u32x4 v) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    acc[2 * i] += p * bf16_lo_to_f32(w[i]);
-    acc[2 * i + 1] += p * bf16_hi_to_f32(w[i]);
+    const float f = __uint_as_float(v[i]);
+#pragma unroll
+    for (int hh = 0; hh < GW; ++hh) acc[hh][off + i] += p[hh] * f;
   }
 }
-__device__ __forceinline__ void axpy16(float* acc, float p, u32x4 v, float*) {
-  acc[0] += p * __uint_as_float(v.x);
-  acc[1] += p * __uint_as_float(v.y);
-  acc[2] += p * __uint_as_float(v.z);
-  acc[3] += p * __uint_as_float(v.w);
-}
 
-// Sum over the 8 lanes of an aligned lane octet (xor 1, xor 2, then the
-// mirrored half-row), all through DPP lane permutes.
-__device__ __forceinline__ float octet_sum(float x) {
-  x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp_f32<0x141>(x);  // row_half_mirror
-  return x;
-}
-
-template <typename T, int D, int GW>
+template <int D, int GW>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(
-    const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
+    const float* __restrict__ q, const float* __restrict__ k_cache, const float* __restrict__ v_cache,
     const int32_t* __restrict__ cache_lens, float* __restrict__ partials, int num_q_heads, int num_kv_heads,
     int cache_capacity, int num_splits, int chunks_per_kv, float scale_log2) {
+  typedef float T;
   constexpr int ES = sizeof(T);
   constexpr int E16 = 16 / ES;          // elements per 16-byte load
   constexpr int LPK = 8;                // lanes per key row
@@ -96,7 +71,6 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   constexpr int EPL = D / LPK;          // elements per lane per key row
   constexpr int NL = EPL / E16;         // 16-byte loads per lane per key row
   constexpr int KPW = SPLIT / 4;        // keys per wavefront
-  constexpr float TAU = 8.0f;           // rescale only when the max grows by more than 2^TAU
 
   __shared__ float s_part[4][GW][D + 2];
 
@@ -144,49 +118,98 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   const T* kb = k_cache + head_off;
   const T* vb = v_cache + head_off;
 
-  u32x4 k0r[NL], v0r[NL], k1r[NL], v1r[NL];
+  // Four register buffers in a ring: three steps' loads stay in flight while
+  // the fourth step is consumed.  Loads are unconditional (rows past the
+  // split's end are clamped to its last row, a valid row) so that the only
+  // waits are the in-order ones on the buffer about to be consumed; the
+  // clamped duplicates are masked out of the softmax by `ok`.
+  u32x4 kr0[NL], vr0[NL], kr1[NL], vr1[NL], kr2[NL], vr2[NL], kr3[NL], vr3[NL];
   auto load = [&](u32x4 (&kr)[NL], u32x4 (&vr)[NL], int base) {
-    const int key = base + kl;
-    const bool ok = key < ke;
-    const T* kp = kb + static_cast<size_t>(ok ? key : 0) * D;
-    const T* vp = vb + static_cast<size_t>(ok ? key : 0) * D;
+    const int key = min(base + kl, ke - 1);
+    const T* kp = kb + static_cast<size_t>(key) * D;
+    const T* vp = vb + static_cast<size_t>(key) * D;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      kr[i] = ok ? *reinterpret_cast<const u32x4*>(kp + elem_off(i)) : u32x4{0, 0, 0, 0};
-      vr[i] = ok ? *reinterpret_cast<const u32x4*>(vp + elem_off(i)) : u32x4{0, 0, 0, 0};
+      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + elem_off(i)));
+      vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + elem_off(i)));
     }
   };
+  // One step: the GW heads run as independent instruction chains (no branch
+  // between them), so their dependent dot/reduce/exp sequences interleave.
   auto consume = [&](const u32x4 (&kr)[NL], const u32x4 (&vr)[NL], int base) {
     const bool ok = base + kl < ke;
+    float s[GW][2];
+#pragma unroll
+    for (int hh = 0; hh < GW; ++hh) s[hh][0] = s[hh][1] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+      for (int hh = 0; hh < GW; ++hh) s[hh][i & 1] = dot16(qr[hh][i], kr[i], s[hh][i & 1]);
+    float x[GW];
+#pragma unroll
+    for (int hh = 0; hh < GW; ++hh) x[hh] = s[hh][0] + s[hh][1];
+#pragma unroll
+    for (int hh = 0; hh < GW; ++hh) x[hh] += dpp_f32<0xB1>(x[hh]);   // quad_perm [1,0,3,2]
+#pragma unroll
+    for (int hh = 0; hh < GW; ++hh) x[hh] += dpp_f32<0x4E>(x[hh]);   // quad_perm [2,3,0,1]
+#pragma unroll
+    for (int hh = 0; hh < GW; ++hh) x[hh] += dpp_f32<0x141>(x[hh]);  // row_half_mirror
+    bool need = false;
 #pragma unroll
     for (int hh = 0; hh < GW; ++hh) {
-      float s = 0.f;
+      x[hh] *= scale_log2;
+      need |= ok && x[hh] > m_run[hh] + TAU;
+    }
+    if (__any(need)) {  // rare after the first key of each octet
 #pragma unroll
-      for (int i = 0; i < NL; ++i) s = dot16(qr[hh][i], kr[i], s, static_cast<T*>(nullptr));
-      s = octet_sum(s);
-      const float x = s * scale_log2;
-      if (ok && x > m_run[hh] + TAU) {  // rare after the first key of the octet
-        const float alpha = fast_exp2(m_run[hh] - x);
+      for (int hh = 0; hh < GW; ++hh) {
+        // alpha stays 1 where this head's max does not rise (the octet may
+        // still hold m = -inf, and 2^(-inf - -inf) would be NaN).
+        const bool up = ok && x[hh] > m_run[hh] + TAU;
+        const float m_new = up ? x[hh] : m_run[hh];
+        const float alpha = up ? fast_exp2(m_run[hh] - m_new) : 1.0f;
         l_run[hh] *= alpha;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[hh][e] *= alpha;
-        m_run[hh] = x;
+        m_run[hh] = m_new;
       }
-      const float p = ok ? fast_exp2(x - m_run[hh]) : 0.f;
-      l_run[hh] += p;
-#pragma unroll
-      for (int i = 0; i < NL; ++i) axpy16(&acc[hh][i * E16], p, vr[i], static_cast<T*>(nullptr));
     }
+    float p[GW];
+#pragma unroll
+    for (int hh = 0; hh < GW; ++hh) {
+      p[hh] = ok ? fast_exp2(x[hh] - m_run[hh]) : 0.f;
+      l_run[hh] += p[hh];
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) axpy16_heads<GW, EPL>(acc, i * E16, p, vr[i]);
   };
 
   if (ks < ke) {
-    load(k0r, v0r, ks);
-    for (int base = ks; base < ke; base += 2 * KPS) {
-      const bool second = base + KPS < ke;
-      if (second) load(k1r, v1r, base + KPS);
-      consume(k0r, v0r, base);
-      if (base + 2 * KPS < ke) load(k0r, v0r, base + 2 * KPS);
-      if (second) consume(k1r, v1r, base + KPS);
+    // Straight-line ring: every load and consume is issued unconditionally
+    // (trailing steps read clamped rows and contribute p = 0), which keeps the
+    // waits exact: consuming buffer j waits only for buffer j's loads.
+    const int nquads = (ke - ks + 4 * KPS - 1) / (4 * KPS);
+    // The scheduling barriers keep each refill ahead of the next consume (the
+    // scheduler would otherwise sink the loads and shorten the ring).
+    __builtin_amdgcn_sched_barrier(0);
+    load(kr0, vr0, ks);
+    __builtin_amdgcn_sched_barrier(0);
+    load(kr1, vr1, ks + KPS);
+    __builtin_amdgcn_sched_barrier(0);
+    load(kr2, vr2, ks + 2 * KPS);
+    for (int it = 0, base = ks; it < nquads; ++it, base += 4 * KPS) {
+      load(kr3, vr3, base + 3 * KPS);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(kr0, vr0, base);
+      load(kr0, vr0, base + 4 * KPS);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(kr1, vr1, base + KPS);
+      load(kr1, vr1, base + 5 * KPS);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(kr2, vr2, base + 2 * KPS);
+      load(kr2, vr2, base + 6 * KPS);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(kr3, vr3, base + 3 * KPS);
     }
   }
 
@@ -246,10 +269,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   }
 }
 
-template <typename T, int D>
+template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ partials,
                                                             const int32_t* __restrict__ cache_lens,
-                                                            T* __restrict__ out, int num_q_heads, int num_splits) {
+                                                            float* __restrict__ out, int num_q_heads, int num_splits) {
   constexpr int PER = D / 64;
   const int bh = blockIdx.x;
   const int b = bh / num_q_heads;
@@ -269,56 +292,56 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     for (int e = 0; e < PER; ++e) o[e] += p[2 + lane + 64 * e] * w;
   }
   const float inv = 1.0f / l;
-  T* dst = out + static_cast<size_t>(bh) * D;
+  float* dst = out + static_cast<size_t>(bh) * D;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) store_elem<T>(dst + lane + 64 * e, o[e] * inv);
+  for (int e = 0; e < PER; ++e) dst[lane + 64 * e] = o[e] * inv;
 }
 
-template <typename T, int D, int GW>
+template <int D, int GW>
 hipError_t launch_split_typed(const DecodeAttnArgs& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   const int chunks_per_kv = group / GW;
   const long long items = static_cast<long long>(a.num_seqs) * a.num_kv_heads * chunks_per_kv * a.num_splits;
   if (items <= 0) return hipSuccess;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((decode_split_kernel<T, D, GW>), dim3(static_cast<unsigned>(items)), dim3(256), 0, stream,
-                     static_cast<const T*>(a.q), static_cast<const T*>(a.k_cache), static_cast<const T*>(a.v_cache),
-                     a.cache_lens, a.partials, a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.num_splits,
-                     chunks_per_kv, a.scale_log2);
+  hipLaunchKernelGGL((decode_split_kernel<D, GW>), dim3(static_cast<unsigned>(items)), dim3(256), 0, stream,
+                     static_cast<const float*>(a.q), static_cast<const float*>(a.k_cache),
+                     static_cast<const float*>(a.v_cache), a.cache_lens, a.partials, a.num_q_heads, a.num_kv_heads,
+                     a.cache_capacity, a.num_splits, chunks_per_kv, a.scale_log2);
   return hipGetLastError();
 }
 
-template <typename T, int D>
+// Two heads per wavefront at most: four fp32 heads would not fit in registers.
+template <int D>
 hipError_t launch_split_dim(const DecodeAttnArgs& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
-  if (group % 4 == 0) return launch_split_typed<T, D, 4>(a, stream);
-  if (group % 2 == 0) return launch_split_typed<T, D, 2>(a, stream);
-  return launch_split_typed<T, D, 1>(a, stream);
+  if (group % 2 == 0) return launch_split_typed<D, 2>(a, stream);
+  return launch_split_typed<D, 1>(a, stream);
 }
 
-template <typename T, int D>
+template <int D>
 hipError_t launch_combine_typed(const DecodeAttnArgs& a, hipStream_t stream) {
   const long long items = static_cast<long long>(a.num_seqs) * a.num_q_heads;
   if (items <= 0) return hipSuccess;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(static_cast<unsigned>(items)), dim3(64), 0, stream,
-                     a.partials, a.cache_lens, static_cast<T*>(a.out), a.num_q_heads, a.num_splits);
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(static_cast<unsigned>(items)), dim3(64), 0, stream,
+                     a.partials, a.cache_lens, static_cast<float*>(a.out), a.num_q_heads, a.num_splits);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode_split(const DecodeAttnArgs& a, hipStream_t stream) {
-  const bool bf = a.dtype == 0;
-  if (a.head_dim == 128) return bf ? launch_split_dim<bf16, 128>(a, stream) : launch_split_dim<float, 128>(a, stream);
-  if (a.head_dim == 64) return bf ? launch_split_dim<bf16, 64>(a, stream) : launch_split_dim<float, 64>(a, stream);
+  if (a.dtype != 1) return hipErrorInvalidValue;  // fp32 only
+  if (a.head_dim == 128) return launch_split_dim<128>(a, stream);
+  if (a.head_dim == 64) return launch_split_dim<64>(a, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_combine(const DecodeAttnArgs& a, hipStream_t stream) {
-  const bool bf = a.dtype == 0;
-  if (a.head_dim == 128) return bf ? launch_combine_typed<bf16, 128>(a, stream) : launch_combine_typed<float, 128>(a, stream);
-  if (a.head_dim == 64) return bf ? launch_combine_typed<bf16, 64>(a, stream) : launch_combine_typed<float, 64>(a, stream);
+  if (a.dtype != 1) return hipErrorInvalidValue;
+  if (a.head_dim == 128) return launch_combine_typed<128>(a, stream);
+  if (a.head_dim == 64) return launch_combine_typed<64>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -1,0 +1,442 @@
+// Kernels 3p/3a/3b for bf16: decode attention on the matrix cores with an
+// evenly balanced split of the cached keys (one new token per request).
+//
+// The new token's query attends over cache slots 0..L_b of its request, the
+// L_b cached entries plus its own K/V that kernel 1 has just appended (concept
+// chapter "Chapter 3 Forward Pass and Generation", section 4.2; jq-wei
+// "transformer basics", "Prefill vs Decode": one more row of the causal
+// triangle).  Query head h reads KV head floor(h / G).
+//
+// Decode reads every cached K/V byte once and does ~G multiply-adds per byte,
+// so it is bound by HBM bandwidth; the design keeps every wavefront streaming:
+//  * Work: a unit is (request b, KV head g, chunk of GW query heads of g); it
+//    covers ceil(n_b / 32) steps of 32 keys, n_b = L_b + 1.  All units' steps
+//    are laid end to end and cut into equal contiguous ranges, one per
+//    wavefront of a persistent grid, so every wavefront streams the same
+//    number of bytes whatever the length mix.  A wavefront whose range crosses
+//    unit boundaries carries its load pipeline across them and writes one
+//    partial (m, l, o) per unit portion; 3b merges a unit's portions.
+//  * 3p (plan) computes the step prefix over units, the range length and each
+//    wavefront's first unit on the device, from the cache lengths.
+//  * Per 32-key step a wavefront loads its K and V rows lane-linearly (1 KB of
+//    contiguous rows per instruction, non-temporal: read once) into registers,
+//    while it computes the previous step from LDS; the rows then go to padded
+//    per-wavefront LDS tiles.
+//  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 with the GW
+//    query heads as the 16 columns (unused columns are zero).  The score
+//    accumulators hold, for lane l, query l%16 and keys 4g+r and 16+4g+r
+//    (g = l/16, r = 0..3): exactly the k-slots of a 32-key B operand, so P^T
+//    needs no lane exchange.  V^T comes from ds_read_b64_tr_b16, whose 16-lane
+//    transpose hands lane i four keys of one d column.
+//  * Online softmax per query in the log2 domain; the running max is only
+//    raised when a score exceeds it by more than 2^8, which keeps the
+//    arithmetic exact (every p and the sum use the same stale max) and makes
+//    rescaling rare.
+//  * 3b merges the portions of a (request, head) in a fixed order with the
+//    log-sum-exp rule m = max m_s, l = sum l_s 2^(m_s - m),
+//    o = sum o_s 2^(m_s - m) / l.  Deterministic, no atomics.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace qkra {
+namespace {
+
+constexpr int STEP = kDecodeStepKeys;  // keys per wavefront step
+constexpr float TAU = 8.0f;            // lazy-rescale threshold (log2 units)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(reinterpret_cast<__attribute__((address_space(3))) char*>(
+          reinterpret_cast<uintptr_t>(p))));
+}
+
+// Max of a value over lanes l, l ^ 16, l ^ 32 and l ^ 48 (gfx950 row swaps).
+__device__ __forceinline__ float quarter_max(float x) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
+__device__ __forceinline__ int unit_steps(const int32_t* cache_lens, int unit, int nchunks, int cache_capacity) {
+  const int nkeys = min(cache_lens[unit / nchunks] + 1, cache_capacity);
+  return (nkeys + STEP - 1) / STEP;
+}
+
+// ---- 3p: plan = [T, per, S0[0..N], first_unit[0..W)] (one workgroup).
+// S0[i] is the first global step of unit i (S0[N] = T, the total), per the
+// steps per wavefront, first_unit[w] the unit holding step w*per (-1: idle).
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t* __restrict__ cache_lens,
+                                                                   int32_t* __restrict__ plan, int num_units,
+                                                                   int nchunks, int cache_capacity, int num_waves,
+                                                                   int min_steps) {
+  __shared__ int32_t s_scan[kPlanThreads];
+  const int tid = threadIdx.x;
+  const int per_thread = (num_units + kPlanThreads - 1) / kPlanThreads;
+  const int i0 = min(tid * per_thread, num_units);
+  const int i1 = min(i0 + per_thread, num_units);
+  int local = 0;
+  for (int i = i0; i < i1; ++i) local += unit_steps(cache_lens, i, nchunks, cache_capacity);
+  s_scan[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive scan of the per-thread sums
+    const int v = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += v;
+    __syncthreads();
+  }
+  int32_t* S0 = plan + 2;
+  int run = s_scan[tid] - local;
+  for (int i = i0; i < i1; ++i) {
+    S0[i] = run;
+    run += unit_steps(cache_lens, i, nchunks, cache_capacity);
+  }
+  const int total = s_scan[kPlanThreads - 1];
+  const int per = max((total + num_waves - 1) / num_waves, min_steps);
+  if (tid == 0) {
+    plan[0] = total;
+    plan[1] = per;
+    S0[num_units] = total;
+  }
+  __syncthreads();  // S0 complete and visible to the workgroup
+  int32_t* first = plan + 3 + num_units;
+  for (int w = tid; w < num_waves; w += kPlanThreads) {
+    const long long t0 = static_cast<long long>(w) * per;
+    int unit = -1;
+    if (t0 < total) {  // last unit whose first step is <= t0
+      int lo = 0, hi = num_units;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (S0[mid] <= t0) lo = mid; else hi = mid;
+      }
+      unit = lo;
+    }
+    first[w] = unit;
+  }
+}
+
+// ---- 3a: one wavefront per range of steps; 4 independent wavefronts per workgroup.
+template <int D, int GW>
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k_cache, const bf16* __restrict__ v_cache,
+    const int32_t* __restrict__ cache_lens, const int32_t* __restrict__ plan, float* __restrict__ partials,
+    int num_q_heads, int num_kv_heads, int cache_capacity, int chunks_per_kv, int num_units, float scale_log2) {
+  constexpr int KS = D / 32;               // 32-d steps of the score product
+  constexpr int DBLK = D / 16;             // 16-d blocks of the output
+  constexpr int CPR = D / 8;               // 16-byte chunks per key row
+  constexpr int VLOADS = STEP * CPR / 64;  // 16-byte loads per lane per step, for K and for V
+  constexpr int PREC = D + 4;              // floats per partial record: m, l, 2 pad, o[D]
+  static_assert(GW <= 16, "at most 16 query heads per wavefront");
+  // Per wavefront: one K tile and one V tile of STEP rows, each row padded by
+  // 16 bytes, so that the A-operand reads of 16 K rows hit 16 distinct bank
+  // quads and the transpose reads of 16 V rows cover every bank exactly twice
+  // (the two-pass minimum for 512 bytes).
+  constexpr int VROW = D + 8;              // elements per padded row
+  constexpr int TILE = STEP * VROW;        // elements per tile
+  __shared__ __attribute__((aligned(16))) bf16 lds[4][2 * TILE];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + wave;
+  const int total = plan[0], per = plan[1];
+  const int32_t* S0 = plan + 2;
+  const int first_unit = plan[3 + num_units + w];
+  if (first_unit < 0) return;  // idle wavefront (no barriers below)
+  const int t0 = w * per;
+  const int t1 = min(t0 + per, total);
+
+  const int group = num_q_heads / num_kv_heads;
+  const int nchunks = num_kv_heads * chunks_per_kv;
+  const int l16 = lane & 15;  // query column / key row within a 16-key block
+  const int lg = lane >> 4;   // lane group
+  bf16* ktile = lds[wave];
+  bf16* vtile = ktile + TILE;
+
+  // Unit geometry (all wave-uniform).
+  struct Unit {
+    int s0, s1, nkeys, b, h0;
+    const bf16* kb;
+    const bf16* vb;
+  };
+  auto unit_at = [&](int i) {
+    Unit u;
+    u.s0 = S0[i];
+    u.s1 = S0[i + 1];
+    u.b = i / nchunks;
+    const int hc = i % nchunks;
+    const int g = hc / chunks_per_kv;
+    u.h0 = g * group + (hc % chunks_per_kv) * GW;
+    u.nkeys = min(cache_lens[u.b] + 1, cache_capacity);
+    const size_t head_off = (static_cast<size_t>(u.b) * num_kv_heads + g) * cache_capacity * D;
+    u.kb = k_cache + head_off;
+    u.vb = v_cache + head_off;
+    return u;
+  };
+
+  // Q^T (B operand): slot (step s, group lg, e) <-> d = 32*s + 8*lg + e.
+  bf16x8 qf[KS];
+  auto load_q = [&](const Unit& u) {
+    const bool valid = l16 < GW;
+    const bf16* src = q + (static_cast<size_t>(u.b) * num_q_heads + u.h0 + (valid ? l16 : 0)) * D + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(src + 32 * s);
+      if (!valid) v = bf16x8{};
+      qf[s] = v;
+    }
+  };
+
+  f32x4 o[DBLK];
+  float m_run, l_run;
+  auto reset = [&]() {
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) o[db] = f32x4{};
+    m_run = kNegInf;
+    l_run = 0.f;
+  };
+
+  // One step of K and V rows, loaded lane-linearly (each instruction reads
+  // 1 KB of contiguous rows, 16 bytes per lane) with buffer loads over the
+  // unit's keys: keys at or past n_b, or any key when `live` is false, read as
+  // zero without touching memory (their scores are masked and their
+  // probabilities are zero).
+  const uint32_t lin = static_cast<uint32_t>(16 * lane);
+  u32x4 kst[VLOADS], vst[VLOADS];
+  auto load_step = [&](const Unit& u, int t, bool live) {
+    const uint32_t range = live ? static_cast<uint32_t>(u.nkeys) * (D * 2) : 0u;
+    const auto krs = buffer_rsrc(u.kb, range);
+    const auto vrs = buffer_rsrc(u.vb, range);
+    const uint32_t off = lin + static_cast<uint32_t>(t - u.s0) * (STEP * D * 2);
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {  // 16-byte chunk 64*i + lane of the step's rows
+      kst[i] = buffer_load16<true>(krs, off + 1024 * i);
+      vst[i] = buffer_load16<true>(vrs, off + 1024 * i);
+    }
+  };
+  auto store_step = [&]() {
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int c = 64 * i + lane;
+      const int at = (c / CPR) * VROW + (c % CPR) * 8;
+      *reinterpret_cast<u32x4*>(ktile + at) = kst[i];
+      *reinterpret_cast<u32x4*>(vtile + at) = vst[i];
+    }
+  };
+
+  // The transpose read of lane group lg covers key rows 4*lg + j/4 (first
+  // half) and 16 + 4*lg + j/4 (second half), j = lane % 16.
+  const int r1 = 4 * lg + (l16 >> 2);
+  const int r2 = r1 + 16;
+  auto step = [&](int key0, int nkeys) {
+    // ---- scores: A operand of key block kblk, step s = K[16*kblk + l16][32*s + 8*lg ..]
+    bf16x8 kf[2][KS];
+#pragma unroll
+    for (int kblk = 0; kblk < 2; ++kblk)
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        kf[kblk][s] = *reinterpret_cast<const bf16x8*>(ktile + (16 * kblk + l16) * VROW + 32 * s + 8 * lg);
+    f32x4 sc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int kblk = 0; kblk < 2; ++kblk)
+        sc[kblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kblk][s], qf[s], sc[kblk], 0, 0, 0);
+    // ---- V^T operands, read while the softmax runs
+    bf16x8 vf[DBLK];
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const int col = 16 * db + 4 * (l16 & 3);  // element column read by this lane
+      const s16x4 a0 = lds_read_tr16(vtile + r1 * VROW + col);
+      const s16x4 a1 = lds_read_tr16(vtile + r2 * VROW + col);
+      vf[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    // ---- softmax: register t of the B operand holds key 4*lg + t (t < 4) or 16 + 4*lg + t-4
+    float x[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int key = key0 + (t < 4 ? 4 * lg + t : 16 + 4 * lg + t - 4);
+      x[t] = key < nkeys ? sc[t >> 2][t & 3] : kNegInf;
+    }
+    float mloc = x[0];
+#pragma unroll
+    for (int t = 1; t < 8; ++t) mloc = fmaxf(mloc, x[t]);
+    mloc *= scale_log2;
+    if (__any(mloc > m_run + TAU)) {  // rare: raise the max of the queries that need it
+      const float mt = quarter_max(mloc);
+      const bool up = mt > m_run + TAU;
+      const float alpha = up ? fast_exp2(m_run - mt) : 1.0f;
+      if (up) m_run = mt;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
+    }
+    uint32_t wpk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = fast_exp2(__builtin_fmaf(x[2 * e], scale_log2, -m_run));
+      const float p1 = fast_exp2(__builtin_fmaf(x[2 * e + 1], scale_log2, -m_run));
+      wpk[e] = pack_bf16x2(p0, p1);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wpk[e]),
+                                              bf16x2{static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)}, l_run, false);
+    }
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{wpk[0], wpk[1], wpk[2], wpk[3]});
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf, o[db], 0, 0, 0);
+  };
+
+  // Partial record of unit i's portion: lane l holds d = 16*db + 4*lg + r of
+  // query l%16; l is summed over the four lane groups of a query.  Slot i + w
+  // is unique per (unit, wavefront) pair that meet.
+  auto write_partial = [&](int i) {
+    float l_tot = l_run + xor_shuffle(l_run, 16);
+    l_tot += xor_shuffle(l_tot, 32);
+    if (l16 < GW) {
+      float* rec = partials + (static_cast<size_t>(i + w) * GW + l16) * PREC;
+      if (lg == 0) *reinterpret_cast<f32x2*>(rec) = f32x2{m_run, l_tot};
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) *reinterpret_cast<f32x4*>(rec + 4 + 16 * db + 4 * lg) = o[db];
+    }
+  };
+
+  // Flat loop over the wavefront's steps; the loads of step t + 1 (possibly
+  // of the next unit) are in flight while step t is computed from the tiles.
+  int ci = first_unit;  // unit of the step being computed
+  Unit cu = unit_at(ci);
+  int pi = ci;          // unit of the step being loaded
+  Unit pu = cu;
+  load_q(cu);
+  reset();
+  load_step(pu, t0, true);
+  store_step();
+  for (int t = t0; t < t1; ++t) {
+    const int tn = t + 1;
+    const bool more = tn < t1;
+    if (more && tn == pu.s1) pu = unit_at(++pi);
+    load_step(pu, more ? tn : pu.s0, more);
+    step((t - cu.s0) * STEP, cu.nkeys);
+    if (tn == cu.s1 || !more) {
+      write_partial(ci);
+      if (more) {
+        ci = pi;
+        cu = pu;
+        load_q(cu);
+        reset();
+      }
+    }
+    store_step();  // the step above has read the tiles
+  }
+}
+
+// ---- 3b: merge the portions of one (request, head); one wavefront each.
+template <int D>
+__global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ partials,
+                                                            const int32_t* __restrict__ plan, bf16* __restrict__ out,
+                                                            int num_q_heads, int num_kv_heads, int chunks_per_kv,
+                                                            int gw) {
+  constexpr int PER_LANE = D / 64;
+  constexpr int PREC = D + 4;
+  const int bh = blockIdx.x;
+  const int b = bh / num_q_heads, h = bh % num_q_heads;
+  const int group = num_q_heads / num_kv_heads;
+  const int g = h / group, within = h % group;
+  const int i = (b * num_kv_heads + g) * chunks_per_kv + within / gw;
+  const int hh = within % gw;
+  const int per = plan[1];
+  const int32_t* S0 = plan + 2;
+  const int s_first = S0[i] / per, s_last = (S0[i + 1] - 1) / per;
+  const int lane = threadIdx.x;
+  auto rec = [&](int s) { return partials + (static_cast<size_t>(i + s) * gw + hh) * PREC; };
+  float m = kNegInf;
+  for (int s = s_first; s <= s_last; ++s) m = fmaxf(m, rec(s)[0]);
+  float l = 0.f, acc[PER_LANE];
+#pragma unroll
+  for (int e = 0; e < PER_LANE; ++e) acc[e] = 0.f;
+  for (int s = s_first; s <= s_last; ++s) {
+    const float* r = rec(s);
+    const float wgt = fast_exp2(r[0] - m);
+    l += r[1] * wgt;
+#pragma unroll
+    for (int e = 0; e < PER_LANE; ++e) acc[e] += r[4 + lane + 64 * e] * wgt;
+  }
+  const float inv = 1.0f / l;
+  bf16* dst = out + static_cast<size_t>(bh) * D;
+#pragma unroll
+  for (int e = 0; e < PER_LANE; ++e) dst[lane + 64 * e] = static_cast<bf16>(acc[e] * inv);
+}
+
+template <int D, int GW>
+hipError_t launch_mfma_typed(const DecodeAttnArgs& a, hipStream_t stream) {
+  const int chunks_per_kv = (a.num_q_heads / a.num_kv_heads) / GW;
+  hipLaunchKernelGGL((decode_mfma_kernel<D, GW>), dim3(kDecodeWaves / 4), dim3(256), 0, stream,
+                     static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k_cache),
+                     static_cast<const bf16*>(a.v_cache), a.cache_lens, a.plan, a.partials, a.num_q_heads,
+                     a.num_kv_heads, a.cache_capacity, chunks_per_kv, a.num_units, a.scale_log2);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_mfma_dim(const DecodeAttnArgs& a, hipStream_t stream) {
+  switch (a.heads_per_wave) {
+    case 16: return launch_mfma_typed<D, 16>(a, stream);
+    case 15: return launch_mfma_typed<D, 15>(a, stream);
+    case 14: return launch_mfma_typed<D, 14>(a, stream);
+    case 13: return launch_mfma_typed<D, 13>(a, stream);
+    case 12: return launch_mfma_typed<D, 12>(a, stream);
+    case 11: return launch_mfma_typed<D, 11>(a, stream);
+    case 10: return launch_mfma_typed<D, 10>(a, stream);
+    case 9: return launch_mfma_typed<D, 9>(a, stream);
+    case 8: return launch_mfma_typed<D, 8>(a, stream);
+    case 7: return launch_mfma_typed<D, 7>(a, stream);
+    case 6: return launch_mfma_typed<D, 6>(a, stream);
+    case 5: return launch_mfma_typed<D, 5>(a, stream);
+    case 4: return launch_mfma_typed<D, 4>(a, stream);
+    case 3: return launch_mfma_typed<D, 3>(a, stream);
+    case 2: return launch_mfma_typed<D, 2>(a, stream);
+    case 1: return launch_mfma_typed<D, 1>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_plan(const DecodeAttnArgs& a, hipStream_t stream) {
+  if (a.num_units <= 0) return hipSuccess;
+  const int nchunks = a.num_kv_heads * (a.num_q_heads / a.num_kv_heads / a.heads_per_wave);
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.cache_lens, a.plan,
+                     a.num_units, nchunks, a.cache_capacity, kDecodeWaves, kDecodeMinStepsPerWave);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma(const DecodeAttnArgs& a, hipStream_t stream) {
+  if (a.num_units <= 0) return hipSuccess;
+  if (a.head_dim == 128) return launch_mfma_dim<128>(a, stream);
+  if (a.head_dim == 64) return launch_mfma_dim<64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_mfma_combine(const DecodeAttnArgs& a, hipStream_t stream) {
+  const long long items = static_cast<long long>(a.num_seqs) * a.num_q_heads;
+  if (items <= 0) return hipSuccess;
+  if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const int chunks_per_kv = (a.num_q_heads / a.num_kv_heads) / a.heads_per_wave;
+  if (a.head_dim == 128) {
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(static_cast<unsigned>(items)), dim3(64), 0, stream,
+                       a.partials, a.plan, static_cast<bf16*>(a.out), a.num_q_heads, a.num_kv_heads, chunks_per_kv,
+                       a.heads_per_wave);
+  } else if (a.head_dim == 64) {
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(static_cast<unsigned>(items)), dim3(64), 0, stream,
+                       a.partials, a.plan, static_cast<bf16*>(a.out), a.num_q_heads, a.num_kv_heads, chunks_per_kv,
+                       a.heads_per_wave);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qkra

@@ -61,4 +61,17 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Butterfly exchange across lanes (xor of the lane id) within a wavefront.
 __device__ __forceinline__ float xor_shuffle(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Raw buffer resource over [base, base + bytes) (stride 0, 32-bit data format
+// as gfx9-family untyped accesses require): a load at a byte offset >= bytes
+// returns zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// 16-byte buffer load at a per-lane byte offset; NT marks it non-temporal.
+template <bool NT>
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, NT ? 2 : 0));
+}
+
 }  // namespace qkra

@@ -15,7 +15,8 @@ enum KernelId : int {
   kKernelDecodeSplit = 3,
   kKernelDecodeCombine = 4,
   kKernelQkNormRopeDecode = 5,
-  kNumKernels = 6,
+  kKernelDecodePlan = 6,
+  kNumKernels = 7,
 };
 
 // Kernel 1: per token row, RMSNorm + RoPE of the Q and K heads; q~ to
@@ -52,23 +53,53 @@ hipError_t launch_prefill_attn_bf16(const PrefillAttnArgs& a, hipStream_t stream
 hipError_t launch_prefill_attn_fp32(const PrefillAttnArgs& a, hipStream_t stream);
 
 // Kernels 3a/3b: split-KV decode attention and the log-sum-exp combine.
-constexpr int kDecodeKeysPerSplit = 1024;  // keys per workgroup (4 wavefronts x 256)
+//
+// fp32 (decode.hip): one workgroup per (request, KV-head chunk, split of
+// kDecodeKeysPerSplit keys); partials [B, Hq, num_splits, D + 2] = (m, l, o[D]).
+constexpr int kDecodeKeysPerSplit = 1024;  // keys per workgroup (4 wavefronts)
 
 inline int decode_num_splits(int max_cache_len) {
   return (max_cache_len + 1 + kDecodeKeysPerSplit - 1) / kDecodeKeysPerSplit;
 }
+
+// bf16 (decode_mfma.hip): units (request, KV head, chunk of GW query heads)
+// cut into steps of kDecodeStepKeys keys; the steps of all units are split
+// evenly over kDecodeWaves persistent wavefronts (at least
+// kDecodeMinStepsPerWave each).  Kernel 3p writes the plan
+// [T, per, S0[0..N], first_unit[0..W)] (int32), 3a one partial record
+// (m, l, pad, pad, o[D]) fp32 per (unit, wavefront) that meet, at slot
+// unit + wavefront of [N + W, GW, D + 4].
+constexpr int kDecodeStepKeys = 32;
+constexpr int kDecodeWaves = 2048;          // 256 CUs x 2 workgroups x 4 wavefronts
+constexpr int kDecodeMinStepsPerWave = 8;
+
+// Query heads per wavefront on the matrix-core path: the whole group if it
+// fits in the 16 columns of the MFMA tile, else its largest divisor that does.
+inline int decode_heads_per_wave(int group) {
+  for (int c = 16; c >= 1; --c)
+    if (group % c == 0) return c;
+  return 1;
+}
+
+inline size_t decode_plan_ints(long long num_units) { return static_cast<size_t>(3 + num_units + kDecodeWaves); }
 
 struct DecodeAttnArgs {
   const void* q;            // q~ [B, Hq, D]
   const void* k_cache;      // [B, Hkv, S, D]
   const void* v_cache;
   const int32_t* cache_lens;
-  float* partials;          // [B, Hq, num_splits, D + 2] fp32: (m, l, o[D])
+  float* partials;          // fp32 partial records (layout per path, above)
+  int32_t* plan;            // bf16 path: the step plan
   void* out;                // [B, Hq*D]
-  int num_q_heads, num_kv_heads, head_dim, dtype, cache_capacity, num_seqs, num_splits;
+  int num_q_heads, num_kv_heads, head_dim, dtype, cache_capacity, num_seqs;
+  int num_splits;           // fp32 path
+  int num_units, heads_per_wave;  // bf16 path
   float scale_log2;
 };
 hipError_t launch_decode_split(const DecodeAttnArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeAttnArgs& a, hipStream_t stream);
+hipError_t launch_decode_plan(const DecodeAttnArgs& a, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeAttnArgs& a, hipStream_t stream);
+hipError_t launch_decode_mfma_combine(const DecodeAttnArgs& a, hipStream_t stream);
 
 }  // namespace qkra

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
       const bool need = mx[qb] > m_run[qb] + TAU;
       if (__any(need)) {
         const float m_new = need ? mx[qb] : m_run[qb];
-        const float alpha = fast_exp2(m_run[qb] - m_new);
+        const float alpha = need ? fast_exp2(m_run[qb] - m_new) : 1.0f;
         l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;

@@ -131,8 +131,14 @@ QKRA_API int32_t qknorm_rope_attn_prefill(const qkra_config* cfg, const void* qk
  *   out            [num_seqs, Hq*D], write-only.
  *   workspace      at least qknorm_rope_attn_workspace_bytes(cfg,
  *                  QKRA_MODE_DECODE, num_seqs, max_cache_len) bytes: q~ as
- *                  [num_seqs, Hq, D] in the dtype, then fp32 split partials.
- * num_seqs == 0 is a no-op returning QKRA_OK.
+ *                  [num_seqs, Hq, D] in the dtype, then (bf16) an int32 step
+ *                  plan and fp32 partial records of an even split of all
+ *                  requests' keys over a fixed set of wavefronts, or (fp32)
+ *                  fp32 partials per 1024-key split.
+ * num_seqs == 0 is a no-op returning QKRA_OK.  bf16 calls whose step count
+ * num_seqs * Hkv * (G / GW) * ceil(cache_capacity / 32) reaches 2^31 (GW: the
+ * query heads per matrix tile, the largest divisor of G up to 16) return
+ * QKRA_ERR_UNSUPPORTED.
  */
 QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv,
                                          const void* q_norm_weight, const void* k_norm_weight,

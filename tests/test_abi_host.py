@@ -47,12 +47,25 @@ def test_workspace_bytes():
     # prefill: q~ [N, Hq, D] bf16, rounded up to 256 bytes
     assert da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_PREFILL, 100, 100) == 100 * 32 * 128 * 2
     assert da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_PREFILL, 1, 1) == 8192
-    # decode: q~ then fp32 (m, l, o[D]) per (request, head, 1024-key split)
-    b, L = 3, 2047
+    up = lambda n: -(-n // 256) * 256
+    # bf16 decode: q~, then the int32 step plan [T, per, S0[0..N], first[0..W)]
+    # over N = b * Hkv units (G = 4 heads per tile), then fp32 records
+    # (m, l, pad, pad, o[D]) for N + W (unit, wavefront) slots of 4 heads.
+    b, L, W = 3, 2047, 2048
+    n_units = b * 8
+    q_bytes = up(b * 32 * 128 * 2)
+    plan_bytes = up((3 + n_units + W) * 4)
+    rec_bytes = up((n_units + W) * 4 * 132 * 4)
+    assert da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_DECODE, b, L) == q_bytes + plan_bytes + rec_bytes
+    # fp32 decode: q~ then fp32 (m, l, o[D]) per (request, head, 1024-key split)
+    cfg32 = da.make_config(32, 8, 128, da.QKRA_FP32)
     splits = (L + 1 + 1023) // 1024
-    q_bytes = -(-(b * 32 * 128 * 2) // 256) * 256
-    p_bytes = -(-(b * 32 * splits * 130 * 4) // 256) * 256
-    assert da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_DECODE, b, L) == q_bytes + p_bytes
+    assert da.qknorm_rope_attn_workspace_bytes(cfg32, da.QKRA_MODE_DECODE, b, L) == \
+        up(b * 32 * 128 * 4) + up(b * 32 * splits * 130 * 4)
+    # a group of 12 heads runs as one tile of 12 columns; 48 heads over 3 KV heads: 16 per tile
+    cfg12 = da.make_config(12, 1, 64, da.QKRA_BF16)
+    assert da.qknorm_rope_attn_workspace_bytes(cfg12, da.QKRA_MODE_DECODE, 2, 10) == \
+        up(2 * 12 * 64 * 2) + up((3 + 2 + W) * 4) + up((2 + W) * 12 * 68 * 4)
     bad = da.make_config(5, 2, 128)
     assert da.qknorm_rope_attn_workspace_bytes(bad, da.QKRA_MODE_PREFILL, 10, 10) == 0
     assert da.qknorm_rope_attn_workspace_bytes(cfg, 7, 10, 10) == 0
@@ -118,7 +131,7 @@ def decode_args(**over):
     a = dict(qkv=BASE, q_norm_weight=BASE + 64 * MB, k_norm_weight=BASE + 65 * MB, positions=BASE + 66 * MB,
              cache_lens=BASE + 67 * MB, num_seqs=4, max_cache_len=100, k_cache=BASE + 100 * MB,
              v_cache=BASE + 200 * MB, cache_capacity=101, out=BASE + 300 * MB, workspace=BASE + 400 * MB,
-             workspace_bytes=1 << 20, stream=0)
+             workspace_bytes=16 * MB, stream=0)
     a.update(over)
     return cfg, a
 
@@ -141,6 +154,8 @@ def call_decode(cfg, a):
     (dict(k_cache=BASE + 16 * 1024), da.QKRA_ERR_ALIASING),                     # cache over qkv [B, 48*128] bf16
     (dict(out=BASE + 200 * MB + 4096), da.QKRA_ERR_ALIASING),                    # out over the V cache
     (dict(workspace=BASE + 67 * MB), da.QKRA_ERR_ALIASING),                      # workspace over cache_lens
+    # bf16 step plan counts in int32: 4096 * 8 units of 2^21 / 32 steps = 2^31
+    (dict(num_seqs=4096, cache_capacity=1 << 21), da.QKRA_ERR_UNSUPPORTED),
 ])
 def test_decode_argument_checks(over, status):
     cfg, a = decode_args(**over)
