@@ -36,12 +36,16 @@ PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# Source of each timed kernel on the bf16 path (with the headers every kernel
+# includes): a counter summary applies only to the source it was taken on.
+_COMMON = ["decoder_attention_amd/csrc/device_common.h", "decoder_attention_amd/csrc/launch.h"]
 KERNEL_SOURCES = {
-    "prefill_attn_mfma_bf16": "decoder_attention_amd/csrc/prefill_mfma.hip",
-    "decode_attn_split": "decoder_attention_amd/csrc/decode.hip",
-    "qknorm_rope_kv_prefill": "decoder_attention_amd/csrc/qknorm_rope.hip",
-    "qknorm_rope_kv_decode": "decoder_attention_amd/csrc/qknorm_rope.hip",
-    "decode_attn_combine": "decoder_attention_amd/csrc/decode.hip",
+    "prefill_attn_mfma_bf16": ["decoder_attention_amd/csrc/prefill_mfma.hip"] + _COMMON,
+    "decode_attn_split": ["decoder_attention_amd/csrc/decode_mfma.hip"] + _COMMON,
+    "decode_attn_combine": ["decoder_attention_amd/csrc/decode_mfma.hip"] + _COMMON,
+    "decode_plan": ["decoder_attention_amd/csrc/decode_mfma.hip"] + _COMMON,
+    "qknorm_rope_kv_prefill": ["decoder_attention_amd/csrc/qknorm_rope.hip"] + _COMMON,
+    "qknorm_rope_kv_decode": ["decoder_attention_amd/csrc/qknorm_rope.hip"] + _COMMON,
 }
 
 
@@ -53,9 +57,12 @@ def decode_kv_bytes(cache_lens, hkv, d, elem) -> float:
     return float(sum(2 * hkv * (int(L) + 1) * d * elem for L in cache_lens))
 
 
-def source_digest(path: str) -> str:
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -260,8 +267,8 @@ def main(argv=None):
     roof = roofline_for(dominant, kernels, F, B, args.workload)
     side = {}
     pre_ms = sum(kernels[k][0] for k in ("qknorm_rope_kv_prefill", "prefill_attn_mfma_bf16") if k in kernels)
-    dec_ms = sum(kernels[k][0] for k in ("qknorm_rope_kv_decode", "decode_attn_split", "decode_attn_combine")
-                 if k in kernels)
+    dec_ms = sum(kernels[k][0] for k in ("qknorm_rope_kv_decode", "decode_plan", "decode_attn_split",
+                                         "decode_attn_combine") if k in kernels)
     if F:
         tf = F / (pre_ms / args.steps / 1e3) / 1e12
         side["prefill_call"] = {"tflops": tf, "frac_of_mfma_peak": tf / PEAK_MFMA_TFLOPS,

@@ -54,6 +54,11 @@ CASES = [
     (8, 8, 64, [700, 1]),
     (16, 2, 128, [33, 1025]),
     (12, 4, 64, [50, 600]),
+    # query heads per matrix tile (bf16): 16, 12, 10 (two tiles per KV head), 5
+    (48, 3, 128, [300, 5]),
+    (12, 1, 64, [31, 32, 33]),
+    (20, 1, 128, [250, 0]),
+    (10, 2, 64, [90, 1100]),
 ]
 
 
@@ -70,6 +75,32 @@ def test_decode_matches_oracle(case, dtype):
     note(f"decode {_ids(case)} {dtype}")
     dec = make_decode_inputs(h, lens, seed=sum(lens) % 9973, dtype=dtype, device=DEV, capacity=max(lens) + 4)
     _check_decode(dec)
+
+
+def test_decode_cache_filled_to_capacity():
+    # The new token goes to the last slot of the cache (L_b = capacity - 1).
+    h = HeadConfig(32, 8, 128, 1e-6, 1e6)
+    dec = make_decode_inputs(h, [95, 40, 0], seed=21, device=DEV, capacity=96)
+    _check_decode(dec)
+
+
+def test_decode_many_short_requests():
+    # 600 requests x 8 KV heads of 1-7 steps: each wavefront's range of steps
+    # spans several (request, KV head) units and cuts some of them.
+    h = HeadConfig(32, 8, 128, 1e-6, 1e6)
+    lens = np.random.default_rng(11).integers(0, 200, size=600).tolist()
+    dec = make_decode_inputs(h, lens, seed=12, device=DEV, capacity=201)
+    err = _check_decode(dec)
+    note(f"600 short requests: max-abs error {err:.3e}")
+
+
+def test_decode_long_requests_split_over_many_wavefronts():
+    # 3 x 8 units of ~1250 steps over 2048 wavefronts: every unit is cut into
+    # ~80 portions merged by the combine.
+    h = HeadConfig(32, 8, 128, 1e-6, 1e6)
+    dec = make_decode_inputs(h, [40000, 39999, 20001], seed=13, device=DEV, capacity=40001)
+    err = _check_decode(dec)
+    note(f"long requests: max-abs error {err:.3e}")
 
 
 def test_decode_is_deterministic():
