@@ -124,13 +124,8 @@ class Runner:
         return F, B
 
 
-def time_steps(runner, steps: int, warmup: int):
-    torch, da = runner.torch, runner.da
-    for _ in range(warmup):
-        runner.step()
-    torch.cuda.synchronize()
-    da.qknorm_rope_attn_read_kernel_timing()          # drop anything recorded before
-    da.qknorm_rope_attn_set_kernel_timing(True)
+def _timed_region(runner, steps: int) -> float:
+    torch = runner.torch
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -139,9 +134,29 @@ def time_steps(runner, steps: int, warmup: int):
         runner.step()
     stop.record()
     torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def time_steps(runner, steps: int, warmup: int):
+    """Warm-up steps, then two timed regions of `steps` steps each.
+
+    The first region is the step as a caller runs it: its time per step is
+    the benchmark's.  In the second the library brackets every kernel launch
+    with a pair of HIP events on the launch stream (which adds a little time
+    between launches); it gives each kernel's average launch duration.
+    Returns (ms per step, ms per step with per-kernel events, kernel table).
+    """
+    torch, da = runner.torch, runner.da
+    for _ in range(warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    ms = _timed_region(runner, steps)
+    da.qknorm_rope_attn_read_kernel_timing()          # drop anything recorded before
+    da.qknorm_rope_attn_set_kernel_timing(True)
+    ms_events = _timed_region(runner, steps)
     da.qknorm_rope_attn_set_kernel_timing(False)
     kernels = da.qknorm_rope_attn_read_kernel_timing()
-    return start.elapsed_time(stop) / steps, kernels
+    return ms, ms_events, kernels
 
 
 def roofline_for(name, kernels, F, B, workload):
@@ -255,11 +270,11 @@ def main(argv=None):
     def measure(name, steps, warmup):
         w = build_workload(name, device=dev, parity=False)
         runner = Runner(w, torch, da)
-        ms, kernels = time_steps(runner, steps, warmup)
+        ms, ms_events, kernels = time_steps(runner, steps, warmup)
         F, B = runner.work()
-        return w, runner, ms, kernels, F, B
+        return w, runner, ms, ms_events, kernels, F, B
 
-    w, runner, ms, kernels, F, B = measure(args.workload, args.steps, args.warmup)
+    w, runner, ms, ms_events, kernels, F, B = measure(args.workload, args.steps, args.warmup)
     t = ms / 1e3
     value = 100.0 * (F / (PEAK_MFMA_TFLOPS * 1e12) + B / (PEAK_HBM_GBPS * 1e9)) / t
     per_kernel = {k: {"avg_ms": v[0] / v[1], "launches_per_step": v[1] / args.steps} for k, v in kernels.items()}
@@ -289,7 +304,7 @@ def main(argv=None):
     extra = {}
     if not args.no_extra:
         for name, steps in (("long_prefill_32k", 5), ("qwen3_4b_decode64", 20)):
-            ew, er, ems, ek, eF, eB = measure(name, steps, 2)
+            ew, er, ems, _, ek, eF, eB = measure(name, steps, 2)
             key = "prefill_attn_mfma_bf16" if eF else "decode_attn_split"
             extra[name] = {"ms_per_call": ems, "kernel": roofline_for(key, ek, eF, eB, name),
                            "call_rate": (eF / (ems / 1e3) / 1e12) if eF else (eB / (ems / 1e3) / 1e9),
@@ -305,6 +320,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_with_kernel_events": ms_events,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

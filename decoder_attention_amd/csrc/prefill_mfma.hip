@@ -112,7 +112,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave branches stay scalar
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -322,21 +322,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   // probabilities, then issues tile kt's P.V while the vector units mask and
   // reduce tile kt+1.  Tile kt+2 is fetched from global memory meanwhile and
   // written to the third LDS slot.
+  // The next tile's scores are formed even on a wavefront's last tile (from
+  // whatever the slot holds, and then dropped): that keeps the score, the
+  // probability and the P.V work of a step in one branch-free block, so the
+  // matrix and vector instructions can interleave.
   auto step = [&](int kt, f32x16 (&Scur)[QB][KB], f32x16 (&Snext)[QB][KB]) {
     const bool prefetch = kt + 2 < ntiles;
     if (prefetch) load_tile(kt + 2);
     if (kt < wtiles) {
       bf16x8 pf[QB][KSTEPS];
+      scores((kt + 1) % NSLOT, Snext);
+      probs(Scur, pf);
+      pv(kt % NSLOT, pf);
       if (kt + 1 < wtiles) {
         float mx[QB];
-        scores((kt + 1) % NSLOT, Snext);
-        probs(Scur, pf);
-        pv(kt % NSLOT, pf);
         tile_max(kt + 1, Snext, mx);
         raise_max(mx);
-      } else {
-        probs(Scur, pf);
-        pv(kt % NSLOT, pf);
       }
     }
     if (prefetch) store_tile((kt + 2) % NSLOT);
