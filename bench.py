@@ -140,22 +140,23 @@ def _timed_region(runner, steps: int) -> float:
 def time_steps(runner, steps: int, warmup: int):
     """Warm-up steps, then two timed regions of `steps` steps each.
 
-    The first region is the step as a caller runs it: its time per step is
-    the benchmark's.  In the second the library brackets every kernel launch
-    with a pair of HIP events on the launch stream (which adds a little time
-    between launches); it gives each kernel's average launch duration.
+    In the first region the library brackets every kernel launch with a pair
+    of HIP events on the launch stream (which adds a little time between
+    launches); it gives each kernel's average launch duration.  The second
+    region is the step as a caller runs it: its time per step is the
+    benchmark's (it comes second so that the GPU is fully warm by then).
     Returns (ms per step, ms per step with per-kernel events, kernel table).
     """
     torch, da = runner.torch, runner.da
     for _ in range(warmup):
         runner.step()
     torch.cuda.synchronize()
-    ms = _timed_region(runner, steps)
     da.qknorm_rope_attn_read_kernel_timing()          # drop anything recorded before
     da.qknorm_rope_attn_set_kernel_timing(True)
     ms_events = _timed_region(runner, steps)
     da.qknorm_rope_attn_set_kernel_timing(False)
     kernels = da.qknorm_rope_attn_read_kernel_timing()
+    ms = _timed_region(runner, steps)
     return ms, ms_events, kernels
 
 
