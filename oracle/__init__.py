@@ -16,5 +16,6 @@ from .qknorm_rope_attn import (  # noqa: F401
     prefill,
     prefill_rows,
     decode,
+    prefill_append,
     round_to_bf16,
 )

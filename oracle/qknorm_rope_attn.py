@@ -14,6 +14,10 @@ in float64 NumPy, step by step in the order the pages give:
 4. store K and V in the per-request cache;
 5. causal grouped-query softmax attention, scores scaled by 1/sqrt(D).
 
+Three modes: ``prefill`` (packed requests, empty caches), ``decode`` (one new
+token per request on a filled cache) and ``prefill_append`` (a chunk of new
+tokens per request on a filled cache; it contains the other two).
+
 Sources (page title, then section):
 * zero-to-sglang, "Chapter 3 Forward Pass and Generation (Code Walkthrough)",
   section 3.3 "QKV, RoPE, and causal attention": the split, per-head Q/K
@@ -256,6 +260,52 @@ def decode(qkv, q_norm_weight, k_norm_weight, positions, cache_lens, k_cache, v_
             g = h // group
             out[i, h] = attend_prefix(q_t[i, h], kc[i, g, : L + 1], vc[i, g, : L + 1])
     return {"out": out.reshape(b, num_q_heads * head_dim), "q_tilde": q_t, "k_tilde": k_t,
+            "v": v, "k_cache": kc, "v_cache": vc}
+
+
+def prefill_append(qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens, cache_lens, k_cache, v_cache,
+                   num_q_heads: int, num_kv_heads: int, head_dim: int, rms_eps: float,
+                   rope_base: float, block: int = 1024) -> Dict[str, np.ndarray]:
+    """A chunk of new tokens per request, appended to a cache that already holds entries.
+
+    Request r owns packed rows cu[r]..cu[r+1]-1, its T_r new tokens, on top of
+    P_r = cache_lens[r] cached entries.  New token j goes to slot P_r + j and
+    its query attends over slots 0..P_r + j: the cached history, the chunk's
+    earlier tokens and itself (concept chapter, section 4: prefill builds the
+    cache and later tokens attend to the cached history; "Prefill vs Decode":
+    the cache grows before attention runs).  P_r = 0 is a prefill, T_r = 1 a
+    decode step.  ``k_cache``/``v_cache``: [B, Hkv, S, D] with S >= P_r + T_r.
+    """
+    cu = [int(c) for c in np.asarray(cu_seqlens).tolist()]
+    lens = [int(x) for x in np.asarray(cache_lens).tolist()]
+    q_t, k_t, v = qk_norm_rope(qkv, q_norm_weight, k_norm_weight, positions, num_q_heads,
+                               num_kv_heads, head_dim, rms_eps, rope_base)
+    kc = _f64(k_cache).copy()
+    vc = _f64(v_cache).copy()
+    n = q_t.shape[0]
+    group = num_q_heads // num_kv_heads
+    scale = 1.0 / np.sqrt(head_dim)
+    out = np.zeros((n, num_q_heads, head_dim))
+    for r in range(len(lens)):
+        lo, hi, past = cu[r], cu[r + 1], lens[r]
+        t = hi - lo
+        if past + t > kc.shape[2]:
+            raise ValueError("cache capacity too small for the appended chunk")
+        if t == 0:
+            continue
+        kc[r, :, past:past + t, :] = np.transpose(k_t[lo:hi], (1, 0, 2))
+        vc[r, :, past:past + t, :] = np.transpose(v[lo:hi], (1, 0, 2))
+        for h in range(num_q_heads):
+            g = h // group
+            keys, values = kc[r, g, : past + t], vc[r, g, : past + t]
+            for r0 in range(0, t, block):
+                r1 = min(t, r0 + block)
+                s = (q_t[lo + r0:lo + r1, h, :] @ keys.T) * scale               # [rows, past + t]
+                rows = past + np.arange(r0, r1)[:, None]                       # slot of each query
+                cols = np.arange(past + t)[None, :]
+                p = softmax(np.where(cols <= rows, s, -np.inf), axis=-1)
+                out[lo + r0:lo + r1, h, :] = p @ values
+    return {"out": out.reshape(n, num_q_heads * head_dim), "q_tilde": q_t, "k_tilde": k_t,
             "v": v, "k_cache": kc, "v_cache": vc}
 
 

@@ -315,6 +315,88 @@ def check_sampled_rows(orc):
 
 
 # ---------------------------------------------------------------------------
+# Appending a chunk to a filled cache: it contains prefill (empty cache) and
+# decode (one-token chunks), and a prefill split in two equals the whole.
+# ---------------------------------------------------------------------------
+
+def _append_on(orc, qkv, wq, wk, pos, cu, lens, kc, vc, hq, hkv, d, base=1e4, eps=1e-6):
+    return orc.prefill_append(qkv, wq, wk, pos, cu, lens, kc, vc, **_layer_args(hq, hkv, d, eps, base))
+
+
+def check_append_to_empty_cache_is_prefill(orc):
+    hq, hkv, d = 4, 2, 8
+    seqlens = [5, 0, 9, 1]
+    qkv, wq, wk, pos, cu, res = _random_prefill(orc, seqlens, hq, hkv, d, 60)
+    shape = (len(seqlens), hkv, max(seqlens), d)
+    got = _append_on(orc, qkv, wq, wk, pos, cu, [0] * len(seqlens), np.full(shape, np.nan), np.full(shape, np.nan),
+                     hq, hkv, d)
+    np.testing.assert_allclose(got["out"], res["out"], rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(np.isnan(got["k_cache"]), np.isnan(res["k_cache"]))
+    np.testing.assert_allclose(np.nan_to_num(got["k_cache"]), np.nan_to_num(res["k_cache"]), rtol=0, atol=1e-15)
+
+
+def check_append_single_tokens_is_decode(orc):
+    hq, hkv, d = 8, 2, 16
+    r = _rng(61)
+    lens = [0, 3, 17]
+    cap = 20
+    kc = r.standard_normal((3, hkv, cap, d))
+    vc = r.standard_normal((3, hkv, cap, d))
+    qkv = r.standard_normal((3, (hq + 2 * hkv) * d))
+    wq = 1 + 0.1 * r.standard_normal(d)
+    wk = 1 + 0.1 * r.standard_normal(d)
+    dec = orc.decode(qkv, wq, wk, lens, lens, kc, vc, **_layer_args(hq, hkv, d))
+    got = _append_on(orc, qkv, wq, wk, lens, [0, 1, 2, 3], lens, kc, vc, hq, hkv, d)
+    np.testing.assert_allclose(got["out"], dec["out"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(got["k_cache"], dec["k_cache"], rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(got["v_cache"], dec["v_cache"])
+
+
+def check_append_split_equals_full_prefill(orc):
+    # Prefill of the first T1 tokens, then the next T2 appended onto that
+    # cache, gives the last T2 rows (and the cache) of a prefill of T1 + T2.
+    hq, hkv, d = 4, 2, 16
+    splits = [(3, 4), (0, 6), (7, 0), (1, 1), (9, 5)]
+    full_lens = [a + b for a, b in splits]
+    qkv, wq, wk, pos, cu, res = _random_prefill(orc, full_lens, hq, hkv, d, 62, base=1e6)
+    cap = max(full_lens) + 2
+    b = len(splits)
+    kc = np.full((b, hkv, cap, d), np.nan)
+    vc = np.full((b, hkv, cap, d), np.nan)
+    rows, cu2 = [], [0]
+    for i, (t1, t2) in enumerate(splits):
+        kc[i, :, :t1] = res["k_cache"][i, :, :t1]
+        vc[i, :, :t1] = res["v_cache"][i, :, :t1]
+        rows.extend(range(cu[i] + t1, cu[i] + t1 + t2))
+        cu2.append(cu2[-1] + t2)
+    got = _append_on(orc, qkv[rows], wq, wk, pos[rows], cu2, [t1 for t1, _ in splits], kc, vc, hq, hkv, d,
+                     base=1e6)
+    np.testing.assert_allclose(got["out"], res["out"][rows], rtol=0, atol=1e-13)
+    for i, n in enumerate(full_lens):
+        np.testing.assert_allclose(got["k_cache"][i, :, :n], res["k_cache"][i, :, :n], rtol=0, atol=1e-15)
+        np.testing.assert_array_equal(got["v_cache"][i, :, :n], res["v_cache"][i, :, :n])
+        assert np.all(np.isnan(got["k_cache"][i, :, n:]))
+
+
+def check_append_brute_force(orc):
+    # Scalar loops over the whole sequence (history and chunk) at tiny sizes.
+    hq, hkv, d = 4, 2, 8
+    t1, t2 = 3, 4
+    r = _rng(63)
+    n = t1 + t2
+    qkv = r.standard_normal((n, (hq + 2 * hkv) * d))
+    wq = 1 + 0.1 * r.standard_normal(d)
+    wk = 1 + 0.1 * r.standard_normal(d)
+    pos = np.arange(n)
+    pre = orc.prefill(qkv[:t1], wq, wk, pos[:t1], [0, t1], cache_capacity=n, **_layer_args(hq, hkv, d, 1e-3))
+    got = _append_on(orc, qkv[t1:], wq, wk, pos[t1:], [0, t2], [t1], pre["k_cache"], pre["v_cache"], hq, hkv, d,
+                     eps=1e-3)
+    want = evaluators.brute_force_layer(qkv.tolist(), wq.tolist(), wk.tolist(), pos.tolist(), [n], hq, hkv, d,
+                                        1e-3, 1e4)
+    np.testing.assert_allclose(got["out"].reshape(t2, hq, d), np.array(want)[t1:], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # Shapes and cache lengths the pages print
 # ---------------------------------------------------------------------------
 
@@ -385,4 +467,8 @@ ALL_CHECKS = [
     check_sampled_rows,
     check_golden_shapes,
     check_golden_cache_lengths,
+    check_append_to_empty_cache_is_prefill,
+    check_append_single_tokens_is_decode,
+    check_append_split_equals_full_prefill,
+    check_append_brute_force,
 ]

@@ -14,7 +14,7 @@ import pins
 
 REAL = {name: getattr(orc, name) for name in
         ("split_qkv", "rms_norm", "rope_rotate_half", "rope_frequencies", "causal_gqa_attention",
-         "attend_prefix", "qk_norm_rope", "softmax")}
+         "attend_prefix", "qk_norm_rope", "softmax", "prefill_append")}
 
 
 def _rope_sign(x, positions, base):
@@ -91,7 +91,48 @@ def _softmax_no_norm(scores, axis=-1):
     return np.exp(s - np.max(s, axis=axis, keepdims=True))
 
 
+def _append_ignores_history(qkv, wq, wk, positions, cu, cache_lens, k_cache, v_cache, *args, **kw):
+    # The chunk attends only to itself: the cached entries are written over by a prefill.
+    hist = np.asarray(cache_lens)
+    res = REAL["prefill_append"](qkv, wq, wk, positions, cu, np.zeros_like(hist), k_cache, v_cache, *args, **kw)
+    return res
+
+
+def _append_writes_from_slot_zero(qkv, wq, wk, positions, cu, cache_lens, k_cache, v_cache, *args, **kw):
+    res = REAL["prefill_append"](qkv, wq, wk, positions, cu, cache_lens, k_cache, v_cache, *args, **kw)
+    lens = np.asarray(cache_lens)
+    cu = np.asarray(cu)
+    for r, past in enumerate(lens):
+        t = int(cu[r + 1] - cu[r])
+        if past > 0 and t > 0:  # the chunk's K lands at slot 0 instead of slot P_r
+            res["k_cache"][r, :, :t] = res["k_cache"][r, :, past:past + t]
+    return res
+
+
+def _append_mask_excludes_self(qkv, wq, wk, positions, cu, cache_lens, k_cache, v_cache, num_q_heads,
+                               num_kv_heads, head_dim, rms_eps, rope_base, block=1024):
+    res = REAL["prefill_append"](qkv, wq, wk, positions, cu, cache_lens, k_cache, v_cache, num_q_heads,
+                                 num_kv_heads, head_dim, rms_eps, rope_base, block)
+    q_t, kc, vc = res["q_tilde"], res["k_cache"], res["v_cache"]
+    out = res["out"].reshape(q_t.shape).copy()
+    group = num_q_heads // num_kv_heads
+    cu = np.asarray(cu)
+    for r, past in enumerate(np.asarray(cache_lens)):
+        for j in range(int(cu[r + 1] - cu[r])):
+            n = int(cu[r]) + j
+            if past + j == 0:
+                continue
+            for h in range(num_q_heads):
+                g = h // group
+                out[n, h] = REAL["attend_prefix"](q_t[n, h], kc[r, g, : past + j], vc[r, g, : past + j])
+    res["out"] = out.reshape(res["out"].shape)
+    return res
+
+
 MUTANTS = {
+    "append_ignores_history": ("prefill_append", _append_ignores_history),
+    "append_writes_from_slot_zero": ("prefill_append", _append_writes_from_slot_zero),
+    "append_mask_excludes_self": ("prefill_append", _append_mask_excludes_self),
     "rope_wrong_sign": ("rope_rotate_half", _rope_sign),
     "rope_frequency_exponent": ("rope_frequencies", _freq_exponent),
     "rmsnorm_eps_outside_sqrt": ("rms_norm", _eps_outside),
