@@ -53,6 +53,11 @@ def prefill_flops(seqlens, hq, d) -> float:
     return float(sum(2 * d * hq * t * (t + 1) for t in seqlens))
 
 
+def append_flops(past_lens, chunk_lens, hq, d) -> float:
+    """Chunk token j of request r sees P_r + j + 1 keys: 4*D*Hq FLOP per visible pair."""
+    return float(sum(2 * d * hq * (2 * t * p + t * (t + 1)) for p, t in zip(past_lens, chunk_lens)))
+
+
 def decode_kv_bytes(cache_lens, hkv, d, elem) -> float:
     return float(sum(2 * hkv * (int(L) + 1) * d * elem for L in cache_lens))
 
@@ -95,6 +100,17 @@ class Runner:
             args = (cfg, p.qkv, p.q_norm_weight, p.k_norm_weight, p.positions, p.cu_seqlens, p.num_tokens,
                     p.num_seqs, p.max_seqlen, p.k_cache, p.v_cache, p.cache_capacity, out, ws, ws_bytes)
             self.calls.append((da.qknorm_rope_attn_prefill, args, (out, ws)))
+        if w.append is not None:
+            a = w.append
+            h = a.heads
+            cfg = da.make_config(h.num_q_heads, h.num_kv_heads, h.head_dim, a.qkv.dtype, h.rms_eps, h.rope_base)
+            out = torch.empty((a.num_tokens, h.num_q_heads * h.head_dim), dtype=a.qkv.dtype, device=a.qkv.device)
+            ws_bytes = da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_PREFILL, a.num_tokens, a.max_seqlen)
+            ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=a.qkv.device)
+            args = (cfg, a.qkv, a.q_norm_weight, a.k_norm_weight, a.positions, a.cu_seqlens, a.cache_lens,
+                    a.num_tokens, a.num_seqs, a.max_seqlen, a.max_cache_len, a.k_cache, a.v_cache,
+                    a.cache_capacity, out, ws, ws_bytes)
+            self.calls.append((da.qknorm_rope_attn_prefill_append, args, (out, ws)))
         if w.decode is not None:
             d = w.decode
             h = d.heads
@@ -117,6 +133,9 @@ class Runner:
         if self.w.prefill is not None:
             h = self.w.prefill.heads
             F = prefill_flops(self.w.prefill.seqlens, h.num_q_heads, h.head_dim)
+        if self.w.append is not None:
+            h = self.w.append.heads
+            F += append_flops(self.w.append.past_lens, self.w.append.seqlens, h.num_q_heads, h.head_dim)
         if self.w.decode is not None:
             h = self.w.decode.heads
             B = decode_kv_bytes(self.w.decode.cache_lens.tolist(), h.num_kv_heads, h.head_dim,
@@ -304,7 +323,7 @@ def main(argv=None):
 
     extra = {}
     if not args.no_extra:
-        for name, steps in (("long_prefill_32k", 5), ("qwen3_4b_decode64", 20)):
+        for name, steps in (("long_prefill_32k", 5), ("qwen3_4b_decode64", 20), ("chunked_qwen3_8b", 10)):
             ew, er, ems, _, ek, eF, eB = measure(name, steps, 2)
             key = "prefill_attn_mfma_bf16" if eF else "decode_attn_split"
             extra[name] = {"ms_per_call": ems, "kernel": roofline_for(key, ek, eF, eB, name),

@@ -1,7 +1,7 @@
 """QK-RMSNorm + RoPE + causal grouped-query attention for MI355X (gfx950).
 
 The computation lives in the HIP library ``libqknorm_rope_attn.so`` (C ABI in
-``include/qknorm_rope_attn.h``); this package binds it and adds two
+``include/qknorm_rope_attn.h``); this package binds it and adds three
 conveniences that allocate outputs and workspace with PyTorch before calling
 it.  PyTorch supplies device memory and the current stream only.
 """
@@ -27,6 +27,7 @@ from .binding import (  # noqa: F401
     lib,
     make_config,
     qknorm_rope_attn_prefill,
+    qknorm_rope_attn_prefill_append,
     qknorm_rope_attn_decode,
     qknorm_rope_attn_workspace_bytes,
     qknorm_rope_attn_status_string,
@@ -63,6 +64,27 @@ def prefill(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cu_se
                                       max_seqlen, k_cache, v_cache, k_cache.shape[2], out, workspace,
                                       workspace.numel() * workspace.element_size(), stream)
     check(status, "qknorm_rope_attn_prefill")
+    return out, workspace
+
+
+def prefill_append(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens, cache_lens,
+                   max_seqlen: int, max_cache_len: int, k_cache, v_cache, out=None, workspace=None, stream=None):
+    """Runs ``qknorm_rope_attn_prefill_append``; returns (out [N, Hq*D], workspace)."""
+    import torch
+
+    _require_device(qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens, cache_lens, k_cache, v_cache)
+    n = qkv.shape[0]
+    b = cu_seqlens.shape[0] - 1
+    if out is None:
+        out = torch.empty((n, cfg.num_q_heads * cfg.head_dim), dtype=qkv.dtype, device=qkv.device)
+    need = qknorm_rope_attn_workspace_bytes(cfg, QKRA_MODE_PREFILL, n, max_seqlen)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=qkv.device)
+    status = qknorm_rope_attn_prefill_append(cfg, qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens,
+                                             cache_lens, n, b, max_seqlen, max_cache_len, k_cache, v_cache,
+                                             k_cache.shape[2], out, workspace,
+                                             workspace.numel() * workspace.element_size(), stream)
+    check(status, "qknorm_rope_attn_prefill_append")
     return out, workspace
 
 

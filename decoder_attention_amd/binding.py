@@ -60,6 +60,8 @@ _SZ = ctypes.c_size_t
 _SIGNATURES = {
     "qknorm_rope_attn_prefill": (_I32, [ctypes.POINTER(QkraConfig), _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P,
                                         _I32, _P, _P, _SZ, _P]),
+    "qknorm_rope_attn_prefill_append": (_I32, [ctypes.POINTER(QkraConfig), _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                               _I32, _P, _P, _I32, _P, _P, _SZ, _P]),
     "qknorm_rope_attn_decode": (_I32, [ctypes.POINTER(QkraConfig), _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32,
                                        _P, _P, _SZ, _P]),
     "qknorm_rope_attn_workspace_bytes": (_SZ, [ctypes.POINTER(QkraConfig), _I32, _I32, _I32]),
@@ -131,6 +133,16 @@ def qknorm_rope_attn_prefill(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight,
         ctypes.byref(cfg), _ptr(qkv), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(positions), _ptr(cu_seqlens),
         int(num_tokens), int(num_seqs), int(max_seqlen), _ptr(k_cache), _ptr(v_cache), int(cache_capacity),
         _ptr(out), _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def qknorm_rope_attn_prefill_append(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens,
+                                    cache_lens, num_tokens: int, num_seqs: int, max_seqlen: int,
+                                    max_cache_len: int, k_cache, v_cache, cache_capacity: int, out, workspace,
+                                    workspace_bytes: int, stream=None) -> int:
+    return lib().qknorm_rope_attn_prefill_append(
+        ctypes.byref(cfg), _ptr(qkv), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(positions), _ptr(cu_seqlens),
+        _ptr(cache_lens), int(num_tokens), int(num_seqs), int(max_seqlen), int(max_cache_len), _ptr(k_cache),
+        _ptr(v_cache), int(cache_capacity), _ptr(out), _ptr(workspace), int(workspace_bytes), _stream(stream))
 
 
 def qknorm_rope_attn_decode(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cache_lens,

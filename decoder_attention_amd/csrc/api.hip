@@ -170,19 +170,26 @@ QKRA_API int32_t qknorm_rope_attn_last_hip_error(void) { return g_last_hip_error
 
 QKRA_API int32_t qknorm_rope_attn_version(void) { return 100; }
 
-QKRA_API int32_t qknorm_rope_attn_prefill(const qkra_config* cfg, const void* qkv, const void* q_norm_weight,
-                                          const void* k_norm_weight, const int32_t* positions,
-                                          const int32_t* cu_seqlens, int32_t num_tokens, int32_t num_seqs,
-                                          int32_t max_seqlen, void* k_cache, void* v_cache,
-                                          int32_t cache_capacity, void* out, void* workspace,
-                                          size_t workspace_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Prefill of packed requests onto caches holding cache_lens[r] entries each
+// (cache_lens null: empty caches, max_cache_len 0).
+int32_t prefill_impl(const qkra_config* cfg, const void* qkv, const void* q_norm_weight, const void* k_norm_weight,
+                     const int32_t* positions, const int32_t* cu_seqlens, const int32_t* cache_lens,
+                     int32_t num_tokens, int32_t num_seqs, int32_t max_seqlen, int32_t max_cache_len,
+                     void* k_cache, void* v_cache, int32_t cache_capacity, void* out, void* workspace,
+                     size_t workspace_bytes, void* hip_stream) {
   const int32_t cs = check_config(cfg);
   if (cs != QKRA_OK) return cs;
-  if (num_tokens < 0 || num_seqs < 0 || max_seqlen < 0 || cache_capacity < 0) return QKRA_ERR_INVALID_ARGUMENT;
+  if (num_tokens < 0 || num_seqs < 0 || max_seqlen < 0 || max_cache_len < 0 || cache_capacity < 0)
+    return QKRA_ERR_INVALID_ARGUMENT;
   if (num_tokens == 0) return QKRA_OK;
   if (num_seqs == 0 || max_seqlen == 0 || max_seqlen > num_tokens) return QKRA_ERR_INVALID_ARGUMENT;
   if (static_cast<long long>(max_seqlen) * num_seqs < num_tokens) return QKRA_ERR_INVALID_ARGUMENT;
-  if (cache_capacity < max_seqlen) return QKRA_ERR_CAPACITY;
+  if (static_cast<long long>(cache_capacity) < static_cast<long long>(max_cache_len) + max_seqlen)
+    return QKRA_ERR_CAPACITY;
   if (!qkv || !q_norm_weight || !k_norm_weight || !positions || !cu_seqlens || !k_cache || !v_cache || !out)
     return QKRA_ERR_INVALID_ARGUMENT;
   const size_t need = prefill_workspace(cfg, num_tokens);
@@ -201,8 +208,9 @@ QKRA_API int32_t qknorm_rope_attn_prefill(const qkra_config* cfg, const void* qk
   const Range r_ws = range_of(workspace, need);
   const Range r_wq = range_of(q_norm_weight, d * es), r_wk = range_of(k_norm_weight, d * es);
   const Range r_pos = range_of(positions, num_tokens * 4ull), r_cu = range_of(cu_seqlens, (num_seqs + 1ull) * 4);
+  const Range r_len = range_of(cache_lens, cache_lens ? num_seqs * 4ull : 0);
   for (Range w : {r_out, r_k, r_v, r_ws})
-    for (Range r : {r_qkv, r_wq, r_wk, r_pos, r_cu})
+    for (Range r : {r_qkv, r_wq, r_wk, r_pos, r_cu, r_len})
       if (overlap(w, r)) return QKRA_ERR_ALIASING;
   if (overlap(r_out, r_k) || overlap(r_out, r_v) || overlap(r_out, r_ws) || overlap(r_k, r_v) ||
       overlap(r_k, r_ws) || overlap(r_v, r_ws))
@@ -215,6 +223,7 @@ QKRA_API int32_t qknorm_rope_attn_prefill(const qkra_config* cfg, const void* qk
   ka.k_norm_weight = k_norm_weight;
   ka.positions = positions;
   ka.seq_info = cu_seqlens;
+  ka.slot_offsets = cache_lens;
   ka.decode_mode = 0;
   ka.num_rows = num_tokens;
   ka.num_seqs = num_seqs;
@@ -236,6 +245,7 @@ QKRA_API int32_t qknorm_rope_attn_prefill(const qkra_config* cfg, const void* qk
   pa.k_cache = k_cache;
   pa.v_cache = v_cache;
   pa.cu_seqlens = cu_seqlens;
+  pa.past_lens = cache_lens;
   pa.out = out;
   pa.num_q_heads = cfg->num_q_heads;
   pa.num_kv_heads = cfg->num_kv_heads;
@@ -249,6 +259,33 @@ QKRA_API int32_t qknorm_rope_attn_prefill(const qkra_config* cfg, const void* qk
   else
     err = timed(kKernelPrefillFp32, stream, [&] { return launch_prefill_attn_fp32(pa, stream); });
   return hip_status(err);
+}
+
+}  // namespace
+
+extern "C" {
+
+QKRA_API int32_t qknorm_rope_attn_prefill(const qkra_config* cfg, const void* qkv, const void* q_norm_weight,
+                                          const void* k_norm_weight, const int32_t* positions,
+                                          const int32_t* cu_seqlens, int32_t num_tokens, int32_t num_seqs,
+                                          int32_t max_seqlen, void* k_cache, void* v_cache,
+                                          int32_t cache_capacity, void* out, void* workspace,
+                                          size_t workspace_bytes, void* hip_stream) {
+  return prefill_impl(cfg, qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens, nullptr, num_tokens, num_seqs,
+                      max_seqlen, 0, k_cache, v_cache, cache_capacity, out, workspace, workspace_bytes, hip_stream);
+}
+
+QKRA_API int32_t qknorm_rope_attn_prefill_append(const qkra_config* cfg, const void* qkv,
+                                                 const void* q_norm_weight, const void* k_norm_weight,
+                                                 const int32_t* positions, const int32_t* cu_seqlens,
+                                                 const int32_t* cache_lens, int32_t num_tokens, int32_t num_seqs,
+                                                 int32_t max_seqlen, int32_t max_cache_len, void* k_cache,
+                                                 void* v_cache, int32_t cache_capacity, void* out,
+                                                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (num_tokens > 0 && !cache_lens) return QKRA_ERR_INVALID_ARGUMENT;
+  return prefill_impl(cfg, qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens, cache_lens, num_tokens,
+                      num_seqs, max_seqlen, max_cache_len, k_cache, v_cache, cache_capacity, out, workspace,
+                      workspace_bytes, hip_stream);
 }
 
 QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv, const void* q_norm_weight,

@@ -27,7 +27,8 @@ struct QkNormRopeArgs {
   const void* k_norm_weight;
   const int32_t* positions;
   const int32_t* seq_info;  // prefill: cu_seqlens[num_seqs+1]; decode: cache_lens[num_seqs]
-  int decode_mode;          // 0: slot = in-request index; 1: row b, slot = cache_lens[b]
+  const int32_t* slot_offsets;  // prefill: per-request first slot (entries already cached), or null for 0
+  int decode_mode;          // 0: slot = offset + in-request index; 1: row b, slot = cache_lens[b]
   int num_rows;
   int num_seqs;
   int num_q_heads, num_kv_heads, head_dim, dtype, cache_capacity;
@@ -39,12 +40,14 @@ struct QkNormRopeArgs {
 };
 hipError_t launch_qknorm_rope(const QkNormRopeArgs& a, hipStream_t stream);
 
-// Kernel 2: causal GQA attention over the prefill caches.
+// Kernel 2: causal GQA attention over the prefill caches.  Request r's new token j
+// sits at slot P_r + j and sees slots 0..P_r + j (P_r = past_lens[r], or 0).
 struct PrefillAttnArgs {
   const void* q;            // q~ [N, Hq, D]
   const void* k_cache;      // [B, Hkv, S, D]
   const void* v_cache;
   const int32_t* cu_seqlens;
+  const int32_t* past_lens; // per request: entries cached before this chunk (null: none)
   void* out;                // [N, Hq*D]
   int num_q_heads, num_kv_heads, head_dim, cache_capacity, num_seqs, max_seqlen;
   float scale_log2;         // log2(e) / sqrt(D)

@@ -22,8 +22,8 @@ constexpr int NT = 2 * QT;
 template <int D>
 __global__ __launch_bounds__(NT) void prefill_fp32_kernel(
     const float* __restrict__ q, const float* __restrict__ k_cache, const float* __restrict__ v_cache,
-    const int32_t* __restrict__ cu_seqlens, float* __restrict__ out, int num_q_heads, int num_kv_heads,
-    int cache_capacity, int num_seqs, int tiles_per_seq, float scale_log2) {
+    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ past_lens, float* __restrict__ out,
+    int num_q_heads, int num_kv_heads, int cache_capacity, int num_seqs, int tiles_per_seq, float scale_log2) {
   constexpr int HD = D / 2;
   __shared__ float sK[KT][D + 1];
   __shared__ float sV[KT][D + 1];
@@ -34,7 +34,10 @@ __global__ __launch_bounds__(NT) void prefill_fp32_kernel(
   const int tile = tiles_per_seq - 1 - rest / num_seqs;
   const int seq = rest % num_seqs;
   const int cu0 = cu_seqlens[seq];
-  const int seqlen = min(cu_seqlens[seq + 1] - cu0, cache_capacity);
+  // Entries cached before the chunk; the chunk is clamped to the cache so
+  // out-of-contract inputs cannot address past it.
+  const int past = past_lens ? min(max(past_lens[seq], 0), cache_capacity) : 0;
+  const int seqlen = min(cu_seqlens[seq + 1] - cu0, cache_capacity - past);
   const int t0 = tile * QT;
   if (t0 >= seqlen) return;
   const int g = head / (num_q_heads / num_kv_heads);
@@ -53,7 +56,7 @@ __global__ __launch_bounds__(NT) void prefill_fp32_kernel(
   }
   float m_run = kNegInf, l_run = 0.f;
 
-  const int kv_end = min(seqlen, t0 + QT);
+  const int kv_end = past + min(seqlen, t0 + QT);
   const size_t head_off = (static_cast<size_t>(seq) * num_kv_heads + g) * cache_capacity * D;
   for (int k0 = 0; k0 < kv_end; k0 += KT) {
     __syncthreads();
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(NT) void prefill_fp32_kernel(
       for (int e = 0; e < HD; ++e) dot += qr[e] * sK[j][half * HD + e];
       dot += xor_shuffle(dot, 1);
       const int key = k0 + j;
-      s[j] = (key <= tok && key < kv_end) ? dot * scale_log2 : kNegInf;
+      s[j] = (key <= past + tok && key < kv_end) ? dot * scale_log2 : kNegInf;
       mx = fmaxf(mx, s[j]);
     }
     const float m_new = fmaxf(m_run, mx);
@@ -111,7 +114,7 @@ hipError_t launch_typed(const PrefillAttnArgs& a, hipStream_t stream) {
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((prefill_fp32_kernel<D>), dim3(static_cast<unsigned>(items)), dim3(NT), 0, stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k_cache),
-                     static_cast<const float*>(a.v_cache), a.cu_seqlens, static_cast<float*>(a.out),
+                     static_cast<const float*>(a.v_cache), a.cu_seqlens, a.past_lens, static_cast<float*>(a.out),
                      a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.num_seqs, tiles, a.scale_log2);
   return hipGetLastError();
 }

@@ -73,7 +73,8 @@ __device__ __forceinline__ float half_wave_max(float x) {
 template <int D, int HC>
 __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k_cache, const bf16* __restrict__ v_cache,
-    const int32_t* __restrict__ cu_seqlens, bf16* __restrict__ out, int num_q_heads, int num_kv_heads,
+    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ past_lens, bf16* __restrict__ out,
+    int num_q_heads, int num_kv_heads,
     int cache_capacity, int num_seqs, int tiles_per_seq, int chunks_per_kv, int num_items,
     float scale_log2) {
   constexpr int TBN = 8 / HC;       // token blocks (of 32) per workgroup
@@ -102,8 +103,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   const int tile = tiles_per_seq - 1 - rem / num_seqs;
   const int seq = rem % num_seqs;
   const int cu0 = cu_seqlens[seq];
+  // Entries cached before the chunk (its token t sits at slot past + t).
   // Lengths are clamped to the cache so out-of-contract inputs cannot address past it.
-  const int seqlen = min(cu_seqlens[seq + 1] - cu0, cache_capacity);
+  const int past = past_lens ? min(max(past_lens[seq], 0), cache_capacity) : 0;
+  const int seqlen = min(cu_seqlens[seq + 1] - cu0, cache_capacity - past);
   const int t0 = tile * TM;
   if (t0 >= seqlen) return;
   const int group = num_q_heads / num_kv_heads;
@@ -151,13 +154,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     l_run[qb] = 0.f;
   }
 
-  const int kv_end = min(seqlen, t0 + TM);
+  const int kv_end = past + min(seqlen, t0 + TM);
   const int ntiles = (kv_end + BN - 1) / BN;
   int qlast = qfirst[0];
 #pragma unroll
   for (int qb = 1; qb < QB; ++qb) qlast = max(qlast, qfirst[qb]);
   // Tiles holding a key visible to this wavefront's rows (the rest are only loaded).
-  const int wtiles = min(kv_end - 1, qlast + 31) / BN + 1;
+  const int wtiles = min(kv_end - 1, past + qlast + 31) / BN + 1;
   const size_t head_off = (static_cast<size_t>(seq) * num_kv_heads + g) * cache_capacity * D;
   const bf16* kbase = k_cache + head_off;
   const bf16* vbase = v_cache + head_off;
@@ -242,8 +245,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     const int k0 = kt * BN;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      if (k0 + BN - 1 > qfirst[qb]) {
-        const int lim = qtok[qb] - k0 - 4 * hi;  // register j of block kb holds key k0 + 32kb + 8(j/4) + 4hi + j%4
+      if (k0 + BN - 1 > past + qfirst[qb]) {
+        const int lim = past + qtok[qb] - k0 - 4 * hi;  // register j of block kb holds key k0 + 32kb + 8(j/4) + 4hi + j%4
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -395,7 +398,7 @@ hipError_t launch_typed(const PrefillAttnArgs& a, hipStream_t stream) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((prefill_mfma_kernel<D, HC>), dim3(static_cast<unsigned>(grid)), dim3(NTHREADS), 0, stream,
                      static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k_cache),
-                     static_cast<const bf16*>(a.v_cache), a.cu_seqlens, static_cast<bf16*>(a.out),
+                     static_cast<const bf16*>(a.v_cache), a.cu_seqlens, a.past_lens, static_cast<bf16*>(a.out),
                      a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.num_seqs, tiles, chunks_per_kv,
                      static_cast<int>(items), a.scale_log2);
   return hipGetLastError();

@@ -48,7 +48,8 @@ __device__ __forceinline__ void pack4(const float y[4], u32x4* r) {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
     const T* __restrict__ qkv, const T* __restrict__ q_weight, const T* __restrict__ k_weight,
-    const int32_t* __restrict__ positions, const int32_t* __restrict__ seq_info, int decode_mode,
+    const int32_t* __restrict__ positions, const int32_t* __restrict__ seq_info,
+    const int32_t* __restrict__ slot_offsets, int decode_mode,
     int num_seqs, int num_q_heads, int num_kv_heads, int cache_capacity, float eps,
     double log2_base, T* __restrict__ q_out, T* __restrict__ k_cache, T* __restrict__ v_cache) {
   using Raw = typename Raw4<T>::type;
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
       if (seq_info[mid] <= row_id) lo = mid; else hi = mid;
     }
     req = lo;
-    slot = row_id - seq_info[lo];
+    slot = row_id - seq_info[lo] + (slot_offsets ? slot_offsets[lo] : 0);
   }
   // Rows outside the caller's contract (slot past the cache) write no cache entry.
   const bool slot_ok = slot >= 0 && slot < cache_capacity;
@@ -158,7 +159,8 @@ template <typename T, int D>
 hipError_t launch_typed(const QkNormRopeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((qknorm_rope_kv_kernel<T, D>), dim3(a.num_rows), dim3(256), 0, stream,
                      static_cast<const T*>(a.qkv), static_cast<const T*>(a.q_norm_weight),
-                     static_cast<const T*>(a.k_norm_weight), a.positions, a.seq_info, a.decode_mode,
+                     static_cast<const T*>(a.k_norm_weight), a.positions, a.seq_info, a.slot_offsets,
+                     a.decode_mode,
                      a.num_seqs, a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.rms_eps,
                      a.log2_rope_base, static_cast<T*>(a.q_out), static_cast<T*>(a.k_cache),
                      static_cast<T*>(a.v_cache));

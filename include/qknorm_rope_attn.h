@@ -118,6 +118,39 @@ QKRA_API int32_t qknorm_rope_attn_prefill(const qkra_config* cfg, const void* qk
                                           void* hip_stream);
 
 /*
+ * Prefill of a chunk of new tokens per request onto caches that already hold
+ * entries (chunked prefill, prompt continuation).  It extends the cached
+ * history of each request the way decode extends it by one token (concept
+ * chapter, section 4: later tokens attend to the cached history; "Prefill vs
+ * Decode": the cache grows before attention runs): request r's new token j is
+ * written to slot P_r + j and its query attends over slots 0 .. P_r + j.
+ * With every P_r = 0 this is qknorm_rope_attn_prefill; with one token per
+ * request it is qknorm_rope_attn_decode.
+ *
+ *   qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens, max_seqlen, out
+ *                  as for qknorm_rope_attn_prefill (positions are usually
+ *                  P_r + j, but only the RoPE angle depends on them).
+ *   cache_lens     int32 [num_seqs]: P_r, the number of valid cache entries
+ *                  before this call (slots 0 .. P_r-1 are read, never
+ *                  written).  Not updated by the library.
+ *   max_cache_len  host copy of max_r P_r; cache_capacity >= max_cache_len +
+ *                  max_seqlen.
+ *   k_cache, v_cache [num_seqs, Hkv, cache_capacity, D]; slots P_r .. P_r+T_r-1
+ *                  are written, all others keep their contents.
+ *   workspace      as for qknorm_rope_attn_prefill (same size and contents).
+ * num_tokens == 0 is a no-op returning QKRA_OK; otherwise a null cache_lens
+ * is QKRA_ERR_INVALID_ARGUMENT.
+ */
+QKRA_API int32_t qknorm_rope_attn_prefill_append(const qkra_config* cfg, const void* qkv,
+                                                 const void* q_norm_weight, const void* k_norm_weight,
+                                                 const int32_t* positions, const int32_t* cu_seqlens,
+                                                 const int32_t* cache_lens, int32_t num_tokens,
+                                                 int32_t num_seqs, int32_t max_seqlen,
+                                                 int32_t max_cache_len, void* k_cache, void* v_cache,
+                                                 int32_t cache_capacity, void* out, void* workspace,
+                                                 size_t workspace_bytes, void* hip_stream);
+
+/*
  * Decode step: one new token per request.
  *
  *   qkv            [num_seqs, (Hq+2Hkv)*D]: the new token's projection row.

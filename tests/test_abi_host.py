@@ -168,6 +168,45 @@ def test_decode_empty_batch_is_noop():
     assert call_decode(cfg, a) == da.QKRA_OK
 
 
+def append_args(**over):
+    cfg = over.pop("cfg", da.make_config(32, 8, 128, da.QKRA_BF16))
+    a = dict(qkv=BASE, q_norm_weight=BASE + 64 * MB, k_norm_weight=BASE + 65 * MB, positions=BASE + 66 * MB,
+             cu_seqlens=BASE + 67 * MB, cache_lens=BASE + 68 * MB, num_tokens=100, num_seqs=4, max_seqlen=40,
+             max_cache_len=60, k_cache=BASE + 100 * MB, v_cache=BASE + 200 * MB, cache_capacity=100,
+             out=BASE + 300 * MB, workspace=BASE + 400 * MB, workspace_bytes=16 * MB, stream=0)
+    a.update(over)
+    return cfg, a
+
+
+def call_append(cfg, a):
+    return da.qknorm_rope_attn_prefill_append(cfg, a["qkv"], a["q_norm_weight"], a["k_norm_weight"],
+                                              a["positions"], a["cu_seqlens"], a["cache_lens"], a["num_tokens"],
+                                              a["num_seqs"], a["max_seqlen"], a["max_cache_len"], a["k_cache"],
+                                              a["v_cache"], a["cache_capacity"], a["out"], a["workspace"],
+                                              a["workspace_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(cache_lens=None), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(max_cache_len=-1), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(cache_capacity=99), da.QKRA_ERR_CAPACITY),                             # 60 cached + 40 new > 99
+    (dict(cfg=da.make_config(32, 8, 96)), da.QKRA_ERR_UNSUPPORTED),
+    (dict(workspace_bytes=1024), da.QKRA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(cache_lens=BASE + 100 * MB + 64), da.QKRA_ERR_ALIASING),                # lengths inside the K cache
+    (dict(out=BASE + 68 * MB - 64), da.QKRA_ERR_ALIASING),                        # out over cache_lens
+])
+def test_append_argument_checks(over, status):
+    cfg, a = append_args(**over)
+    assert call_append(cfg, a) == status
+    assert da.qknorm_rope_attn_last_hip_error() == 0  # rejected before any launch
+
+
+def test_append_empty_batch_is_noop():
+    cfg, a = append_args(num_tokens=0, num_seqs=0, max_seqlen=0, qkv=None, out=None, workspace=None,
+                         workspace_bytes=0, cache_lens=None)
+    assert call_append(cfg, a) == da.QKRA_OK
+
+
 def test_kernel_timing_toggle_without_launches():
     assert da.qknorm_rope_attn_set_kernel_timing(True) == 0
     assert da.qknorm_rope_attn_read_kernel_timing() == {}

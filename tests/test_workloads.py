@@ -37,3 +37,22 @@ def test_named_small_workloads():
     assert w.prefill.seqlens == [12] and len(w.chained_decode_qkv) == 9
     w = build_workload("qwen3_0p6b_prefill_varlen8")
     assert len(w.prefill.seqlens) == 8 and all(128 <= t <= 2048 for t in w.prefill.seqlens)
+
+
+def test_append_generator_positions_and_cache():
+    from workloads import make_append_inputs
+    h = HeadConfig(4, 2, 8, 1e-6, 1e4)
+    a = make_append_inputs(h, [0, 3, 5], [2, 0, 4], seed=11, dtype=torch.float32)
+    assert a.qkv.shape == (6, qkv_width(h))
+    assert a.cu_seqlens.tolist() == [0, 2, 2, 6]
+    assert a.positions.tolist() == [0, 1, 5, 6, 7, 8]
+    assert a.cache_capacity == 9 and a.k_cache.shape == (3, 2, 9, 8)  # max P + max T
+    for b, p in enumerate([0, 3, 5]):
+        assert not torch.isnan(a.k_cache[b, :, :p]).any()
+        assert torch.isnan(a.k_cache[b, :, p:]).all() and torch.isnan(a.v_cache[b, :, p:]).all()
+    assert a.max_cache_len == 5 and a.max_seqlen == 4 and a.num_tokens == 6
+
+
+def test_chunked_workload_shape():
+    from workloads import WORKLOADS
+    assert "chunked_qwen3_8b" in WORKLOADS

@@ -10,10 +10,12 @@ from .synth import (  # noqa: F401
     HeadConfig,
     PrefillInputs,
     DecodeInputs,
+    AppendInputs,
     WorkloadInputs,
     WORKLOADS,
     build_workload,
     make_prefill_inputs,
     make_decode_inputs,
+    make_append_inputs,
     qkv_width,
 )

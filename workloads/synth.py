@@ -98,6 +98,38 @@ class DecodeInputs:
 
 
 @dataclasses.dataclass
+class AppendInputs:
+    heads: HeadConfig
+    qkv: torch.Tensor            # [N, (Hq+2Hkv)*D], the chunks' new tokens, packed
+    q_norm_weight: torch.Tensor
+    k_norm_weight: torch.Tensor
+    positions: torch.Tensor      # int32 [N]: P_r + j for token j of request r
+    cu_seqlens: torch.Tensor     # int32 [B+1] over the new tokens
+    seqlens: List[int]           # T_r
+    cache_lens: torch.Tensor     # int32 [B]: P_r, entries cached before the chunk
+    past_lens: List[int]
+    cache_capacity: int
+    k_cache: torch.Tensor        # [B, Hkv, S_cap, D]
+    v_cache: torch.Tensor
+
+    @property
+    def num_tokens(self) -> int:
+        return int(sum(self.seqlens))
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.seqlens)
+
+    @property
+    def max_seqlen(self) -> int:
+        return max(self.seqlens) if self.seqlens else 0
+
+    @property
+    def max_cache_len(self) -> int:
+        return max(self.past_lens) if self.past_lens else 0
+
+
+@dataclasses.dataclass
 class WorkloadInputs:
     name: str
     description: str
@@ -106,6 +138,7 @@ class WorkloadInputs:
     # Rows for decode steps that continue the prefill's own cache: one
     # [B_prefill, W] tensor per step; step s runs at position T_r + s.
     chained_decode_qkv: List[torch.Tensor] = dataclasses.field(default_factory=list)
+    append: Optional[AppendInputs] = None
 
 
 def _sentinel(parity: bool) -> float:
@@ -185,6 +218,32 @@ def make_decode_inputs(h: HeadConfig, cache_lens: Sequence[int], seed: int, dtyp
     return DecodeInputs(heads=h, qkv=rows.to(device), q_norm_weight=wq.to(device),
                         k_norm_weight=wk.to(device), positions=lens.clone().to(device),
                         cache_lens=lens.to(device), cache_capacity=cap, k_cache=k_cache, v_cache=v_cache)
+
+
+def make_append_inputs(h: HeadConfig, past_lens: Sequence[int], chunk_lens: Sequence[int], seed: int,
+                       dtype=torch.bfloat16, device="cpu", capacity: Optional[int] = None,
+                       parity: bool = True) -> AppendInputs:
+    """A chunk of T_r new tokens per request on a cache holding P_r entries (N(0,1), as decode's)."""
+    g = torch.Generator().manual_seed(seed)
+    past = [int(x) for x in past_lens]
+    chunks = [int(x) for x in chunk_lens]
+    rows = _draw_rows(g, int(sum(chunks)), h, dtype)
+    wq = _draw_norm_weight(g, h, dtype)
+    wk = _draw_norm_weight(g, h, dtype)
+    cu = [0]
+    for t in chunks:
+        cu.append(cu[-1] + t)
+    positions = torch.cat([torch.arange(p, p + t, dtype=torch.int32) for p, t in zip(past, chunks)]) \
+        if chunks else torch.zeros((0,), dtype=torch.int32)
+    # Default capacity: the library's bound max_r P_r + max_r T_r.
+    cap = capacity if capacity is not None else max(max(past + [0]) + max(chunks + [0]), 1)
+    lens = torch.tensor(past, dtype=torch.int32)
+    k_cache, v_cache = _fill_decode_cache(h, lens, cap, seed + 1, dtype, device, parity)
+    return AppendInputs(heads=h, qkv=rows.to(device), q_norm_weight=wq.to(device), k_norm_weight=wk.to(device),
+                        positions=positions.to(device),
+                        cu_seqlens=torch.tensor(cu, dtype=torch.int32, device=device), seqlens=chunks,
+                        cache_lens=lens.to(device), past_lens=past, cache_capacity=cap, k_cache=k_cache,
+                        v_cache=v_cache)
 
 
 # ---------------------------------------------------------------------------
@@ -275,6 +334,16 @@ def _mixed_qwen3_8b(dtype, device, parity):
                           "lengths U[1,16384], Hq=32 Hkv=8 D=128", pre, dec)
 
 
+def _chunked_qwen3_8b(dtype, device, parity):
+    h = HeadConfig(32, 8, 128, 1e-6, 1e6)
+    g = torch.Generator().manual_seed(1006)
+    past = torch.randint(2048, 14336 + 1, (8,), generator=g).tolist()
+    app = make_append_inputs(h, past, [2048] * 8, 1006, dtype, device, capacity=16384, parity=parity)
+    return WorkloadInputs("chunked_qwen3_8b",
+                          "2048-token chunks appended to 8 caches holding U[2048,14336] entries, "
+                          "Hq=32 Hkv=8 D=128, base 1e6", None, None, append=app)
+
+
 WORKLOADS: Dict[str, object] = {
     "pages_t12_decode9": _pages_t12_decode9,
     "single_t64_hq4_hkv2_d64": _single_t64,
@@ -282,6 +351,7 @@ WORKLOADS: Dict[str, object] = {
     "qwen3_4b_decode64": _qwen3_4b_decode64,
     "long_prefill_32k": _long_prefill_32k,
     "mixed_qwen3_8b": _mixed_qwen3_8b,
+    "chunked_qwen3_8b": _chunked_qwen3_8b,
 }
 
 
