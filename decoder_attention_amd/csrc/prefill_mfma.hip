@@ -8,12 +8,12 @@
 // the same result).  Keys and values are read from the per-request cache that
 // kernel 1 has just written.
 //
-// Design (one workgroup = 4 wavefronts = 256 threads):
+// Design (one workgroup = 8 wavefronts = 512 threads, one workgroup per CU):
 //  * Work item = (KV-head chunk, request, query tile).  A chunk is HC query
 //    heads of one KV group; the tile is 8/HC blocks of 32 consecutive tokens,
 //    so every workgroup owns 8 "query blocks" of 32 (head, token) rows and each
 //    K/V tile it stages in LDS feeds all of them (GQA sharing).
-//  * Each wavefront owns two query blocks.  Scores are formed transposed,
+//  * Each wavefront owns one query block.  Scores are formed transposed,
 //    S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K rows come from LDS as the A
 //    operand, Q^T stays in registers as the B operand for the whole loop.  In
 //    the 32x32 accumulator layout a lane then holds one query (lane % 32) and
@@ -27,13 +27,19 @@
 //    is a per-lane multiply.
 //  * fp32 online softmax in the log2 domain (scale log2(e)/sqrt(D) folded into
 //    the exponent's FMA); the running max is raised lazily (only when a tile
-//    max exceeds it by more than 2^8), so the O rescale is rare.  K/V tiles run only up to the causal diagonal of the
-//    workgroup's last token; tiles entirely above a wavefront's rows are
-//    skipped by that wavefront; only tiles that cross the diagonal are masked.
-//  * Keys at or past the request's length are zero-filled on load so that
-//    whatever the cache holds there never reaches the accumulators.
-//  * Double-buffered LDS: the next tile's global loads are issued before the
-//    current tile's matrix work and written to the other buffer after it.
+//    max exceeds it by more than 2^8), so the O rescale is rare.  K/V tiles
+//    run only up to the causal diagonal of the workgroup's last token; tiles
+//    entirely above a wavefront's rows are skipped by that wavefront; only
+//    tiles that cross the diagonal are masked.
+//  * Keys at or past the request's length read as zeros (buffer loads with
+//    the range ending at the last key), so whatever the cache holds there
+//    never reaches the accumulators.
+//  * Three LDS slots: step kt forms tile kt+1's scores while it turns tile
+//    kt's scores into probabilities and multiplies them by tile kt's V; tile
+//    kt+2 is loaded from global memory meanwhile and stored into the third
+//    slot.  One barrier per step.  The tile loop is unrolled by six so that
+//    every slot index, hence every LDS address offset, is a compile-time
+//    constant.
 //  * Grid: heaviest (latest) query tiles first; block ids are remapped so
 //    that consecutive work items land on the same XCD (the hardware deals
 //    workgroups round-robin over the 8 XCDs), keeping one KV head's tiles in
@@ -166,33 +172,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   const bf16* vbase = v_cache + head_off;
 
   // ---- global -> registers -> LDS staging -------------------------------------
-  // Rows past kv_end are read from row kv_end-1 instead (a valid row, so the
-  // values are finite); every such key lies after every stored query row and
-  // is removed by the causal mask.
+  // Buffer loads over rows k0 .. kv_end-1 of the tile: the resource is formed
+  // per tile in scalar registers and every lane's offset is loop-invariant.
+  // Rows at or past kv_end read as zeros (finite; every such key lies after
+  // every stored query row and is removed by the causal mask).
   u32x4 kreg[KCHUNKS];
   u32x4 vreg[4];
   const int v_kq = tid % (BN / 4);   // which 4-key quad of the tile
   const int v_dq = tid / (BN / 4);   // which 8-wide slice of D
   const bool v_loader = tid < VITEMS;
+  const uint32_t v_off = static_cast<uint32_t>((4 * v_kq * D + v_dq * 8) * 2);
 
   auto load_tile = [&](int kt) {
     const int k0 = kt * BN;
+    const uint32_t bytes = static_cast<uint32_t>(kv_end - k0) * D * 2;
+    const auto rk = buffer_rsrc(kbase + static_cast<size_t>(k0) * D, bytes);
+    const auto rv = buffer_rsrc(vbase + static_cast<size_t>(k0) * D, bytes);
     static_for<KCHUNKS>([&](auto i) {
-      const int c = tid + NTHREADS * i;
-      if (KCH % NTHREADS == 0 || c < KCH) {
-        const int key = min(k0 + c / (D / 8), kv_end - 1);
-        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(key) * D + (c % (D / 8)) * 8);
-      }
+      const int c = tid + NTHREADS * i;  // 16-byte chunk c of the tile's contiguous rows
+      if (KCH % NTHREADS == 0 || c < KCH) kreg[i] = buffer_load16<false>(rk, static_cast<uint32_t>(c) * 16);
     });
     if (v_loader) {
-      static_for<4>([&](auto r) {
-        const int key = min(k0 + 4 * v_kq + r, kv_end - 1);
-        vreg[r] = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(key) * D + v_dq * 8);
-      });
+      static_for<4>([&](auto r) { vreg[r] = buffer_load16<false>(rv, v_off + decltype(r)::value * D * 2); });
     }
   };
 
-  auto store_tile = [&](int slot) {
+  // LDS slots are compile-time constants (the tile loop below is unrolled by
+  // the ring length), so every fragment address is one base register plus an
+  // immediate offset.
+  auto store_tile = [&](auto slotc) {
+    constexpr int slot = decltype(slotc)::value;
     static_for<KCHUNKS>([&](auto i) {
       const int c = tid + NTHREADS * i;
       if (KCH % NTHREADS == 0 || c < KCH)
@@ -222,7 +231,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   // ---- the matrix and softmax pieces ----------------------------------------
   // S^T = K Q^T for the tile in `slot`: lane holds query l32 and, per 32-key
   // block kb, keys 32kb + 8(j/4) + 4hi + j%4 in register j.
-  auto scores = [&](int slot, f32x16 (&S)[QB][KB]) {
+  auto scores = [&](auto slotc, f32x16 (&S)[QB][KB]) {
+    constexpr int slot = decltype(slotc)::value;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -307,11 +317,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   };
 
   // O^T += V^T P^T for the tile in `slot`.
-  auto pv = [&](int slot, const bf16x8 (&pf)[QB][KSTEPS]) {
+  auto pv = [&](auto slotc, const bf16x8 (&pf)[QB][KSTEPS]) {
+    constexpr int slot = decltype(slotc)::value;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
+      for (int db = 0; db < DB; ++db) {
         const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[slot][(db * 32 + l32) * VST + 16 * ks + 8 * hi]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -329,41 +340,61 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   // whatever the slot holds, and then dropped): that keeps the score, the
   // probability and the P.V work of a step in one branch-free block, so the
   // matrix and vector instructions can interleave.
-  auto step = [&](int kt, f32x16 (&Scur)[QB][KB], f32x16 (&Snext)[QB][KB]) {
+  // Step kt (J = kt mod 2*NSLOT) reads slots kt mod NSLOT (P.V) and kt+1 mod
+  // NSLOT (scores) and fills slot kt+2 mod NSLOT.
+  auto step = [&](auto jc, int kt, f32x16 (&Scur)[QB][KB], f32x16 (&Snext)[QB][KB]) {
+    constexpr int J = decltype(jc)::value;
+    using SlotPv = std::integral_constant<int, J % NSLOT>;
+    using SlotS = std::integral_constant<int, (J + 1) % NSLOT>;
+    using SlotLd = std::integral_constant<int, (J + 2) % NSLOT>;
     const bool prefetch = kt + 2 < ntiles;
     if (prefetch) load_tile(kt + 2);
     if (kt < wtiles) {
       bf16x8 pf[QB][KSTEPS];
-      scores((kt + 1) % NSLOT, Snext);
+      scores(SlotS{}, Snext);
       probs(Scur, pf);
-      pv(kt % NSLOT, pf);
+      pv(SlotPv{}, pf);
       if (kt + 1 < wtiles) {
         float mx[QB];
         tile_max(kt + 1, Snext, mx);
         raise_max(mx);
       }
     }
-    if (prefetch) store_tile((kt + 2) % NSLOT);
+    if (prefetch) store_tile(SlotLd{});
     __syncthreads();
   };
 
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
   load_tile(0);
-  store_tile(0);
+  store_tile(C0{});
   if (ntiles > 1) {
     load_tile(1);
-    store_tile(1);
+    store_tile(C1{});
   }
   __syncthreads();
   f32x16 sA[QB][KB], sB[QB][KB];
   {
     float mx[QB];
-    scores(0, sA);
+    scores(C0{}, sA);
     tile_max(0, sA, mx);
     raise_max(mx);
   }
-  for (int kt = 0; kt < ntiles; kt += 2) {
-    step(kt, sA, sB);
-    if (kt + 1 < ntiles) step(kt + 1, sB, sA);
+  // Unrolled by 2*NSLOT: the score buffers alternate every step and the LDS
+  // slots cycle every NSLOT steps.
+  static_assert(NSLOT == 3, "the unroll below assumes a ring of three slots");
+  for (int kt = 0; kt < ntiles; kt += 6) {
+    step(std::integral_constant<int, 0>{}, kt, sA, sB);
+    if (kt + 1 >= ntiles) break;
+    step(std::integral_constant<int, 1>{}, kt + 1, sB, sA);
+    if (kt + 2 >= ntiles) break;
+    step(std::integral_constant<int, 2>{}, kt + 2, sA, sB);
+    if (kt + 3 >= ntiles) break;
+    step(std::integral_constant<int, 3>{}, kt + 3, sB, sA);
+    if (kt + 4 >= ntiles) break;
+    step(std::integral_constant<int, 4>{}, kt + 4, sA, sB);
+    if (kt + 5 >= ntiles) break;
+    step(std::integral_constant<int, 5>{}, kt + 5, sB, sA);
   }
 
   // ---- normalise and store: lane holds query l32, d = 32*db + 8*(j/4) + 4*hi + j%4
