@@ -1,4 +1,4 @@
-"""CPU fp64 oracle of the attention layer's forward pass.
+"""CPU fp64 oracle of the attention layer's forward pass and the steps around it.
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
 and ``bench.py``'s ``cpu_baseline`` leg, never by the product library.
@@ -18,4 +18,10 @@ from .qknorm_rope_attn import (  # noqa: F401
     decode,
     prefill_append,
     round_to_bf16,
+)
+from .layer_ops import (  # noqa: F401
+    fused_add_rms_norm,
+    last_positions,
+    gather_last,
+    greedy_argmax,
 )

@@ -472,3 +472,123 @@ ALL_CHECKS = [
     check_append_split_equals_full_prefill,
     check_append_brute_force,
 ]
+
+
+# ---------------------------------------------------------------------------
+# Steps around the attention layer (oracle.layer_ops): the fused residual add
+# + RMSNorm (Code Walkthrough, section 3.2) and next-token selection (section
+# 4.1: each request's last row; section 4.3: greedy argmax).  These checks take
+# the ``oracle.layer_ops`` module.
+# ---------------------------------------------------------------------------
+
+def _torch_rms_norm(x, w, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return torch.nn.functional.rms_norm(torch.from_numpy(x), (x.shape[-1],),
+                                        torch.from_numpy(np.asarray(w, dtype=np.float64)), eps).numpy()
+
+
+def check_fused_norm_first_call(lo):
+    # No residual yet: x itself becomes the residual and the output is RMSNorm(x).
+    r = _rng(80)
+    x = r.standard_normal((6, 48)) * 2
+    w = 1 + 0.1 * r.standard_normal(48)
+    out, res = lo.fused_add_rms_norm(x, None, w, 1e-6)
+    assert np.array_equal(res, x)
+    np.testing.assert_allclose(out, _torch_rms_norm(x, w, 1e-6), rtol=1e-13, atol=1e-14)
+
+
+def check_fused_norm_adds_then_normalises(lo):
+    # Integer-valued inputs, so the sum is exact and known: the new residual is
+    # x + residual; the output is the library RMSNorm of that sum.
+    r = _rng(81)
+    x = r.integers(-8, 9, (5, 40)).astype(np.float64)
+    res0 = r.integers(-8, 9, (5, 40)).astype(np.float64)
+    w = 1 + 0.1 * r.standard_normal(40)
+    out, res = lo.fused_add_rms_norm(x, res0, w, 1e-6)
+    total = np.array([[int(a) + int(b) for a, b in zip(ra, rb)] for ra, rb in zip(x, res0)], dtype=np.float64)
+    assert np.array_equal(res, total)
+    np.testing.assert_allclose(out, _torch_rms_norm(total, w, 1e-6), rtol=1e-13, atol=1e-14)
+
+
+def check_fused_norm_constant_rows(lo):
+    # x = a*1 and residual = b*1: the output is (a+b)/sqrt((a+b)^2 + eps) * w.
+    c, eps = 24, 1e-2
+    w = 1 + 0.1 * _rng(82).standard_normal(c)
+    for a, b in ((0.25, 0.5), (-1.5, 0.25), (2.0, -2.0)):
+        out, res = lo.fused_add_rms_norm(np.full((1, c), a), np.full((1, c), b), w, eps)
+        s = a + b
+        np.testing.assert_allclose(res[0], s, rtol=0, atol=0)
+        np.testing.assert_allclose(out[0], s / math.sqrt(s * s + eps) * w, rtol=1e-14, atol=1e-15)
+
+
+def check_fused_norm_decoder_chain(lo):
+    # The pages' layer loop, written with the fused call, equals the expanded
+    # form h = x + Attn(RMSNorm(x)), out = h + MLP(RMSNorm(h)) followed by the
+    # model's final norm (section 3.2).  The sublayers are fixed stand-ins.
+    r = _rng(83)
+    n, c, layers, eps = 5, 32, 3, 1e-6
+    x0 = r.standard_normal((n, c))
+    w_in = [1 + 0.1 * r.standard_normal(c) for _ in range(layers)]
+    w_post = [1 + 0.1 * r.standard_normal(c) for _ in range(layers)]
+    w_final = 1 + 0.1 * r.standard_normal(c)
+    attn = [r.standard_normal((c, c)) / math.sqrt(c) for _ in range(layers)]
+    mlp = [r.standard_normal((c, c)) / math.sqrt(c) for _ in range(layers)]
+    x, res = x0, None
+    for i in range(layers):
+        x, res = lo.fused_add_rms_norm(x, res, w_in[i], eps)
+        x = np.tanh(x @ attn[i])
+        x, res = lo.fused_add_rms_norm(x, res, w_post[i], eps)
+        x = np.tanh(x @ mlp[i])
+    got, _ = lo.fused_add_rms_norm(x, res, w_final, eps)
+    h = x0
+    for i in range(layers):
+        h = h + np.tanh(_torch_rms_norm(h, w_in[i], eps) @ attn[i])
+        h = h + np.tanh(_torch_rms_norm(h, w_post[i], eps) @ mlp[i])
+    np.testing.assert_allclose(got, _torch_rms_norm(h, w_final, eps), rtol=1e-12, atol=1e-12)
+
+
+def check_last_positions_pages_example(lo):
+    # Section 4.1: for the input [1, 2, 3] the logits at position 2 predict the
+    # next token, so a 3-token request selects row 2.  Packed requests select
+    # cu[r+1]-1; an empty request selects nothing (-1).
+    assert list(lo.last_positions([0, 3])) == [2]
+    assert list(lo.last_positions([0, 3, 3, 7, 8])) == [2, -1, 6, 7]
+
+
+def check_gather_last_rows(lo):
+    h = _rng(84).standard_normal((8, 6))
+    g = lo.gather_last(h, [0, 3, 3, 7, 8])
+    assert np.array_equal(g[0], h[2]) and np.array_equal(g[2], h[6]) and np.array_equal(g[3], h[7])
+    assert np.isnan(g[1]).all()
+
+
+def check_argmax_library(lo):
+    # Rows without ties: numpy's and torch's argmax.
+    z = _rng(85).standard_normal((7, 300))
+    got = lo.greedy_argmax(z)
+    assert np.array_equal(got, np.argmax(z, axis=1))
+    assert np.array_equal(got, torch.argmax(torch.from_numpy(z), dim=-1).numpy())
+
+
+def check_argmax_ties_and_nan(lo):
+    # Ties go to the lowest index; a NaN beats every number (first NaN wins).
+    z = np.zeros((5, 10))
+    z[0, [3, 7]] = 5.0
+    z[2, 4], z[2, 8] = np.nan, 100.0
+    z[3, [6, 2]] = np.nan
+    z[4] = -np.inf
+    z[4, 9] = -1e300
+    assert list(lo.greedy_argmax(z)) == [3, 0, 4, 2, 9]
+    assert list(np.argmax(z, axis=1)) == [3, 0, 4, 2, 9]
+
+
+LAYER_OPS_CHECKS = [
+    check_fused_norm_first_call,
+    check_fused_norm_adds_then_normalises,
+    check_fused_norm_constant_rows,
+    check_fused_norm_decoder_chain,
+    check_last_positions_pages_example,
+    check_gather_last_rows,
+    check_argmax_library,
+    check_argmax_ties_and_nan,
+]

@@ -9,6 +9,7 @@ import math
 import numpy as np
 import pytest
 
+import oracle.layer_ops as lo
 import oracle.qknorm_rope_attn as orc
 import pins
 
@@ -157,6 +158,67 @@ def test_planted_mistake_is_caught(name, monkeypatch):
         try:
             check(orc)
         except Exception as exc:  # any failure (assertion, shape error) means the pin noticed
+            caught.append((check.__name__, type(exc).__name__))
+            break
+    assert caught, f"mutant {name} passed every pin"
+
+
+# ---- steps around the attention layer (oracle.layer_ops) ----------------------
+
+LO_REAL = {name: getattr(lo, name) for name in ("fused_add_rms_norm", "last_positions", "greedy_argmax")}
+
+
+def _fused_residual_not_updated(x, residual, weight, eps):
+    out, r = LO_REAL["fused_add_rms_norm"](x, residual, weight, eps)
+    return out, (np.asarray(x, dtype=np.float64) if residual is None else np.asarray(residual, dtype=np.float64))
+
+
+def _fused_normalises_x(x, residual, weight, eps):
+    _, r = LO_REAL["fused_add_rms_norm"](x, residual, weight, eps)
+    return orc.rms_norm(x, weight, eps), r
+
+
+def _fused_adds_after_norm(x, residual, weight, eps):
+    if residual is None:
+        return LO_REAL["fused_add_rms_norm"](x, residual, weight, eps)
+    r = np.asarray(x, dtype=np.float64) + np.asarray(residual, dtype=np.float64)
+    return orc.rms_norm(x, weight, eps) + np.asarray(residual, dtype=np.float64), r
+
+
+def _first_position(cu_seqlens):
+    cu = [int(c) for c in np.asarray(cu_seqlens).tolist()]
+    return np.array([cu[r] if cu[r + 1] > cu[r] else -1 for r in range(len(cu) - 1)], dtype=np.int64)
+
+
+def _argmax_last_tie(logits):
+    z = np.asarray(logits, dtype=np.float64)[:, ::-1]
+    return z.shape[1] - 1 - LO_REAL["greedy_argmax"](z)
+
+
+def _argmax_ignores_nan(logits):
+    z = np.asarray(logits, dtype=np.float64)
+    return LO_REAL["greedy_argmax"](np.where(np.isnan(z), -np.inf, z))
+
+
+LO_MUTANTS = {
+    "fused_residual_not_updated": ("fused_add_rms_norm", _fused_residual_not_updated),
+    "fused_normalises_x_not_sum": ("fused_add_rms_norm", _fused_normalises_x),
+    "fused_adds_after_norm": ("fused_add_rms_norm", _fused_adds_after_norm),
+    "gather_first_position": ("last_positions", _first_position),
+    "argmax_last_tie": ("greedy_argmax", _argmax_last_tie),
+    "argmax_ignores_nan": ("greedy_argmax", _argmax_ignores_nan),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LO_MUTANTS))
+def test_planted_layer_ops_mistake_is_caught(name, monkeypatch):
+    attr, fn = LO_MUTANTS[name]
+    monkeypatch.setattr(lo, attr, fn)
+    caught = []
+    for check in pins.LAYER_OPS_CHECKS:
+        try:
+            check(lo)
+        except Exception as exc:
             caught.append((check.__name__, type(exc).__name__))
             break
     assert caught, f"mutant {name} passed every pin"

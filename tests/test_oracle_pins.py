@@ -2,6 +2,7 @@
 
 import pytest
 
+import oracle.layer_ops as lo
 import oracle.qknorm_rope_attn as orc
 import pins
 
@@ -9,6 +10,11 @@ import pins
 @pytest.mark.parametrize("check", pins.ALL_CHECKS, ids=lambda c: c.__name__)
 def test_pin(check):
     check(orc)
+
+
+@pytest.mark.parametrize("check", pins.LAYER_OPS_CHECKS, ids=lambda c: c.__name__)
+def test_layer_ops_pin(check):
+    check(lo)
 
 
 def test_round_to_bf16_matches_torch():
