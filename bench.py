@@ -46,6 +46,9 @@ KERNEL_SOURCES = {
     "decode_plan": ["decoder_attention_amd/csrc/decode_mfma.hip"] + _COMMON,
     "qknorm_rope_kv_prefill": ["decoder_attention_amd/csrc/qknorm_rope.hip"] + _COMMON,
     "qknorm_rope_kv_decode": ["decoder_attention_amd/csrc/qknorm_rope.hip"] + _COMMON,
+    "fused_add_rmsnorm": ["decoder_attention_amd/csrc/layer_ops.hip"] + _COMMON,
+    "gather_last": ["decoder_attention_amd/csrc/layer_ops.hip"] + _COMMON,
+    "argmax_partial": ["decoder_attention_amd/csrc/layer_ops.hip"] + _COMMON,
 }
 
 
@@ -121,12 +124,44 @@ class Runner:
             args = (cfg, d.qkv, d.q_norm_weight, d.k_norm_weight, d.positions, d.cache_lens, d.num_seqs,
                     d.max_cache_len, d.k_cache, d.v_cache, d.cache_capacity, out, ws, ws_bytes)
             self.calls.append((da.qknorm_rope_attn_decode, args, (out, ws)))
+        if w.norm is not None:
+            n = w.norm
+            out = torch.empty_like(n.x)
+            res = n.residual if n.has_residual else torch.empty_like(n.x)
+            args = (da_dtype(da, n.x), n.rms_eps, n.x, res, n.has_residual, n.weight, out, n.x.shape[0],
+                    n.x.shape[1])
+            self.calls.append((da.qknorm_rope_attn_fused_add_rmsnorm, args, (out, res)))
+        if w.next_token is not None:
+            nt = w.next_token
+            b, c, v = len(nt.seqlens), nt.hidden.shape[1], nt.logits.shape[1]
+            last = torch.empty((b, c), dtype=nt.hidden.dtype, device=nt.hidden.device)
+            args = (da_dtype(da, nt.hidden), nt.hidden, nt.cu_seqlens, nt.hidden.shape[0], b, c, last)
+            self.calls.append((da.qknorm_rope_attn_gather_last, args, (last,)))
+            idx = torch.empty((b,), dtype=torch.int32, device=nt.logits.device)
+            ws_bytes = da.qknorm_rope_attn_argmax_workspace_bytes(b, v)
+            ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=nt.logits.device)
+            args = (da_dtype(da, nt.logits), nt.logits, b, v, nt.logits.stride(0), idx, ws, ws_bytes)
+            self.calls.append((da.qknorm_rope_attn_argmax, args, (idx, ws)))
 
     def step(self):
         for fn, args, _ in self.calls:
             status = fn(*args)
             if status != 0:
                 raise self.da.QkraError(status, fn.__name__)
+
+    def hbm_bytes(self):
+        """Algorithmic HBM bytes per launch of the kernels outside the attention roofline."""
+        out = {}
+        if self.w.norm is not None:
+            n = self.w.norm
+            row = n.x.shape[1] * n.x.element_size()
+            out["fused_add_rmsnorm"] = float(n.x.shape[0] * row * (4 if n.has_residual else 3) + row)
+        if self.w.next_token is not None:
+            nt = self.w.next_token
+            row = nt.hidden.shape[1] * nt.hidden.element_size()
+            out["gather_last"] = float(2 * row * sum(1 for t in nt.seqlens if t > 0))
+            out["argmax_partial"] = float(nt.logits.shape[0] * nt.logits.shape[1] * nt.logits.element_size())
+        return out
 
     def work(self):
         F = B = 0.0
@@ -141,6 +176,10 @@ class Runner:
             B = decode_kv_bytes(self.w.decode.cache_lens.tolist(), h.num_kv_heads, h.head_dim,
                                 self.w.decode.qkv.element_size())
         return F, B
+
+
+def da_dtype(da, t):
+    return da.QKRA_BF16 if str(t.dtype) == "torch.bfloat16" else da.QKRA_FP32
 
 
 def _timed_region(runner, steps: int) -> float:
@@ -179,10 +218,14 @@ def time_steps(runner, steps: int, warmup: int):
     return ms, ms_events, kernels
 
 
-def roofline_for(name, kernels, F, B, workload):
+def roofline_for(name, kernels, F, B, workload, layer_bytes=None):
     total_ms, launches = kernels[name]
     avg_s = total_ms / launches / 1e3
-    if name.startswith("prefill_attn"):
+    if layer_bytes and name in layer_bytes:
+        achieved = layer_bytes[name] / avg_s / 1e9
+        rf = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+              "frac": achieved / PEAK_HBM_GBPS, "bytes_per_launch": layer_bytes[name]}
+    elif name.startswith("prefill_attn"):
         achieved = F / avg_s / 1e12
         rf = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
               "frac": achieved / PEAK_MFMA_TFLOPS}
@@ -329,6 +372,14 @@ def main(argv=None):
             extra[name] = {"ms_per_call": ems, "kernel": roofline_for(key, ek, eF, eB, name),
                            "call_rate": (eF / (ems / 1e3) / 1e12) if eF else (eB / (ems / 1e3) / 1e9),
                            "call_rate_unit": "TFLOP/s" if eF else "GB/s"}
+            del er, ew
+            torch.cuda.empty_cache()
+        # Steps next to the attention layer, each against the HBM roofline.
+        for name, steps in (("residual_rmsnorm_qwen3_8b", 20), ("next_token_qwen3_8b", 20)):
+            ew, er, ems, _, ek, _, _ = measure(name, steps, 2)
+            lb = er.hbm_bytes()
+            extra[name] = {"ms_per_call": ems,
+                           "kernels": {k: roofline_for(k, ek, 0.0, 0.0, name, lb) for k in lb if k in ek}}
             del er, ew
             torch.cuda.empty_cache()
 

@@ -1,9 +1,8 @@
 """QK-RMSNorm + RoPE + causal grouped-query attention for MI355X (gfx950).
 
 The computation lives in the HIP library ``libqknorm_rope_attn.so`` (C ABI in
-``include/qknorm_rope_attn.h``); this package binds it and adds three
-conveniences that allocate outputs and workspace with PyTorch before calling
-it.  PyTorch supplies device memory and the current stream only.
+``include/qknorm_rope_attn.h``); this package binds it and adds conveniences
+that allocate outputs and workspace with PyTorch before calling it.  PyTorch supplies device memory and the current stream only.
 """
 
 from __future__ import annotations
@@ -36,6 +35,10 @@ from .binding import (  # noqa: F401
     qknorm_rope_attn_set_kernel_timing,
     qknorm_rope_attn_read_kernel_timing,
     qknorm_rope_attn_kernel_name,
+    qknorm_rope_attn_fused_add_rmsnorm,
+    qknorm_rope_attn_gather_last,
+    qknorm_rope_attn_argmax_workspace_bytes,
+    qknorm_rope_attn_argmax,
 )
 
 
@@ -105,3 +108,58 @@ def decode(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cache_
                                      workspace.numel() * workspace.element_size(), stream)
     check(status, "qknorm_rope_attn_decode")
     return out, workspace
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return QKRA_BF16
+    if t.dtype == torch.float32:
+        return QKRA_FP32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def fused_add_rmsnorm(x, residual, weight, eps: float, has_residual: bool, out=None, stream=None):
+    """Runs ``qknorm_rope_attn_fused_add_rmsnorm``; returns out [N, C] (residual is updated in place)."""
+    import torch
+
+    _require_device(x, residual, weight)
+    if out is None:
+        out = torch.empty_like(x)
+    status = qknorm_rope_attn_fused_add_rmsnorm(_dtype_code(x), eps, x, residual, has_residual, weight, out,
+                                                x.shape[0], x.shape[1], stream)
+    check(status, "qknorm_rope_attn_fused_add_rmsnorm")
+    return out
+
+
+def gather_last(hidden, cu_seqlens, out=None, stream=None):
+    """Runs ``qknorm_rope_attn_gather_last``; returns [B, C] (rows of empty requests are left as allocated)."""
+    import torch
+
+    _require_device(hidden, cu_seqlens)
+    b = cu_seqlens.shape[0] - 1
+    if out is None:
+        out = torch.zeros((b, hidden.shape[1]), dtype=hidden.dtype, device=hidden.device)
+    status = qknorm_rope_attn_gather_last(_dtype_code(hidden), hidden, cu_seqlens, hidden.shape[0], b,
+                                          hidden.shape[1], out, stream)
+    check(status, "qknorm_rope_attn_gather_last")
+    return out
+
+
+def argmax(logits, out=None, workspace=None, stream=None):
+    """Runs ``qknorm_rope_attn_argmax`` on a [B, V] tensor (rows may be strided); returns int32 [B]."""
+    import torch
+
+    if not logits.is_cuda or logits.stride(1) != 1:
+        raise ValueError("logits must be a GPU tensor with contiguous rows")
+    b, v = logits.shape
+    if out is None:
+        out = torch.empty((b,), dtype=torch.int32, device=logits.device)
+    need = qknorm_rope_attn_argmax_workspace_bytes(b, v)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=logits.device)
+    status = qknorm_rope_attn_argmax(_dtype_code(logits), logits, b, v, logits.stride(0), out, workspace,
+                                     workspace.numel(), stream)
+    check(status, "qknorm_rope_attn_argmax")
+    return out

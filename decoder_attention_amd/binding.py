@@ -72,6 +72,10 @@ _SIGNATURES = {
     "qknorm_rope_attn_read_kernel_timing": (_I32, [ctypes.POINTER(ctypes.c_double),
                                                    ctypes.POINTER(ctypes.c_int64), _I32]),
     "qknorm_rope_attn_kernel_name": (ctypes.c_char_p, [_I32]),
+    "qknorm_rope_attn_fused_add_rmsnorm": (_I32, [_I32, ctypes.c_float, _P, _P, _I32, _P, _P, _I32, _I32, _P]),
+    "qknorm_rope_attn_gather_last": (_I32, [_I32, _P, _P, _I32, _I32, _I32, _P, _P]),
+    "qknorm_rope_attn_argmax_workspace_bytes": (_SZ, [_I32, _I32]),
+    "qknorm_rope_attn_argmax": (_I32, [_I32, _P, _I32, _I32, ctypes.c_int64, _P, _P, _SZ, _P]),
 }
 
 
@@ -178,7 +182,30 @@ def qknorm_rope_attn_kernel_name(kernel_id: int) -> str:
     return lib().qknorm_rope_attn_kernel_name(int(kernel_id)).decode()
 
 
-def qknorm_rope_attn_read_kernel_timing(max_kernels: int = 8):
+def qknorm_rope_attn_fused_add_rmsnorm(dtype: int, rms_eps: float, x, residual, has_residual: bool, weight, out,
+                                       num_tokens: int, hidden_size: int, stream=None) -> int:
+    return lib().qknorm_rope_attn_fused_add_rmsnorm(int(dtype), float(rms_eps), _ptr(x), _ptr(residual),
+                                                    1 if has_residual else 0, _ptr(weight), _ptr(out),
+                                                    int(num_tokens), int(hidden_size), _stream(stream))
+
+
+def qknorm_rope_attn_gather_last(dtype: int, hidden, cu_seqlens, num_tokens: int, num_seqs: int, hidden_size: int,
+                                 out, stream=None) -> int:
+    return lib().qknorm_rope_attn_gather_last(int(dtype), _ptr(hidden), _ptr(cu_seqlens), int(num_tokens),
+                                              int(num_seqs), int(hidden_size), _ptr(out), _stream(stream))
+
+
+def qknorm_rope_attn_argmax_workspace_bytes(num_rows: int, vocab: int) -> int:
+    return int(lib().qknorm_rope_attn_argmax_workspace_bytes(int(num_rows), int(vocab)))
+
+
+def qknorm_rope_attn_argmax(dtype: int, logits, num_rows: int, vocab: int, row_stride: int, out_index, workspace,
+                            workspace_bytes: int, stream=None) -> int:
+    return lib().qknorm_rope_attn_argmax(int(dtype), _ptr(logits), int(num_rows), int(vocab), int(row_stride),
+                                         _ptr(out_index), _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def qknorm_rope_attn_read_kernel_timing(max_kernels: int = 16):
     """Returns {kernel name: (total ms, launches)} for kernels launched since the last read."""
     ms = (ctypes.c_double * max_kernels)()
     n = (ctypes.c_int64 * max_kernels)()

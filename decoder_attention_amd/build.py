@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libqknorm_rope_attn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["qknorm_rope.hip", "prefill_mfma.hip", "prefill_fp32.hip", "decode.hip", "decode_mfma.hip", "api.hip"]
+SOURCES = ["qknorm_rope.hip", "prefill_mfma.hip", "prefill_fp32.hip", "decode.hip", "decode_mfma.hip", "layer_ops.hip", "api.hip"]
 ARCH = "gfx950"
 CFLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-fvisibility=hidden",

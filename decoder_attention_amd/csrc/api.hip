@@ -134,6 +134,8 @@ int32_t hip_status(hipError_t err) {
 
 double log2_of(double base) { return std::log2(base); }
 
+constexpr int kMaxNormHidden = 16 * 256 * 8;  // 16 pieces of 8 per thread, 256 threads
+
 float softmax_scale_log2(int head_dim) {
   return static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(head_dim)));
 }
@@ -384,6 +386,107 @@ QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv
   return hip_status(err);
 }
 
+// ---- steps next to the attention layer ----------------------------------------
+
+QKRA_API int32_t qknorm_rope_attn_fused_add_rmsnorm(int32_t dtype, float rms_eps, const void* x, void* residual,
+                                                    int32_t has_residual, const void* weight, void* out,
+                                                    int32_t num_tokens, int32_t hidden_size, void* hip_stream) {
+  if (dtype != QKRA_BF16 && dtype != QKRA_FP32) return QKRA_ERR_UNSUPPORTED;
+  if (!(rms_eps >= 0.0f) || !std::isfinite(rms_eps)) return QKRA_ERR_INVALID_ARGUMENT;
+  if (num_tokens < 0 || hidden_size <= 0 || hidden_size % 8 != 0) return QKRA_ERR_INVALID_ARGUMENT;
+  if (hidden_size > kMaxNormHidden) return QKRA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return QKRA_OK;
+  if (!x || !residual || !weight || !out) return QKRA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(residual) || !aligned16(weight) || !aligned16(out)) return QKRA_ERR_INVALID_ARGUMENT;
+  const size_t rows = static_cast<size_t>(num_tokens) * hidden_size * elem_size(dtype);
+  const Range r_x = range_of(x, rows), r_res = range_of(residual, rows), r_out = range_of(out, rows);
+  const Range r_w = range_of(weight, static_cast<size_t>(hidden_size) * elem_size(dtype));
+  const bool res_is_x = residual == x && !has_residual;
+  if (out != x && overlap(r_out, r_x)) return QKRA_ERR_ALIASING;
+  if (!res_is_x && overlap(r_res, r_x)) return QKRA_ERR_ALIASING;
+  if (overlap(r_out, r_res) || overlap(r_out, r_w) || overlap(r_res, r_w)) return QKRA_ERR_ALIASING;
+  AddRmsNormArgs a{};
+  a.x = x;
+  a.residual = residual;
+  a.weight = weight;
+  a.out = out;
+  a.num_tokens = num_tokens;
+  a.hidden_size = hidden_size;
+  a.dtype = dtype;
+  a.has_residual = has_residual ? 1 : 0;
+  a.copy_residual = (!has_residual && !res_is_x) ? 1 : 0;
+  a.rms_eps = rms_eps;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  return hip_status(timed(kKernelAddRmsNorm, stream, [&] { return launch_fused_add_rmsnorm(a, stream); }));
+}
+
+QKRA_API int32_t qknorm_rope_attn_gather_last(int32_t dtype, const void* hidden, const int32_t* cu_seqlens,
+                                              int32_t num_tokens, int32_t num_seqs, int32_t hidden_size, void* out,
+                                              void* hip_stream) {
+  if (dtype != QKRA_BF16 && dtype != QKRA_FP32) return QKRA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_seqs < 0 || hidden_size <= 0) return QKRA_ERR_INVALID_ARGUMENT;
+  const size_t row_bytes = static_cast<size_t>(hidden_size) * elem_size(dtype);
+  if (row_bytes % 16 != 0 || row_bytes > (1u << 30)) return QKRA_ERR_INVALID_ARGUMENT;
+  if (num_seqs == 0) return QKRA_OK;
+  if (!cu_seqlens || !out || (num_tokens > 0 && !hidden)) return QKRA_ERR_INVALID_ARGUMENT;
+  if ((num_tokens > 0 && !aligned16(hidden)) || !aligned16(out) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+    return QKRA_ERR_INVALID_ARGUMENT;
+  const Range r_out = range_of(out, num_seqs * row_bytes);
+  if (overlap(r_out, range_of(hidden, num_tokens * row_bytes)) ||
+      overlap(r_out, range_of(cu_seqlens, (num_seqs + 1ull) * 4)))
+    return QKRA_ERR_ALIASING;
+  GatherLastArgs a{};
+  a.hidden = hidden;
+  a.cu_seqlens = cu_seqlens;
+  a.out = out;
+  a.num_rows = num_tokens;
+  a.num_seqs = num_seqs;
+  a.hidden_size = hidden_size;
+  a.dtype = dtype;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  return hip_status(timed(kKernelGatherLast, stream, [&] { return launch_gather_last(a, stream); }));
+}
+
+QKRA_API size_t qknorm_rope_attn_argmax_workspace_bytes(int32_t num_rows, int32_t vocab) {
+  if (num_rows < 0 || vocab <= 0) return 0;
+  const size_t recs = static_cast<size_t>(num_rows) * argmax_segments(std::max(num_rows, 1), vocab);
+  return 2 * align_up(recs * 4);
+}
+
+QKRA_API int32_t qknorm_rope_attn_argmax(int32_t dtype, const void* logits, int32_t num_rows, int32_t vocab,
+                                         int64_t row_stride, int32_t* out_index, void* workspace,
+                                         size_t workspace_bytes, void* hip_stream) {
+  if (dtype != QKRA_BF16 && dtype != QKRA_FP32) return QKRA_ERR_UNSUPPORTED;
+  if (num_rows < 0 || vocab <= 0 || row_stride < vocab || row_stride % 8 != 0) return QKRA_ERR_INVALID_ARGUMENT;
+  if (num_rows == 0) return QKRA_OK;
+  if (!logits || !out_index) return QKRA_ERR_INVALID_ARGUMENT;
+  const int segments = argmax_segments(num_rows, vocab);
+  if (static_cast<long long>(num_rows) * segments >= (1LL << 31)) return QKRA_ERR_UNSUPPORTED;
+  const size_t need = qknorm_rope_attn_argmax_workspace_bytes(num_rows, vocab);
+  if (workspace_bytes < need) return QKRA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return QKRA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(logits) || !aligned16(workspace) || (reinterpret_cast<uintptr_t>(out_index) & 3u))
+    return QKRA_ERR_INVALID_ARGUMENT;
+  const size_t es = elem_size(dtype);
+  const Range r_in = range_of(logits, ((num_rows - 1) * static_cast<size_t>(row_stride) + vocab) * es);
+  const Range r_idx = range_of(out_index, num_rows * 4ull), r_ws = range_of(workspace, need);
+  if (overlap(r_idx, r_in) || overlap(r_ws, r_in) || overlap(r_idx, r_ws)) return QKRA_ERR_ALIASING;
+  ArgmaxArgs a{};
+  a.logits = logits;
+  a.row_stride = row_stride;
+  a.num_rows = num_rows;
+  a.vocab = vocab;
+  a.dtype = dtype;
+  a.segments = segments;
+  a.part_v = static_cast<float*>(workspace);
+  a.part_i = reinterpret_cast<int*>(static_cast<char*>(workspace) + need / 2);
+  a.out = out_index;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t err = timed(kKernelArgmaxPartial, stream, [&] { return launch_argmax_partial(a, stream); });
+  if (err != hipSuccess) return hip_status(err);
+  return hip_status(timed(kKernelArgmaxFinal, stream, [&] { return launch_argmax_final(a, stream); }));
+}
+
 QKRA_API int32_t qknorm_rope_attn_set_kernel_timing(int32_t enable) {
   std::lock_guard<std::mutex> lock(g_timing_mu);
   g_timing_enabled = enable != 0;
@@ -430,6 +533,10 @@ QKRA_API const char* qknorm_rope_attn_kernel_name(int32_t kernel_id) {
     case kKernelDecodeSplit: return "decode_attn_split";
     case kKernelDecodeCombine: return "decode_attn_combine";
     case kKernelDecodePlan: return "decode_plan";
+    case kKernelAddRmsNorm: return "fused_add_rmsnorm";
+    case kKernelGatherLast: return "gather_last";
+    case kKernelArgmaxPartial: return "argmax_partial";
+    case kKernelArgmaxFinal: return "argmax_final";
     default: return "unknown";
   }
 }

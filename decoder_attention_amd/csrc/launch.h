@@ -16,7 +16,11 @@ enum KernelId : int {
   kKernelDecodeCombine = 4,
   kKernelQkNormRopeDecode = 5,
   kKernelDecodePlan = 6,
-  kNumKernels = 7,
+  kKernelAddRmsNorm = 7,
+  kKernelGatherLast = 8,
+  kKernelArgmaxPartial = 9,
+  kKernelArgmaxFinal = 10,
+  kNumKernels = 11,
 };
 
 // Kernel 1: per token row, RMSNorm + RoPE of the Q and K heads; q~ to
@@ -104,5 +108,40 @@ hipError_t launch_decode_combine(const DecodeAttnArgs& a, hipStream_t stream);
 hipError_t launch_decode_plan(const DecodeAttnArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeAttnArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma_combine(const DecodeAttnArgs& a, hipStream_t stream);
+
+// Steps next to the attention layer (layer_ops.hip).
+struct AddRmsNormArgs {
+  const void* x;          // [N, C]
+  void* residual;         // [N, C]: read when has_residual, written when has_residual or copy_residual
+  const void* weight;     // [C]
+  void* out;              // [N, C] (may be x itself)
+  int num_tokens, hidden_size, dtype;
+  int has_residual;       // 1: residual := x + residual; 0: residual := x
+  int copy_residual;      // with has_residual 0: write x into residual (0 when they are one buffer)
+  float rms_eps;
+};
+hipError_t launch_fused_add_rmsnorm(const AddRmsNormArgs& a, hipStream_t stream);
+
+struct GatherLastArgs {
+  const void* hidden;     // [num_rows, C]
+  const int32_t* cu_seqlens;
+  void* out;              // [num_seqs, C]
+  int num_rows, num_seqs, hidden_size, dtype;
+};
+hipError_t launch_gather_last(const GatherLastArgs& a, hipStream_t stream);
+
+struct ArgmaxArgs {
+  const void* logits;     // row b at logits + b * row_stride elements, vocab entries each
+  long long row_stride;
+  int num_rows, vocab, dtype;
+  int segments;           // per row; pass-1 records [num_rows, segments]
+  float* part_v;
+  int* part_i;
+  int32_t* out;           // [num_rows]
+};
+int argmax_segments(int num_rows, int vocab);
+int argmax_segment_length(int vocab, int segments);
+hipError_t launch_argmax_partial(const ArgmaxArgs& a, hipStream_t stream);
+hipError_t launch_argmax_final(const ArgmaxArgs& a, hipStream_t stream);
 
 }  // namespace qkra

@@ -200,6 +200,78 @@ QKRA_API int32_t qknorm_rope_attn_last_hip_error(void);
 QKRA_API int32_t qknorm_rope_attn_version(void);
 
 /*
+ * ---- Steps next to the attention layer -------------------------------------
+ * The three calls below share the conventions above (device pointers, the
+ * caller's stream, host-side checks, QKRA_* status) but take no qkra_config:
+ * they work on hidden-size rows, not on heads.
+ */
+
+/*
+ * Fused residual add + RMSNorm, the step before every attention and MLP
+ * sublayer (zero-to-sglang, "Chapter 3 Forward Pass and Generation (Code
+ * Walkthrough)", section 3.2 "Computation inside a decoder layer"): the first
+ * call of a forward pass keeps x as the residual stream; every later call adds
+ * the sublayer output to it.  Row by row, over the hidden_size entries:
+ *
+ *   has_residual == 0:  residual := x;             out := RMSNorm(x) * weight
+ *   has_residual != 0:  residual := x + residual;  out := RMSNorm(x + residual) * weight
+ *   RMSNorm(r) = r / sqrt(mean(r^2) + rms_eps)
+ *
+ *   dtype          QKRA_BF16 or QKRA_FP32: element type of x, residual, weight, out.
+ *   x              [num_tokens, hidden_size].
+ *   residual       [num_tokens, hidden_size], read (has_residual) and written.
+ *                  With has_residual == 0 it may be x itself, and then nothing
+ *                  is copied; otherwise it must not overlap x.
+ *   weight         [hidden_size].
+ *   out            [num_tokens, hidden_size]; may be exactly x (in place);
+ *                  must not overlap residual or weight.
+ *   hidden_size    a multiple of 8, at most 32768 (QKRA_ERR_UNSUPPORTED above).
+ * The sum is formed in fp32; residual keeps it rounded to the dtype and out
+ * normalises the fp32 sum.  All pointers 16-byte aligned.  num_tokens == 0 is a
+ * no-op returning QKRA_OK.
+ */
+QKRA_API int32_t qknorm_rope_attn_fused_add_rmsnorm(int32_t dtype, float rms_eps, const void* x, void* residual,
+                                                    int32_t has_residual, const void* weight, void* out,
+                                                    int32_t num_tokens, int32_t hidden_size, void* hip_stream);
+
+/*
+ * Each request's last row of the packed hidden states, the only row the LM
+ * head reads (same page, section 4.1 "Keep the last position of each
+ * request": the logits at a request's last position predict its next token).
+ *
+ *   hidden         [num_tokens, hidden_size] in the dtype.
+ *   cu_seqlens     int32 [num_seqs+1] (device), as for the prefill calls.
+ *   out            [num_seqs, hidden_size]: row r := hidden[cu[r+1]-1] for every
+ *                  request with tokens; rows of requests without tokens are
+ *                  not written.  Must not overlap hidden or cu_seqlens.
+ *   hidden_size    hidden_size * element size a multiple of 16 bytes.
+ * hidden and out 16-byte aligned.  num_seqs == 0 is a no-op.
+ */
+QKRA_API int32_t qknorm_rope_attn_gather_last(int32_t dtype, const void* hidden, const int32_t* cu_seqlens,
+                                              int32_t num_tokens, int32_t num_seqs, int32_t hidden_size, void* out,
+                                              void* hip_stream);
+
+/*
+ * Greedy choice of the next token: per logits row, the index of the largest
+ * value (same page, section 4.3 "Find sampling in the engine": a fully greedy
+ * batch takes the argmax of each row).  Ties go to the lowest index; a NaN
+ * counts as larger than every number, so the first NaN of a row wins.
+ *
+ *   logits         row b at logits + b * row_stride elements, vocab entries,
+ *                  in the dtype; row_stride >= vocab and a multiple of 8;
+ *                  16-byte aligned.
+ *   out_index      int32 [num_rows].
+ *   workspace      at least qknorm_rope_attn_argmax_workspace_bytes(num_rows,
+ *                  vocab) bytes, 16-byte aligned: per-segment (value, index)
+ *                  records.
+ * num_rows == 0 is a no-op.
+ */
+QKRA_API size_t qknorm_rope_attn_argmax_workspace_bytes(int32_t num_rows, int32_t vocab);
+QKRA_API int32_t qknorm_rope_attn_argmax(int32_t dtype, const void* logits, int32_t num_rows, int32_t vocab,
+                                         int64_t row_stride, int32_t* out_index, void* workspace,
+                                         size_t workspace_bytes, void* hip_stream);
+
+/*
  * Per-kernel timing, for benchmarks.  While enabled, every kernel launch is
  * bracketed by two hipEvents recorded on the launch stream.
  * qknorm_rope_attn_read_kernel_timing() waits for those events, writes for each

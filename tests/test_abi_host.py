@@ -211,3 +211,113 @@ def test_kernel_timing_toggle_without_launches():
     assert da.qknorm_rope_attn_set_kernel_timing(True) == 0
     assert da.qknorm_rope_attn_read_kernel_timing() == {}
     assert da.qknorm_rope_attn_set_kernel_timing(False) == 0
+
+
+# ---- steps next to the attention layer ------------------------------------------
+
+def norm_args(**over):
+    a = dict(dtype=da.QKRA_BF16, eps=1e-6, x=BASE, residual=BASE + 64 * MB, has_residual=True,
+             weight=BASE + 128 * MB, out=BASE + 192 * MB, num_tokens=100, hidden_size=4096, stream=0)
+    a.update(over)
+    return a
+
+
+def call_norm(a):
+    return da.qknorm_rope_attn_fused_add_rmsnorm(a["dtype"], a["eps"], a["x"], a["residual"], a["has_residual"],
+                                                 a["weight"], a["out"], a["num_tokens"], a["hidden_size"],
+                                                 a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=7), da.QKRA_ERR_UNSUPPORTED),
+    (dict(eps=-1.0), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(eps=float("nan")), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(hidden_size=4100), da.QKRA_ERR_INVALID_ARGUMENT),                 # not a multiple of 8
+    (dict(hidden_size=0), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(hidden_size=32776), da.QKRA_ERR_UNSUPPORTED),                     # above 32768
+    (dict(num_tokens=-1), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(weight=None), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(out=BASE + 192 * MB + 8), da.QKRA_ERR_INVALID_ARGUMENT),          # misaligned
+    (dict(out=BASE + 4096), da.QKRA_ERR_ALIASING),                          # partly over x
+    (dict(out=BASE + 64 * MB), da.QKRA_ERR_ALIASING),                       # out is the residual
+    (dict(residual=BASE), da.QKRA_ERR_ALIASING),                            # residual is x, but it is read
+    (dict(weight=BASE + 64 * MB + 1024), da.QKRA_ERR_ALIASING),             # weight inside the residual
+])
+def test_fused_add_rmsnorm_argument_checks(over, status):
+    assert call_norm(norm_args(**over)) == status
+    assert da.qknorm_rope_attn_last_hip_error() == 0
+
+
+def test_fused_add_rmsnorm_empty_batch_is_noop():
+    assert call_norm(norm_args(num_tokens=0, x=None, residual=None, weight=None, out=None)) == da.QKRA_OK
+
+
+def gather_args(**over):
+    a = dict(dtype=da.QKRA_BF16, hidden=BASE, cu_seqlens=BASE + 64 * MB, num_tokens=100, num_seqs=4,
+             hidden_size=4096, out=BASE + 128 * MB, stream=0)
+    a.update(over)
+    return a
+
+
+def call_gather(a):
+    return da.qknorm_rope_attn_gather_last(a["dtype"], a["hidden"], a["cu_seqlens"], a["num_tokens"], a["num_seqs"],
+                                           a["hidden_size"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=2), da.QKRA_ERR_UNSUPPORTED),
+    (dict(hidden_size=4), da.QKRA_ERR_INVALID_ARGUMENT),                    # 8 bytes: not a 16-byte multiple
+    (dict(num_seqs=-1), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(cu_seqlens=None), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(out=BASE + 128 * MB + 4), da.QKRA_ERR_INVALID_ARGUMENT),          # misaligned
+    (dict(out=BASE + 8192), da.QKRA_ERR_ALIASING),                          # inside hidden
+    (dict(out=BASE + 64 * MB - 16), da.QKRA_ERR_ALIASING),                  # over cu_seqlens
+])
+def test_gather_last_argument_checks(over, status):
+    assert call_gather(gather_args(**over)) == status
+    assert da.qknorm_rope_attn_last_hip_error() == 0
+
+
+def test_gather_last_empty_batch_is_noop():
+    assert call_gather(gather_args(num_seqs=0, hidden=None, cu_seqlens=None, out=None)) == da.QKRA_OK
+
+
+def argmax_args(**over):
+    a = dict(dtype=da.QKRA_BF16, logits=BASE, num_rows=132, vocab=151936, row_stride=151936,
+             out_index=BASE + 128 * MB, workspace=BASE + 192 * MB, workspace_bytes=1 * MB, stream=0)
+    a.update(over)
+    return a
+
+
+def call_argmax(a):
+    return da.qknorm_rope_attn_argmax(a["dtype"], a["logits"], a["num_rows"], a["vocab"], a["row_stride"],
+                                      a["out_index"], a["workspace"], a["workspace_bytes"], a["stream"])
+
+
+def test_argmax_workspace_bytes():
+    # (value, index) records for each (row, segment): 8 segments of 132 rows of 151936.
+    assert da.qknorm_rope_attn_argmax_workspace_bytes(132, 151936) == 2 * 4352
+    assert da.qknorm_rope_attn_argmax_workspace_bytes(0, 10) == 0
+    assert da.qknorm_rope_attn_argmax_workspace_bytes(4, 0) == 0
+    for rows, vocab in ((1, 1), (1, 151936), (5000, 32000), (132, 2 ** 31 - 1)):
+        assert da.qknorm_rope_attn_argmax_workspace_bytes(rows, vocab) >= rows * 8
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=3), da.QKRA_ERR_UNSUPPORTED),
+    (dict(vocab=0), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(row_stride=151935), da.QKRA_ERR_INVALID_ARGUMENT),               # shorter than a row
+    (dict(row_stride=151940), da.QKRA_ERR_INVALID_ARGUMENT),               # not a multiple of 8
+    (dict(out_index=None), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(workspace_bytes=100), da.QKRA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(logits=BASE + 2), da.QKRA_ERR_INVALID_ARGUMENT),                  # misaligned
+    (dict(out_index=BASE + 1024), da.QKRA_ERR_ALIASING),                    # inside the logits
+    (dict(workspace=BASE + 38 * MB), da.QKRA_ERR_ALIASING),                 # over the logits' end (38.25 MB)
+])
+def test_argmax_argument_checks(over, status):
+    assert call_argmax(argmax_args(**over)) == status
+    assert da.qknorm_rope_attn_last_hip_error() == 0
+
+
+def test_argmax_empty_batch_is_noop():
+    assert call_argmax(argmax_args(num_rows=0, logits=None, out_index=None, workspace=None)) == da.QKRA_OK

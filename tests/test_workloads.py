@@ -56,3 +56,22 @@ def test_append_generator_positions_and_cache():
 def test_chunked_workload_shape():
     from workloads import WORKLOADS
     assert "chunked_qwen3_8b" in WORKLOADS
+
+
+def test_norm_and_next_token_generators():
+    from workloads import make_next_token_inputs, make_norm_inputs
+
+    a = make_norm_inputs(5, 16, seed=3)
+    b = make_norm_inputs(5, 16, seed=3)
+    assert torch.equal(a.x, b.x) and torch.equal(a.residual, b.residual) and torch.equal(a.weight, b.weight)
+    first = make_norm_inputs(5, 16, seed=3, has_residual=False)
+    assert first.residual is None and not first.has_residual and torch.equal(first.x, a.x)
+    nt = make_next_token_inputs([3, 0, 2], 8, 11, seed=4)
+    assert nt.cu_seqlens.tolist() == [0, 3, 3, 5]
+    assert nt.hidden.shape == (5, 8) and nt.logits.shape == (3, 11)
+
+
+def test_layer_step_workloads_present():
+    from workloads import WORKLOADS
+
+    assert {"residual_rmsnorm_qwen3_8b", "next_token_qwen3_8b"} <= set(WORKLOADS)

@@ -11,11 +11,15 @@ from .synth import (  # noqa: F401
     PrefillInputs,
     DecodeInputs,
     AppendInputs,
+    NormInputs,
+    NextTokenInputs,
     WorkloadInputs,
     WORKLOADS,
     build_workload,
     make_prefill_inputs,
     make_decode_inputs,
     make_append_inputs,
+    make_norm_inputs,
+    make_next_token_inputs,
     qkv_width,
 )

@@ -130,6 +130,28 @@ class AppendInputs:
 
 
 @dataclasses.dataclass
+class NormInputs:
+    """Inputs of the fused residual add + RMSNorm over hidden-size rows."""
+    x: torch.Tensor                   # [N, C] sublayer output
+    residual: Optional[torch.Tensor]  # [N, C] residual stream (None: first call of a forward pass)
+    weight: torch.Tensor              # [C]
+    rms_eps: float = 1e-6
+
+    @property
+    def has_residual(self) -> bool:
+        return self.residual is not None
+
+
+@dataclasses.dataclass
+class NextTokenInputs:
+    """Packed hidden states and one logits row per request, for next-token selection."""
+    hidden: torch.Tensor       # [N, C]
+    cu_seqlens: torch.Tensor   # int32 [B+1]
+    seqlens: List[int]
+    logits: torch.Tensor       # [B, V], drawn directly (the LM head is outside the path)
+
+
+@dataclasses.dataclass
 class WorkloadInputs:
     name: str
     description: str
@@ -139,6 +161,8 @@ class WorkloadInputs:
     # [B_prefill, W] tensor per step; step s runs at position T_r + s.
     chained_decode_qkv: List[torch.Tensor] = dataclasses.field(default_factory=list)
     append: Optional[AppendInputs] = None
+    norm: Optional[NormInputs] = None
+    next_token: Optional[NextTokenInputs] = None
 
 
 def _sentinel(parity: bool) -> float:
@@ -344,6 +368,42 @@ def _chunked_qwen3_8b(dtype, device, parity):
                           "Hq=32 Hkv=8 D=128, base 1e6", None, None, append=app)
 
 
+def make_norm_inputs(num_rows: int, hidden: int, seed: int, dtype=torch.bfloat16, device="cpu",
+                     has_residual: bool = True, rms_eps: float = 1e-6) -> NormInputs:
+    """x, then the residual stream (when there is one), N(0,1); then the weight 1 + 0.1 N(0,1)."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((num_rows, hidden), generator=g, dtype=torch.float32).to(dtype)
+    res = torch.randn((num_rows, hidden), generator=g, dtype=torch.float32).to(dtype) if has_residual else None
+    w = (1.0 + 0.1 * torch.randn((hidden,), generator=g, dtype=torch.float32)).to(dtype)
+    return NormInputs(x.to(device), None if res is None else res.to(device), w.to(device), rms_eps)
+
+
+def make_next_token_inputs(seqlens: Sequence[int], hidden: int, vocab: int, seed: int, dtype=torch.bfloat16,
+                           device="cpu") -> NextTokenInputs:
+    """Hidden states N(0,1) for the packed requests, then one logits row per request N(0,1)."""
+    g = torch.Generator().manual_seed(seed)
+    n = int(sum(seqlens))
+    cu = torch.zeros(len(seqlens) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(list(seqlens), dtype=torch.int64), 0).to(torch.int32)
+    h = torch.randn((n, hidden), generator=g, dtype=torch.float32).to(dtype)
+    z = torch.randn((len(seqlens), vocab), generator=g, dtype=torch.float32).to(dtype)
+    return NextTokenInputs(h.to(device), cu.to(device), [int(t) for t in seqlens], z.to(device))
+
+
+def _residual_rmsnorm_qwen3_8b(dtype, device, parity):
+    norm = make_norm_inputs(4 * 4096 + 128, 4096, 1007, dtype, device, has_residual=True)
+    return WorkloadInputs("residual_rmsnorm_qwen3_8b",
+                          "fused residual add + RMSNorm over the mixed step's 16512 token rows, hidden 4096",
+                          None, None, norm=norm)
+
+
+def _next_token_qwen3_8b(dtype, device, parity):
+    nt = make_next_token_inputs([4096] * 4 + [1] * 128, 4096, 151936, 1008, dtype, device)
+    return WorkloadInputs("next_token_qwen3_8b",
+                          "last-row gather over the mixed step's 132 requests (hidden 4096) and greedy argmax "
+                          "over 132 logits rows of 151936", None, None, next_token=nt)
+
+
 WORKLOADS: Dict[str, object] = {
     "pages_t12_decode9": _pages_t12_decode9,
     "single_t64_hq4_hkv2_d64": _single_t64,
@@ -352,6 +412,8 @@ WORKLOADS: Dict[str, object] = {
     "long_prefill_32k": _long_prefill_32k,
     "mixed_qwen3_8b": _mixed_qwen3_8b,
     "chunked_qwen3_8b": _chunked_qwen3_8b,
+    "residual_rmsnorm_qwen3_8b": _residual_rmsnorm_qwen3_8b,
+    "next_token_qwen3_8b": _next_token_qwen3_8b,
 }
 
 
