@@ -40,6 +40,12 @@ template <>
 struct Piece<bf16> {
   u32x4 raw;
   __device__ __forceinline__ void load(const bf16* p) { raw = *reinterpret_cast<const u32x4*>(p); }
+  // Rows read once: non-temporal loads (measured 6.4 TB/s for the norm's two
+  // reads and two writes, against 5.6 with plain loads; non-temporal stores
+  // were slower).
+  __device__ __forceinline__ void load_stream(const bf16* p) {
+    raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
   __device__ __forceinline__ float at(int i) const {
     const uint32_t w = raw[i >> 1];
     return (i & 1) ? bf16_hi_to_f32(w) : bf16_lo_to_f32(w);
@@ -57,6 +63,10 @@ struct Piece<float> {
   __device__ __forceinline__ void load(const float* p) {
     lo = *reinterpret_cast<const f32x4*>(p);
     hi = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void load_stream(const float* p) {
+    lo = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    hi = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
   }
   __device__ __forceinline__ float at(int i) const { return i < 4 ? lo[i] : hi[i - 4]; }
   __device__ __forceinline__ static void store(float* p, const float (&v)[8]) {
@@ -89,10 +99,10 @@ __global__ __launch_bounds__(kNormThreads) void fused_add_rmsnorm_kernel(
     const int c = tid + kNormThreads * i;
     if (c < pieces) {
       Piece<T> px;
-      px.load(x + base + 8 * c);
+      px.load_stream(x + base + 8 * c);
       if (mode == 1) {
         Piece<T> pr;
-        pr.load(residual + base + 8 * c);
+        pr.load_stream(residual + base + 8 * c);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[i][e] = px.at(e) + pr.at(e);
       } else {
@@ -221,18 +231,31 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_partial_kernel(const T*
   const T* row = logits + static_cast<long long>(b) * row_stride;
   Best best{kNegInf, lo < vocab ? lo : 0};
   bool have_nan = false;
-  for (int p = lo + 8 * static_cast<int>(threadIdx.x); p < hi; p += 8 * kArgmaxThreads) {
+  auto take = [&](const Piece<T>& pc, int p) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float z = pc.at(e);
+      if (!have_nan && (z != z || z > best.v)) {
+        best = Best{z, p + e};
+        have_nan = z != z;
+      }
+    }
+  };
+  constexpr int kStride = 8 * kArgmaxThreads;  // elements between a thread's consecutive pieces
+  constexpr int kBatch = 4;                    // pieces loaded before any is compared
+  int p = lo + 8 * static_cast<int>(threadIdx.x);
+  for (; p + (kBatch - 1) * kStride + 8 <= hi; p += kBatch * kStride) {
+    Piece<T> pc[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) pc[u].load(row + p + u * kStride);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) take(pc[u], p + u * kStride);
+  }
+  for (; p < hi; p += kStride) {
     if (p + 8 <= hi) {
       Piece<T> pc;
       pc.load(row + p);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float z = pc.at(e);
-        if (!have_nan && (z != z || z > best.v)) {
-          best = Best{z, p + e};
-          have_nan = z != z;
-        }
-      }
+      take(pc, p);
     } else {
       for (int e = 0; p + e < hi; ++e) {
         const float z = static_cast<float>(row[p + e]);

@@ -40,10 +40,13 @@
 //    slot.  One barrier per step.  The tile loop is unrolled by six so that
 //    every slot index, hence every LDS address offset, is a compile-time
 //    constant.
-//  * Grid: heaviest (latest) query tiles first; block ids are remapped so
-//    that consecutive work items land on the same XCD (the hardware deals
-//    workgroups round-robin over the 8 XCDs), keeping one KV head's tiles in
-//    one L2.
+//  * Grid: work items ordered by (KV-head chunk, request, query tile from the
+//    last), and block ids remapped so that consecutive items land on the same
+//    XCD (the hardware deals workgroups round-robin over the 8 XCDs).  The
+//    CUs of an XCD then work on the tiles of one request and KV head at a
+//    time, whose K/V stays in that XCD's L2 (ordering by tile across requests
+//    instead made a chunked prefill onto long caches fetch its history from
+//    HBM about 25 times); within a request the heaviest tiles go first.
 
 #include "device_common.h"
 #include "launch.h"
@@ -99,15 +102,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   __shared__ __attribute__((aligned(16))) bf16 sK[NSLOT][BN * KST];
   __shared__ __attribute__((aligned(16))) bf16 sV[NSLOT][D * VST];
 
-  // ---- work item (XCD-aware remap, heaviest tiles first) -------------------
+  // ---- work item (XCD-aware remap; per request, heaviest tiles first) -------
   const int nb = gridDim.x;  // a multiple of 8
   const int logical = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
   if (logical >= num_items) return;
   const int per_chunk = tiles_per_seq * num_seqs;
   const int chunk = logical / per_chunk;
   const int rem = logical - chunk * per_chunk;
-  const int tile = tiles_per_seq - 1 - rem / num_seqs;
-  const int seq = rem % num_seqs;
+  const int seq = rem / tiles_per_seq;
+  const int tile = tiles_per_seq - 1 - rem % tiles_per_seq;
   const int cu0 = cu_seqlens[seq];
   // Entries cached before the chunk (its token t sits at slot past + t).
   // Lengths are clamped to the cache so out-of-contract inputs cannot address past it.
