@@ -248,10 +248,13 @@ def cpu_baseline(w, F_total, B_total, budget_s: float = 20.0):
     import oracle
 
     threads = None
+    blas = None
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+        pools = threadpool_info()
+        threads = max((i.get("num_threads") or 0) for i in pools) or None
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in pools if i.get("user_api") == "blas")
     except Exception:  # threadpoolctl missing or no BLAS pools
         threads = None
     cores = threads or len(os.sched_getaffinity(0))
@@ -298,6 +301,7 @@ def cpu_baseline(w, F_total, B_total, budget_s: float = 20.0):
         parts.append(f"decode: 4 median-length requests ({[lens[b] for b in subset]} cached), all heads, {dt:.1f} s")
     value = 100.0 * (F_total / (PEAK_MFMA_TFLOPS * 1e12) + B_total / (PEAK_HBM_GBPS * 1e9)) / t_total
     return {"value": value, "unit": "% of MI355X peak", "cores": cores, "kind": "oracle",
+            "numpy": np.__version__, "blas": blas or None,
             "sample": "; ".join(parts) + f"; scaled linearly to the whole step: {t_total:.1f} s per step",
             "step_seconds_est": t_total}
 
@@ -354,9 +358,24 @@ def main(argv=None):
         side["prefill_kernel"] = roofline_for("prefill_attn_mfma_bf16", kernels, F, B, args.workload)
     if B:
         gbps = B / (dec_ms / args.steps / 1e3) / 1e9
+        d = w.decode
+        h = d.heads
+        e = d.qkv.element_size()
+        # Everything the call must move: K/V read, plus the qkv rows, both norm weights, the new K/V
+        # entries and the output.
+        total = B + d.num_seqs * h.head_dim * e * ((h.num_q_heads + 2 * h.num_kv_heads) + 2 * h.num_kv_heads
+                                                   + h.num_q_heads) + 2 * h.head_dim * e
         side["decode_call"] = {"gbps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS, "ms": dec_ms / args.steps,
-                               "kv_bytes": B}
+                               "kv_bytes": B, "total_algorithmic_bytes": total}
         side["decode_kernel"] = roofline_for("decode_attn_split", kernels, F, B, args.workload)
+
+    if w.prefill is not None and "qknorm_rope_kv_prefill" in kernels:
+        # Kernel 1's own roofline: every qkv element read once and written once (q~, k~, v).
+        p = w.prefill
+        h = p.heads
+        k1 = 2.0 * p.num_tokens * (h.num_q_heads + 2 * h.num_kv_heads) * h.head_dim * p.qkv.element_size()
+        side["kernel1_prefill"] = roofline_for("qknorm_rope_kv_prefill", kernels, F, B, args.workload,
+                                               {"qknorm_rope_kv_prefill": k1})
 
     cpu = None
     if not args.no_cpu_baseline:
