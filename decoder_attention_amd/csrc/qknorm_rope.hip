@@ -16,7 +16,8 @@
 // so every rotate-half pair stays inside one lane and the rotation needs no
 // cross-lane traffic; only the sum of squares is reduced across the D/8 lanes.
 // Loads and stores are 8 B (bf16) or 16 B (fp32) per lane, contiguous across
-// the lanes of a head.
+// the lanes of a head.  A wavefront's first four passes are loaded before the
+// request lookup and the angle computation, so those latencies overlap.
 
 #include "device_common.h"
 #include "launch.h"
@@ -60,6 +61,31 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
   __shared__ float s_sin[HALF];
 
   const int row_id = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int sub = lane % LPH;
+  const int hslot = lane / LPH;
+  const int i0 = sub * 4;
+  const int heads = num_q_heads + 2 * num_kv_heads;
+  const T* row = qkv + static_cast<size_t>(row_id) * heads * D;
+
+  // The row's first PRE passes are loaded before anything else: they depend
+  // only on the row, so their latency overlaps the request lookup, the angle
+  // computation and the barrier.  Rows are read once (non-temporal).
+  constexpr int PRE = 4;
+  Raw pre1[PRE], pre2[PRE];
+#pragma unroll
+  for (int p = 0; p < PRE; ++p) {
+    const int head = (wave + p * nwaves) * HPW + hslot;
+    pre1[p] = Raw{};
+    pre2[p] = Raw{};
+    if (head < heads) {
+      pre1[p] = __builtin_nontemporal_load(reinterpret_cast<const Raw*>(row + head * D + i0));
+      pre2[p] = __builtin_nontemporal_load(reinterpret_cast<const Raw*>(row + head * D + HALF + i0));
+    }
+  }
+
   int req, slot;
   if (decode_mode) {
     req = row_id;
@@ -87,13 +113,6 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
-  const int sub = lane % LPH;
-  const int hslot = lane / LPH;
-  const int i0 = sub * 4;
-
   float cs[4], sn[4], wq1[4], wq2[4], wk1[4], wk2[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -105,15 +124,21 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
   unpack4(*reinterpret_cast<const Raw*>(k_weight + i0), wk1);
   unpack4(*reinterpret_cast<const Raw*>(k_weight + HALF + i0), wk2);
 
-  const int heads = num_q_heads + 2 * num_kv_heads;
-  const T* row = qkv + static_cast<size_t>(row_id) * heads * D;
-  for (int hb = wave * HPW; hb < heads; hb += nwaves * HPW) {
+  int pass = 0;
+  for (int hb = wave * HPW; hb < heads; hb += nwaves * HPW, ++pass) {
     const int head = hb + hslot;
     const bool active = head < heads;
     Raw r1 = {}, r2 = {};
-    if (active) {
-      r1 = *reinterpret_cast<const Raw*>(row + head * D + i0);
-      r2 = *reinterpret_cast<const Raw*>(row + head * D + HALF + i0);
+    if (pass < PRE) {
+#pragma unroll
+      for (int p = 0; p < PRE; ++p)
+        if (p == pass) {
+          r1 = pre1[p];
+          r2 = pre2[p];
+        }
+    } else if (active) {
+      r1 = __builtin_nontemporal_load(reinterpret_cast<const Raw*>(row + head * D + i0));
+      r2 = __builtin_nontemporal_load(reinterpret_cast<const Raw*>(row + head * D + HALF + i0));
     }
     float x1[4], x2[4];
     unpack4(r1, x1);
