@@ -91,33 +91,28 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
     __syncthreads();
   }
   int32_t* S0 = plan + 2;
-  int run = s_scan[tid] - local;
-  for (int i = i0; i < i1; ++i) {
-    S0[i] = run;
-    run += unit_steps(cache_lens, i, nchunks, cache_capacity);
-  }
+  int32_t* first = plan + 3 + num_units;
   const int total = s_scan[kPlanThreads - 1];
   const int per = max((total + num_waves - 1) / num_waves, min_steps);
+  // Each thread records the first steps of its units and, for every unit, the
+  // wavefronts whose first step w*per falls inside it: w in
+  // [ceil(S0_i / per), ceil((S0_i + steps_i) / per)).  No search, no barrier.
+  int run = s_scan[tid] - local;
+  for (int i = i0; i < i1; ++i) {
+    const int steps = unit_steps(cache_lens, i, nchunks, cache_capacity);
+    S0[i] = run;
+    const long long wlo = (static_cast<long long>(run) + per - 1) / per;
+    const long long whi = min((static_cast<long long>(run) + steps + per - 1) / per, static_cast<long long>(num_waves));
+    for (long long w = wlo; w < whi; ++w) first[w] = i;
+    run += steps;
+  }
   if (tid == 0) {
     plan[0] = total;
     plan[1] = per;
     S0[num_units] = total;
   }
-  __syncthreads();  // S0 complete and visible to the workgroup
-  int32_t* first = plan + 3 + num_units;
-  for (int w = tid; w < num_waves; w += kPlanThreads) {
-    const long long t0 = static_cast<long long>(w) * per;
-    int unit = -1;
-    if (t0 < total) {  // last unit whose first step is <= t0
-      int lo = 0, hi = num_units;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (S0[mid] <= t0) lo = mid; else hi = mid;
-      }
-      unit = lo;
-    }
-    first[w] = unit;
-  }
+  for (int w = tid; w < num_waves; w += kPlanThreads)  // wavefronts past the last step stay idle
+    if (static_cast<long long>(w) * per >= total) first[w] = -1;
 }
 
 // ---- 3a: one wavefront per range of steps; 4 independent wavefronts per workgroup.
