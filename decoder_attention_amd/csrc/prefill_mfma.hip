@@ -400,22 +400,40 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     step(std::integral_constant<int, 5>{}, kt + 5, sB, sA);
   }
 
-  // ---- normalise and store: lane holds query l32, d = 32*db + 8*(j/4) + 4*hi + j%4
+  // ---- normalise and store.  A lane holds query l32 and d = 32db + 8(j/4) +
+  // 4hi + j%4, so storing from registers would write 16 bytes into each of 32
+  // output rows per instruction.  Instead each wavefront writes its 32 x D
+  // tile row-major into its own LDS region (the K/V slots are free: the last
+  // step ended with a barrier) and stores whole rows from there, 16 lanes
+  // per row, 16 bytes each.
+  constexpr int EST = D + 8;  // LDS row stride of the tile (elements)
+  static_assert(NWAVES / 2 * 32 * EST <= NSLOT * BN * KST && NWAVES / 2 * 32 * EST <= NSLOT * D * VST,
+                "the output tiles fit in the K and V slots");
+  bf16* stile = (wave < NWAVES / 2 ? &sK[0][0] : &sV[0][0]) + (wave % (NWAVES / 2)) * 32 * EST;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + xor_shuffle(l_run[qb], 32);
     const float inv = 1.0f / l_tot;
-    if (qtok[qb] < seqlen) {
-      bf16* dst = out + (static_cast<size_t>(cu0 + qtok[qb]) * num_q_heads + qhead[qb]) * D + 4 * hi;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int jq = 0; jq < 4; ++jq) {
-          const f32x16& a = acc[qb][db];
-          const u32x2 w = {pack_bf16x2(a[4 * jq] * inv, a[4 * jq + 1] * inv),
-                           pack_bf16x2(a[4 * jq + 2] * inv, a[4 * jq + 3] * inv)};
-          *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * jq) = w;
-        }
+      for (int jq = 0; jq < 4; ++jq) {
+        const f32x16& a = acc[qb][db];
+        const u32x2 w = {pack_bf16x2(a[4 * jq] * inv, a[4 * jq + 1] * inv),
+                         pack_bf16x2(a[4 * jq + 2] * inv, a[4 * jq + 3] * inv)};
+        *reinterpret_cast<u32x2*>(&stile[l32 * EST + 32 * db + 8 * jq + 4 * hi]) = w;
+      }
+    // Lane L then stores bytes 16(L%16) .. +15 of row L/16 + 4p, p = 0 .. 7.
+    constexpr int LPR = D / 8;        // lanes per row
+    constexpr int RPI = 64 / LPR;     // rows per store instruction
+    const int r0 = lane / LPR, c = lane % LPR;
+#pragma unroll
+    for (int p = 0; p < 32 / RPI; ++p) {
+      const int r = r0 + RPI * p;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&stile[r * EST + 8 * c]);
+      const int tok = qfirst[qb] + r;
+      if (tok < seqlen)
+        *reinterpret_cast<u32x4*>(out + (static_cast<size_t>(cu0 + tok) * num_q_heads + qhead[qb]) * D + 8 * c) = v;
     }
   }
 }
