@@ -39,7 +39,10 @@ int32_t check_config(const qkra_config* cfg) {
   return QKRA_OK;
 }
 
+// bf16: the per-token RoPE table [N][cos D/2, sin D/2] (fp32), from which the
+// attention kernel rotates Q itself; fp32: q~ [N, Hq, D].
 size_t prefill_workspace(const qkra_config* cfg, int64_t num_tokens) {
+  if (cfg->dtype == QKRA_BF16) return align_up(static_cast<size_t>(num_tokens) * cfg->head_dim * sizeof(float));
   return align_up(static_cast<size_t>(num_tokens) * cfg->num_q_heads * cfg->head_dim * elem_size(cfg->dtype));
 }
 
@@ -236,7 +239,9 @@ int32_t prefill_impl(const qkra_config* cfg, const void* qkv, const void* q_norm
   ka.cache_capacity = cache_capacity;
   ka.rms_eps = cfg->rms_eps;
   ka.log2_rope_base = log2_of(cfg->rope_base);
-  ka.q_out = workspace;
+  const bool fused_q = cfg->dtype == QKRA_BF16;
+  ka.q_out = fused_q ? nullptr : workspace;
+  ka.rope_table = fused_q ? static_cast<float*>(workspace) : nullptr;
   ka.k_cache = k_cache;
   ka.v_cache = v_cache;
   hipError_t err = timed(kKernelQkNormRopePrefill, stream, [&] { return launch_qknorm_rope(ka, stream); });
@@ -244,6 +249,10 @@ int32_t prefill_impl(const qkra_config* cfg, const void* qkv, const void* q_norm
 
   PrefillAttnArgs pa{};
   pa.q = workspace;
+  pa.qkv = qkv;
+  pa.q_norm_weight = q_norm_weight;
+  pa.rope_table = static_cast<const float*>(workspace);
+  pa.rms_eps = cfg->rms_eps;
   pa.k_cache = k_cache;
   pa.v_cache = v_cache;
   pa.cu_seqlens = cu_seqlens;

@@ -38,7 +38,8 @@ struct QkNormRopeArgs {
   int num_q_heads, num_kv_heads, head_dim, dtype, cache_capacity;
   float rms_eps;
   double log2_rope_base;
-  void* q_out;
+  void* q_out;              // q~ [rows, Hq, D], or null when rope_table is set
+  float* rope_table;        // prefill, bf16: per row cos[D/2] then sin[D/2] (fp32); Q heads skipped
   void* k_cache;
   void* v_cache;
 };
@@ -47,7 +48,12 @@ hipError_t launch_qknorm_rope(const QkNormRopeArgs& a, hipStream_t stream);
 // Kernel 2: causal GQA attention over the prefill caches.  Request r's new token j
 // sits at slot P_r + j and sees slots 0..P_r + j (P_r = past_lens[r], or 0).
 struct PrefillAttnArgs {
-  const void* q;            // q~ [N, Hq, D]
+  const void* q;            // q~ [N, Hq, D] (fp32 path)
+  // bf16 path: Q comes raw from qkv and is normalised and rotated on load.
+  const void* qkv;          // [N, (Hq + 2Hkv) D]
+  const void* q_norm_weight;
+  const float* rope_table;  // [N][cos D/2, sin D/2]
+  float rms_eps;
   const void* k_cache;      // [B, Hkv, S, D]
   const void* v_cache;
   const int32_t* cu_seqlens;

@@ -81,11 +81,12 @@ __device__ __forceinline__ float half_wave_max(float x) {
 
 template <int D, int HC>
 __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k_cache, const bf16* __restrict__ v_cache,
+    const bf16* __restrict__ qkv, const bf16* __restrict__ q_norm_weight, const float* __restrict__ rope_table,
+    const bf16* __restrict__ k_cache, const bf16* __restrict__ v_cache,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ past_lens, bf16* __restrict__ out,
     int num_q_heads, int num_kv_heads,
     int cache_capacity, int num_seqs, int tiles_per_seq, int chunks_per_kv, int num_items,
-    float scale_log2) {
+    float rms_eps, float scale_log2) {
   constexpr int TBN = 8 / HC;       // token blocks (of 32) per workgroup
   constexpr int TM = 32 * TBN;      // tokens per workgroup
   constexpr int DS = D / 16;        // k-steps over D for the scores
@@ -138,18 +139,70 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   }
 
   // Q^T fragments (B operand): lane holds query l32, d = 16*ds + 8*hi .. +7.
+  // Q comes raw from qkv and is RMS-normalised with w_q and rotated with the
+  // row's cos/sin pairs (kernel 1 forms them in fp64) while loading, as
+  // kernel 1 does for K: a lane's fragments ds and ds + DS/2 hold the
+  // rotate-half partners d and d + D/2, and lanes l32 and l32 + 32 share the
+  // row's sum of squares.  Rows past the request's end are zero.
   bf16x8 qf[QB][DS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const bool valid = qtok[qb] < seqlen;
-    const bf16* src = q + (static_cast<size_t>(cu0 + (valid ? qtok[qb] : 0)) * num_q_heads + qhead[qb]) * D + 8 * hi;
+  auto load_q = [&]() {
+    const int qkv_width = (num_q_heads + 2 * num_kv_heads) * D;
+    float wq[DS][8];
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(src + 16 * ds);
-      if (!valid) v = bf16x8{};
-      qf[qb][ds] = v;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(q_norm_weight + 16 * ds + 8 * hi);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wq[ds][e] = (e & 1) ? bf16_hi_to_f32(w[e >> 1]) : bf16_lo_to_f32(w[e >> 1]);
     }
-  }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const bool valid = qtok[qb] < seqlen;
+      const int tok = cu0 + (valid ? qtok[qb] : 0);
+      const bf16* src = qkv + static_cast<size_t>(tok) * qkv_width + qhead[qb] * D + 8 * hi;
+      const float* tab = rope_table + static_cast<size_t>(tok) * D + 8 * hi;
+      u32x4 raw[DS];
+      f32x4 cs[DS / 2][2], sn[DS / 2][2];
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) raw[ds] = *reinterpret_cast<const u32x4*>(src + 16 * ds);
+#pragma unroll
+      for (int ds = 0; ds < DS / 2; ++ds) {
+        cs[ds][0] = *reinterpret_cast<const f32x4*>(tab + 16 * ds);
+        cs[ds][1] = *reinterpret_cast<const f32x4*>(tab + 16 * ds + 4);
+        sn[ds][0] = *reinterpret_cast<const f32x4*>(tab + D / 2 + 16 * ds);
+        sn[ds][1] = *reinterpret_cast<const f32x4*>(tab + D / 2 + 16 * ds + 4);
+      }
+      float x[DS][8];
+      float ss = 0.f;
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[ds][e] = (e & 1) ? bf16_hi_to_f32(raw[ds][e >> 1]) : bf16_lo_to_f32(raw[ds][e >> 1]);
+          ss += x[ds][e] * x[ds][e];
+        }
+      ss += xor_shuffle(ss, 32);
+      const float inv_rms = rsqrtf(ss * (1.0f / D) + rms_eps);
+#pragma unroll
+      for (int ds = 0; ds < DS / 2; ++ds) {
+        float y1[8], y2[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float c = cs[ds][e >> 2][e & 3], sv = sn[ds][e >> 2][e & 3];
+          const float a = x[ds][e] * inv_rms * wq[ds][e];
+          const float b = x[ds + DS / 2][e] * inv_rms * wq[ds + DS / 2][e];
+          y1[e] = a * c - b * sv;
+          y2[e] = b * c + a * sv;
+        }
+        u32x4 w1 = {pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3]), pack_bf16x2(y1[4], y1[5]),
+                    pack_bf16x2(y1[6], y1[7])};
+        u32x4 w2 = {pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3]), pack_bf16x2(y2[4], y2[5]),
+                    pack_bf16x2(y2[6], y2[7])};
+        if (!valid) w1 = w2 = u32x4{};
+        qf[qb][ds] = __builtin_bit_cast(bf16x8, w1);
+        qf[qb][ds + DS / 2] = __builtin_bit_cast(bf16x8, w2);
+      }
+    }
+  };
 
   f32x16 acc[QB][DB];
 #pragma unroll
@@ -369,7 +422,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
 
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
+  // Tile 0's loads go out first; Q is loaded, normalised and rotated while
+  // they are in flight.
   load_tile(0);
+  load_q();
   store_tile(C0{});
   if (ntiles > 1) {
     load_tile(1);
@@ -449,10 +505,11 @@ hipError_t launch_typed(const PrefillAttnArgs& a, hipStream_t stream) {
   const long long grid = (items + 7) / 8 * 8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((prefill_mfma_kernel<D, HC>), dim3(static_cast<unsigned>(grid)), dim3(NTHREADS), 0, stream,
-                     static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k_cache),
+                     static_cast<const bf16*>(a.qkv), static_cast<const bf16*>(a.q_norm_weight), a.rope_table,
+                     static_cast<const bf16*>(a.k_cache),
                      static_cast<const bf16*>(a.v_cache), a.cu_seqlens, a.past_lens, static_cast<bf16*>(a.out),
                      a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.num_seqs, tiles, chunks_per_kv,
-                     static_cast<int>(items), a.scale_log2);
+                     static_cast<int>(items), a.rms_eps, a.scale_log2);
   return hipGetLastError();
 }
 

@@ -8,6 +8,10 @@
 // every prompt token's K and V) and jq-wei "transformer basics", "Prefill vs
 // Decode" (a decode step appends one entry).
 //
+// With a rope table (bf16 prefill), the kernel writes the row's fp32 cos/sin
+// pairs there instead of q~ and skips the Q heads: the attention kernel
+// normalises and rotates Q itself while loading it.
+//
 // Layout of the work: one workgroup per token row.  The D/2 rotation angles
 // of the row are formed once in fp64 (position * base^(-2i/D), then sin/cos)
 // and kept in LDS, so positions up to tens of thousands keep full fp32
@@ -52,7 +56,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
     const int32_t* __restrict__ positions, const int32_t* __restrict__ seq_info,
     const int32_t* __restrict__ slot_offsets, int decode_mode,
     int num_seqs, int num_q_heads, int num_kv_heads, int cache_capacity, float eps,
-    double log2_base, T* __restrict__ q_out, T* __restrict__ k_cache, T* __restrict__ v_cache) {
+    double log2_base, T* __restrict__ q_out, float* __restrict__ rope_table, T* __restrict__ k_cache,
+    T* __restrict__ v_cache) {
   using Raw = typename Raw4<T>::type;
   constexpr int HALF = D / 2;
   constexpr int LPH = HALF / 4;  // lanes per head row
@@ -69,6 +74,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
   const int i0 = sub * 4;
   const int heads = num_q_heads + 2 * num_kv_heads;
   const T* row = qkv + static_cast<size_t>(row_id) * heads * D;
+  // With a rope table the attention kernel rotates Q itself: only K and V heads here.
+  const int head0 = rope_table ? num_q_heads : 0;
 
   // The row's first PRE passes are loaded before anything else: they depend
   // only on the row, so their latency overlaps the request lookup, the angle
@@ -77,7 +84,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
   Raw pre1[PRE], pre2[PRE];
 #pragma unroll
   for (int p = 0; p < PRE; ++p) {
-    const int head = (wave + p * nwaves) * HPW + hslot;
+    const int head = head0 + (wave + p * nwaves) * HPW + hslot;
     pre1[p] = Raw{};
     pre2[p] = Raw{};
     if (head < heads) {
@@ -110,6 +117,10 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
     sincos(pos * theta, &sn, &cs);
     s_cos[i] = static_cast<float>(cs);
     s_sin[i] = static_cast<float>(sn);
+    if (rope_table) {  // [row][cos 0..D/2-1, sin 0..D/2-1], fp32
+      rope_table[static_cast<size_t>(row_id) * D + i] = static_cast<float>(cs);
+      rope_table[static_cast<size_t>(row_id) * D + HALF + i] = static_cast<float>(sn);
+    }
   }
   __syncthreads();
 
@@ -125,7 +136,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
   unpack4(*reinterpret_cast<const Raw*>(k_weight + HALF + i0), wk2);
 
   int pass = 0;
-  for (int hb = wave * HPW; hb < heads; hb += nwaves * HPW, ++pass) {
+  for (int hb = head0 + wave * HPW; hb < heads; hb += nwaves * HPW, ++pass) {
     const int head = hb + hslot;
     const bool active = head < heads;
     Raw r1 = {}, r2 = {};
@@ -187,7 +198,7 @@ hipError_t launch_typed(const QkNormRopeArgs& a, hipStream_t stream) {
                      static_cast<const T*>(a.k_norm_weight), a.positions, a.seq_info, a.slot_offsets,
                      a.decode_mode,
                      a.num_seqs, a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.rms_eps,
-                     a.log2_rope_base, static_cast<T*>(a.q_out), static_cast<T*>(a.k_cache),
+                     a.log2_rope_base, static_cast<T*>(a.q_out), a.rope_table, static_cast<T*>(a.k_cache),
                      static_cast<T*>(a.v_cache));
   return hipGetLastError();
 }

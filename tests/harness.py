@@ -46,6 +46,8 @@ def run_prefill(p) -> Dict[str, torch.Tensor]:
                          p.max_seqlen, p.k_cache, p.v_cache)
     torch.cuda.synchronize()
     n, h = p.num_tokens, p.heads
+    if p.qkv.dtype != torch.float32:  # bf16: Q is normalised and rotated inside the attention kernel
+        return {"out": out, "q_tilde": None}
     q_tilde = ws[: n * h.num_q_heads * h.head_dim * p.qkv.element_size()].view(p.qkv.dtype)
     return {"out": out, "q_tilde": q_tilde.view(n, h.num_q_heads, h.head_dim)}
 

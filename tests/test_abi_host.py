@@ -44,10 +44,13 @@ def test_status_strings_and_version():
 
 def test_workspace_bytes():
     cfg = da.make_config(32, 8, 128, da.QKRA_BF16)
-    # prefill: q~ [N, Hq, D] bf16, rounded up to 256 bytes
-    assert da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_PREFILL, 100, 100) == 100 * 32 * 128 * 2
-    assert da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_PREFILL, 1, 1) == 8192
     up = lambda n: -(-n // 256) * 256
+    # bf16 prefill: the per-token RoPE table [N][cos D/2, sin D/2] fp32, rounded up to 256 bytes
+    assert da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_PREFILL, 100, 100) == up(100 * 128 * 4)
+    assert da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_PREFILL, 1, 1) == 512
+    # fp32 prefill: q~ [N, Hq, D] fp32
+    assert da.qknorm_rope_attn_workspace_bytes(da.make_config(32, 8, 128, da.QKRA_FP32), da.QKRA_MODE_PREFILL,
+                                               100, 100) == 100 * 32 * 128 * 4
     # bf16 decode: q~, then the int32 step plan [T, per, S0[0..N], first[0..W)]
     # over N = b * Hkv units (G = 4 heads per tile), then fp32 records
     # (m, l, pad, pad, o[D]) for N + W (unit, wavefront) slots of 4 heads.
@@ -106,7 +109,7 @@ def call_prefill(cfg, a):
     (dict(cache_capacity=63), da.QKRA_ERR_CAPACITY),
     (dict(qkv=None), da.QKRA_ERR_INVALID_ARGUMENT),
     (dict(cu_seqlens=None), da.QKRA_ERR_INVALID_ARGUMENT),
-    (dict(workspace_bytes=64 * 4 * 64 * 2 - 1), da.QKRA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(workspace_bytes=64 * 64 * 4 - 1), da.QKRA_ERR_WORKSPACE_TOO_SMALL),    # bf16: RoPE table [N, D] fp32
     (dict(workspace=None), da.QKRA_ERR_INVALID_ARGUMENT),
     (dict(out=BASE + 8), da.QKRA_ERR_INVALID_ARGUMENT),                          # misaligned
     (dict(out=BASE), da.QKRA_ERR_ALIASING),                                      # out over qkv
