@@ -370,10 +370,16 @@ def main(argv=None):
         side["decode_kernel"] = roofline_for("decode_attn_split", kernels, F, B, args.workload)
 
     if w.prefill is not None and "qknorm_rope_kv_prefill" in kernels:
-        # Kernel 1's own roofline: every qkv element read once and written once (q~, k~, v).
+        # Kernel 1's own roofline.  bf16: the K and V columns read once and written once to the cache,
+        # plus each token's fp32 cos/sin pairs (Q is rotated inside the attention kernel); fp32: every
+        # qkv element read once and written once (q~, k~, v).
         p = w.prefill
         h = p.heads
-        k1 = 2.0 * p.num_tokens * (h.num_q_heads + 2 * h.num_kv_heads) * h.head_dim * p.qkv.element_size()
+        e = p.qkv.element_size()
+        if e == 2:
+            k1 = 2.0 * p.num_tokens * 2 * h.num_kv_heads * h.head_dim * e + p.num_tokens * h.head_dim * 4.0
+        else:
+            k1 = 2.0 * p.num_tokens * (h.num_q_heads + 2 * h.num_kv_heads) * h.head_dim * e
         side["kernel1_prefill"] = roofline_for("qknorm_rope_kv_prefill", kernels, F, B, args.workload,
                                                {"qknorm_rope_kv_prefill": k1})
 
