@@ -140,56 +140,77 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
 
   // Q^T fragments (B operand): lane holds query l32, d = 16*ds + 8*hi .. +7.
   // Q comes raw from qkv and is RMS-normalised with w_q and rotated with the
-  // row's cos/sin pairs (kernel 1 forms them in fp64) while loading, as
-  // kernel 1 does for K: a lane's fragments ds and ds + DS/2 hold the
-  // rotate-half partners d and d + D/2, and lanes l32 and l32 + 32 share the
-  // row's sum of squares.  Rows past the request's end are zero.
+  // row's cos/sin pairs (kernel 1 forms them in fp64) in a row-coalesced
+  // layout: QLPR lanes per row, lane j holding d = 8j .. 8j+7 and its
+  // rotate-half partners D/2 + 8j .. +7, so every 16-byte load instruction
+  // reads whole 128-byte lines (a lane-per-row load touches 32 lines per
+  // instruction and made the prologue twice as long).  The row's sum of
+  // squares is reduced over its QLPR lanes.  Each wavefront then passes its
+  // 32 x D tile through its own LDS region (in slots 1 and 2, free until the
+  // second tile is stored) into the fragment layout.  Rows past the
+  // request's end are zero.
+  constexpr int QLPR = D / 16;       // lanes per row
+  constexpr int QRPI = 64 / QLPR;    // rows per load instruction
+  constexpr int QNG = 32 / QRPI;     // load groups per 32-row block
+  constexpr int EST = D + 8;         // LDS row stride of a staged 32 x D tile (elements)
+  static_assert(NWAVES / 2 * 32 * EST <= (NSLOT - 1) * BN * KST &&
+                    NWAVES / 2 * 32 * EST <= (NSLOT - 1) * D * VST,
+                "the staged Q tiles fit in LDS slots 1 and 2");
+  const int qj = lane % QLPR;
+  const int qr = lane / QLPR;
   bf16x8 qf[QB][DS];
-  auto load_q = [&]() {
+  u32x4 qraw[QB][QNG][2];
+  f32x4 qtab[QB][QNG][4];
+  bool qvalid[QB][QNG];
+  // Issue every Q, table and weight load; nothing waits for them here.
+  auto q_issue = [&]() {
     const int qkv_width = (num_q_heads + 2 * num_kv_heads) * D;
-    float wq[DS][8];
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(q_norm_weight + 16 * ds + 8 * hi);
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) wq[ds][e] = (e & 1) ? bf16_hi_to_f32(w[e >> 1]) : bf16_lo_to_f32(w[e >> 1]);
-    }
+      for (int gi = 0; gi < QNG; ++gi) {
+        const int t = qfirst[qb] + QRPI * gi + qr;
+        qvalid[qb][gi] = t < seqlen;
+        const int tok = cu0 + (qvalid[qb][gi] ? t : 0);
+        const bf16* src = qkv + static_cast<size_t>(tok) * qkv_width + qhead[qb] * D + 8 * qj;
+        qraw[qb][gi][0] = *reinterpret_cast<const u32x4*>(src);
+        qraw[qb][gi][1] = *reinterpret_cast<const u32x4*>(src + D / 2);
+        // Table row: four runs of D/4 floats (cos of pair indices 8j..8j+3,
+        // cos 8j+4..8j+7, sin 8j..8j+3, sin 8j+4..8j+7), lane j's 4 floats at 4j.
+        const float* tab = rope_table + static_cast<size_t>(tok) * D + 4 * qj;
+#pragma unroll
+        for (int pc = 0; pc < 4; ++pc) qtab[qb][gi][pc] = *reinterpret_cast<const f32x4*>(tab + pc * (D / 4));
+      }
+  };
+  // Normalise, rotate, stage and read back as fragments.
+  auto q_finish = [&]() {
+    const u32x4 wlo = *reinterpret_cast<const u32x4*>(q_norm_weight + 8 * qj);
+    const u32x4 whi = *reinterpret_cast<const u32x4*>(q_norm_weight + D / 2 + 8 * qj);
+    bf16* stage = (wave < NWAVES / 2 ? &sK[1][0] : &sV[1][0]) + (wave % (NWAVES / 2)) * 32 * EST;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const bool valid = qtok[qb] < seqlen;
-      const int tok = cu0 + (valid ? qtok[qb] : 0);
-      const bf16* src = qkv + static_cast<size_t>(tok) * qkv_width + qhead[qb] * D + 8 * hi;
-      const float* tab = rope_table + static_cast<size_t>(tok) * D + 8 * hi;
-      u32x4 raw[DS];
-      f32x4 cs[DS / 2][2], sn[DS / 2][2];
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) raw[ds] = *reinterpret_cast<const u32x4*>(src + 16 * ds);
-#pragma unroll
-      for (int ds = 0; ds < DS / 2; ++ds) {
-        cs[ds][0] = *reinterpret_cast<const f32x4*>(tab + 16 * ds);
-        cs[ds][1] = *reinterpret_cast<const f32x4*>(tab + 16 * ds + 4);
-        sn[ds][0] = *reinterpret_cast<const f32x4*>(tab + D / 2 + 16 * ds);
-        sn[ds][1] = *reinterpret_cast<const f32x4*>(tab + D / 2 + 16 * ds + 4);
-      }
-      float x[DS][8];
-      float ss = 0.f;
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
+      for (int gi = 0; gi < QNG; ++gi) {
+        float xl[8], xh[8];
+        float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          x[ds][e] = (e & 1) ? bf16_hi_to_f32(raw[ds][e >> 1]) : bf16_lo_to_f32(raw[ds][e >> 1]);
-          ss += x[ds][e] * x[ds][e];
+          const uint32_t wl = qraw[qb][gi][0][e >> 1], wh = qraw[qb][gi][1][e >> 1];
+          xl[e] = (e & 1) ? bf16_hi_to_f32(wl) : bf16_lo_to_f32(wl);
+          xh[e] = (e & 1) ? bf16_hi_to_f32(wh) : bf16_lo_to_f32(wh);
+          ss += xl[e] * xl[e] + xh[e] * xh[e];
         }
-      ss += xor_shuffle(ss, 32);
-      const float inv_rms = rsqrtf(ss * (1.0f / D) + rms_eps);
 #pragma unroll
-      for (int ds = 0; ds < DS / 2; ++ds) {
+        for (int m = 1; m < QLPR; m <<= 1) ss += xor_shuffle(ss, m);
+        const float inv_rms = rsqrtf(ss * (1.0f / D) + rms_eps);
         float y1[8], y2[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float c = cs[ds][e >> 2][e & 3], sv = sn[ds][e >> 2][e & 3];
-          const float a = x[ds][e] * inv_rms * wq[ds][e];
-          const float b = x[ds + DS / 2][e] * inv_rms * wq[ds + DS / 2][e];
+          const float c = qtab[qb][gi][e >> 2][e & 3], sv = qtab[qb][gi][2 + (e >> 2)][e & 3];
+          const float wl = (e & 1) ? bf16_hi_to_f32(wlo[e >> 1]) : bf16_lo_to_f32(wlo[e >> 1]);
+          const float wh = (e & 1) ? bf16_hi_to_f32(whi[e >> 1]) : bf16_lo_to_f32(whi[e >> 1]);
+          const float a = xl[e] * inv_rms * wl;
+          const float b = xh[e] * inv_rms * wh;
           y1[e] = a * c - b * sv;
           y2[e] = b * c + a * sv;
         }
@@ -197,10 +218,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
                     pack_bf16x2(y1[6], y1[7])};
         u32x4 w2 = {pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3]), pack_bf16x2(y2[4], y2[5]),
                     pack_bf16x2(y2[6], y2[7])};
-        if (!valid) w1 = w2 = u32x4{};
-        qf[qb][ds] = __builtin_bit_cast(bf16x8, w1);
-        qf[qb][ds + DS / 2] = __builtin_bit_cast(bf16x8, w2);
+        if (!qvalid[qb][gi]) w1 = w2 = u32x4{};
+        const int r = QRPI * gi + qr;
+        *reinterpret_cast<u32x4*>(&stage[r * EST + 8 * qj]) = w1;
+        *reinterpret_cast<u32x4*>(&stage[r * EST + D / 2 + 8 * qj]) = w2;
       }
+      // A wavefront's LDS accesses complete in order, so its lanes read what
+      // the others wrote without a barrier (and the next block's writes come
+      // after these reads).
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) qf[qb][ds] = *reinterpret_cast<const bf16x8*>(&stage[l32 * EST + 16 * ds + 8 * hi]);
     }
   };
 
@@ -422,15 +449,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
 
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
-  // Tile 0's loads go out first; Q is loaded, normalised and rotated while
-  // they are in flight.
+  // Tile 0's loads go out first, then Q's.  Tile 0 is stored as soon as it
+  // lands (Q is still in flight), tile 1's loads go out, and Q is finished
+  // meanwhile; tile 1 enters slot 1 once every wavefront has read its Q
+  // fragments from there.
   load_tile(0);
-  load_q();
+  q_issue();
   store_tile(C0{});
-  if (ntiles > 1) {
-    load_tile(1);
-    store_tile(C1{});
-  }
+  if (ntiles > 1) load_tile(1);
+  q_finish();
+  __syncthreads();
+  if (ntiles > 1) store_tile(C1{});
   __syncthreads();
   f32x16 sA[QB][KB], sB[QB][KB];
   {
@@ -462,7 +491,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   // tile row-major into its own LDS region (the K/V slots are free: the last
   // step ended with a barrier) and stores whole rows from there, 16 lanes
   // per row, 16 bytes each.
-  constexpr int EST = D + 8;  // LDS row stride of the tile (elements)
   static_assert(NWAVES / 2 * 32 * EST <= NSLOT * BN * KST && NWAVES / 2 * 32 * EST <= NSLOT * D * VST,
                 "the output tiles fit in the K and V slots");
   bf16* stile = (wave < NWAVES / 2 ? &sK[0][0] : &sV[0][0]) + (wave % (NWAVES / 2)) * 32 * EST;

@@ -117,9 +117,15 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
     sincos(pos * theta, &sn, &cs);
     s_cos[i] = static_cast<float>(cs);
     s_sin[i] = static_cast<float>(sn);
-    if (rope_table) {  // [row][cos 0..D/2-1, sin 0..D/2-1], fp32
-      rope_table[static_cast<size_t>(row_id) * D + i] = static_cast<float>(cs);
-      rope_table[static_cast<size_t>(row_id) * D + HALF + i] = static_cast<float>(sn);
+    if (rope_table) {
+      // fp32, D per row: cos in the first half, sin in the second, each half
+      // as two runs of D/4 (pair indices i with i%8 < 4, then i%8 >= 4), i at
+      // 4*(i/8) + i%4 within its run.  A reader holding pairs 8j..8j+7 finds
+      // each four of them as one 16-byte piece, and D/16 such readers cover
+      // a run with one contiguous line.
+      const size_t at = static_cast<size_t>(row_id) * D + (D / 4) * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+      rope_table[at] = static_cast<float>(cs);
+      rope_table[at + HALF] = static_cast<float>(sn);
     }
   }
   __syncthreads();

@@ -107,8 +107,10 @@ typedef struct qkra_config {
  *                  num_tokens, max_seqlen) bytes.  On return (after the stream
  *                  work completes) it holds, for fp32, q~ as [num_tokens, Hq,
  *                  D]; for bf16, each token's RoPE pairs as fp32 [num_tokens]
- *                  [cos D/2, sin D/2] (the attention kernel normalises and
- *                  rotates Q as it loads it, so q~ is never stored).
+ *                  [D]: cos in the first half, sin in the second, pair i of
+ *                  each half at (D/4)*((i/4)%2) + 4*(i/8) + i%4 (the attention
+ *                  kernel normalises and rotates Q as it loads it, so q~ is
+ *                  never stored).
  * num_tokens == 0 is a no-op returning QKRA_OK.
  */
 QKRA_API int32_t qknorm_rope_attn_prefill(const qkra_config* cfg, const void* qkv,

@@ -6,6 +6,8 @@ import numpy as np
 import pytest
 import torch
 
+import decoder_attention_amd as da
+import harness
 import oracle
 from harness import (BF16_TOL, FP32_TOL, assert_close, bits, check_prefill_caches, f64, layer_kw, note,
                      oracle_prefill, run_prefill, sample_tokens, tol_for)
@@ -63,6 +65,30 @@ def test_single_token_returns_v_exactly(dtype):
     out = got["out"].reshape(3, 32, 128)
     for hh in range(32):
         assert torch.equal(bits(out[:, hh].contiguous()), bits(v[:, hh // 4].contiguous()))
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_bf16_workspace_holds_the_rope_table(d):
+    # The documented bf16 workspace: fp32 [N][D], cos then sin, pair i of each
+    # half at (D/4)*((i/4)%2) + 4*(i/8) + i%4; values are the fp64 cos/sin of
+    # p * theta_i rounded to fp32 (within one fp32 ulp of the oracle's angle).
+    h = HeadConfig(16, 8, d, 1e-6, 1e6)
+    lens = [1, 31, 0, 65, 130]
+    p = make_prefill_inputs(h, lens, seed=21, device=DEV, capacity=max(lens))
+    cfg = harness.cfg_of(h, torch.bfloat16)
+    _, ws = da.prefill(cfg, p.qkv, p.q_norm_weight, p.k_norm_weight, p.positions, p.cu_seqlens, p.max_seqlen,
+                       p.k_cache, p.v_cache)
+    torch.cuda.synchronize()
+    n = p.num_tokens
+    table = ws[: n * d * 4].view(torch.float32).view(n, d).cpu().numpy().astype(np.float64)
+    i = np.arange(d // 2)
+    at = (d // 4) * ((i // 4) % 2) + 4 * (i // 8) + i % 4
+    assert sorted(at.tolist()) == list(range(d // 2))
+    ang = p.positions.cpu().numpy().astype(np.float64)[:, None] * oracle.rope_frequencies(d, 1e6)[None, :]
+    for got, want in ((table[:, at], np.cos(ang)), (table[:, d // 2 + at], np.sin(ang))):
+        want32 = want.astype(np.float32).astype(np.float64)
+        ulp = np.spacing(np.abs(want32).astype(np.float32)).astype(np.float64)
+        assert (np.abs(got - want32) <= ulp).all(), f"max error {np.abs(got - want32).max():.3e}"
 
 
 def test_prefill_is_deterministic_and_causal():
