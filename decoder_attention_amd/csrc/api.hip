@@ -39,8 +39,9 @@ int32_t check_config(const qkra_config* cfg) {
   return QKRA_OK;
 }
 
-// bf16: the per-token RoPE table [N][cos D/2, sin D/2] (fp32), from which the
-// attention kernel rotates Q itself; fp32: q~ [N, Hq, D].
+// bf16: the per-token RoPE table [N][D] (fp32, cos then sin, in the order
+// kernel 1 documents), from which the attention kernel rotates Q itself;
+// fp32: q~ [N, Hq, D].
 size_t prefill_workspace(const qkra_config* cfg, int64_t num_tokens) {
   if (cfg->dtype == QKRA_BF16) return align_up(static_cast<size_t>(num_tokens) * cfg->head_dim * sizeof(float));
   return align_up(static_cast<size_t>(num_tokens) * cfg->num_q_heads * cfg->head_dim * elem_size(cfg->dtype));
