@@ -199,7 +199,12 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
 
 template <typename T, int D>
 hipError_t launch_typed(const QkNormRopeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((qknorm_rope_kv_kernel<T, D>), dim3(a.num_rows), dim3(256), 0, stream,
+  // bf16 prefill (K and V heads only): one wavefront per token, whose four
+  // prefetched passes cover its 2*Hkv rows for Hkv <= 8 and whose fp64 angles
+  // then overlap other tokens' work on the CU (four wavefronts waiting on the
+  // first one's angles made the kernel a third slower).  Otherwise four.
+  const int threads = a.rope_table ? 64 : 256;
+  hipLaunchKernelGGL((qknorm_rope_kv_kernel<T, D>), dim3(a.num_rows), dim3(threads), 0, stream,
                      static_cast<const T*>(a.qkv), static_cast<const T*>(a.q_norm_weight),
                      static_cast<const T*>(a.k_norm_weight), a.positions, a.seq_info, a.slot_offsets,
                      a.decode_mode,
