@@ -39,7 +39,7 @@ struct QkNormRopeArgs {
   float rms_eps;
   double log2_rope_base;
   void* q_out;              // q~ [rows, Hq, D], or null when rope_table is set
-  float* rope_table;        // prefill, bf16: per row cos[D/2] then sin[D/2] (fp32); Q heads skipped
+  float* rope_table;        // prefill, bf16: per row D fp32, cos then sin (order in qknorm_rope.hip); Q heads skipped
   void* k_cache;
   void* v_cache;
 };
@@ -52,7 +52,7 @@ struct PrefillAttnArgs {
   // bf16 path: Q comes raw from qkv and is normalised and rotated on load.
   const void* qkv;          // [N, (Hq + 2Hkv) D]
   const void* q_norm_weight;
-  const float* rope_table;  // [N][cos D/2, sin D/2]
+  const float* rope_table;  // [N][D] fp32: cos then sin, in kernel 1's order
   float rms_eps;
   const void* k_cache;      // [B, Hkv, S, D]
   const void* v_cache;

@@ -12,7 +12,8 @@
 // pairs there instead of q~ and skips the Q heads: the attention kernel
 // normalises and rotates Q itself while loading it.
 //
-// Layout of the work: one workgroup per token row.  The D/2 rotation angles
+// Layout of the work: one workgroup per token row (one wavefront with a rope
+// table, four otherwise).  The D/2 rotation angles
 // of the row are formed once in fp64 (position * base^(-2i/D), then sin/cos)
 // and kept in LDS, so positions up to tens of thousands keep full fp32
 // accuracy in cos/sin.  Each head row is handled by D/8 lanes: a lane holds 4

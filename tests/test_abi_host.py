@@ -45,7 +45,7 @@ def test_status_strings_and_version():
 def test_workspace_bytes():
     cfg = da.make_config(32, 8, 128, da.QKRA_BF16)
     up = lambda n: -(-n // 256) * 256
-    # bf16 prefill: the per-token RoPE table [N][cos D/2, sin D/2] fp32, rounded up to 256 bytes
+    # bf16 prefill: the per-token RoPE table [N, D] fp32 (cos then sin), rounded up to 256 bytes
     assert da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_PREFILL, 100, 100) == up(100 * 128 * 4)
     assert da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_PREFILL, 1, 1) == 512
     # fp32 prefill: q~ [N, Hq, D] fp32
