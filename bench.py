@@ -43,9 +43,9 @@ KERNEL_SOURCES = {
     "prefill_attn_mfma_bf16": ["decoder_attention_amd/csrc/prefill_mfma.hip"] + _COMMON,
     "decode_attn_split": ["decoder_attention_amd/csrc/decode_mfma.hip"] + _COMMON,
     "decode_attn_combine": ["decoder_attention_amd/csrc/decode_mfma.hip"] + _COMMON,
-    "decode_plan": ["decoder_attention_amd/csrc/decode_mfma.hip"] + _COMMON,
     "qknorm_rope_kv_prefill": ["decoder_attention_amd/csrc/qknorm_rope.hip"] + _COMMON,
-    "qknorm_rope_kv_decode": ["decoder_attention_amd/csrc/qknorm_rope.hip"] + _COMMON,
+    "qknorm_rope_kv_decode": ["decoder_attention_amd/csrc/qknorm_rope.hip", "decoder_attention_amd/csrc/decode_plan.h"]
+    + _COMMON,
     "fused_add_rmsnorm": ["decoder_attention_amd/csrc/layer_ops.hip"] + _COMMON,
     "gather_last": ["decoder_attention_amd/csrc/layer_ops.hip"] + _COMMON,
     "argmax_partial": ["decoder_attention_amd/csrc/layer_ops.hip"] + _COMMON,
@@ -349,8 +349,8 @@ def main(argv=None):
     roof = roofline_for(dominant, kernels, F, B, args.workload)
     side = {}
     pre_ms = sum(kernels[k][0] for k in ("qknorm_rope_kv_prefill", "prefill_attn_mfma_bf16") if k in kernels)
-    dec_ms = sum(kernels[k][0] for k in ("qknorm_rope_kv_decode", "decode_plan", "decode_attn_split",
-                                         "decode_attn_combine") if k in kernels)
+    dec_ms = sum(kernels[k][0] for k in ("qknorm_rope_kv_decode", "decode_attn_split", "decode_attn_combine")
+                 if k in kernels)
     if F:
         tf = F / (pre_ms / args.steps / 1e3) / 1e12
         side["prefill_call"] = {"tflops": tf, "frac_of_mfma_peak": tf / PEAK_MFMA_TFLOPS,

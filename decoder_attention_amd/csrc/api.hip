@@ -359,6 +359,13 @@ QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv
   ka.q_out = workspace;
   ka.k_cache = k_cache;
   ka.v_cache = v_cache;
+  char* ws = static_cast<char*>(workspace) + decode_q_bytes(cfg, num_seqs);
+  if (cfg->dtype == QKRA_BF16) {  // kernel 1's launch also builds the split kernel's plan (one extra block)
+    const int group = cfg->num_q_heads / cfg->num_kv_heads;
+    ka.plan = reinterpret_cast<int32_t*>(ws);
+    ka.plan_units = static_cast<int>(decode_units(cfg, num_seqs));
+    ka.plan_nchunks = cfg->num_kv_heads * (group / decode_heads_per_wave(group));
+  }
   hipError_t err = timed(kKernelQkNormRopeDecode, stream, [&] { return launch_qknorm_rope(ka, stream); });
   if (err != hipSuccess) return hip_status(err);
 
@@ -375,14 +382,11 @@ QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv
   da.cache_capacity = cache_capacity;
   da.num_seqs = num_seqs;
   da.scale_log2 = softmax_scale_log2(cfg->head_dim);
-  char* ws = static_cast<char*>(workspace) + decode_q_bytes(cfg, num_seqs);
   if (cfg->dtype == QKRA_BF16) {
     da.plan = reinterpret_cast<int32_t*>(ws);
     da.partials = reinterpret_cast<float*>(ws + decode_plan_bytes(cfg, num_seqs));
     da.num_units = static_cast<int>(decode_units(cfg, num_seqs));
     da.heads_per_wave = decode_heads_per_wave(cfg->num_q_heads / cfg->num_kv_heads);
-    err = timed(kKernelDecodePlan, stream, [&] { return launch_decode_plan(da, stream); });
-    if (err != hipSuccess) return hip_status(err);
     err = timed(kKernelDecodeSplit, stream, [&] { return launch_decode_mfma(da, stream); });
     if (err != hipSuccess) return hip_status(err);
     err = timed(kKernelDecodeCombine, stream, [&] { return launch_decode_mfma_combine(da, stream); });
@@ -542,7 +546,6 @@ QKRA_API const char* qknorm_rope_attn_kernel_name(int32_t kernel_id) {
     case kKernelPrefillFp32: return "prefill_attn_fp32";
     case kKernelDecodeSplit: return "decode_attn_split";
     case kKernelDecodeCombine: return "decode_attn_combine";
-    case kKernelDecodePlan: return "decode_plan";
     case kKernelAddRmsNorm: return "fused_add_rmsnorm";
     case kKernelGatherLast: return "gather_last";
     case kKernelArgmaxPartial: return "argmax_partial";

@@ -16,8 +16,9 @@
 //    number of bytes whatever the length mix.  A wavefront whose range crosses
 //    unit boundaries carries its load pipeline across them and writes one
 //    partial (m, l, o) per unit portion; 3b merges a unit's portions.
-//  * 3p (plan) computes the step prefix over units, the range length and each
-//    wavefront's first unit on the device, from the cache lengths.
+//  * The plan (decode_plan.h: the step prefix over units, the range length and
+//    each wavefront's first unit) is built on the device from the cache
+//    lengths, by one extra block of kernel 1's decode launch.
 //  * Per 32-key step a wavefront loads its K and V rows lane-linearly (1 KB of
 //    contiguous rows per instruction, non-temporal: read once) into registers,
 //    while it computes the previous step from LDS; the rows then go to padded
@@ -59,60 +60,6 @@ __device__ __forceinline__ float quarter_max(float x) {
   const float y = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
   const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
   return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
-}
-
-__device__ __forceinline__ int unit_steps(const int32_t* cache_lens, int unit, int nchunks, int cache_capacity) {
-  const int nkeys = min(cache_lens[unit / nchunks] + 1, cache_capacity);
-  return (nkeys + STEP - 1) / STEP;
-}
-
-// ---- 3p: plan = [T, per, S0[0..N], first_unit[0..W)] (one workgroup).
-// S0[i] is the first global step of unit i (S0[N] = T, the total), per the
-// steps per wavefront, first_unit[w] the unit holding step w*per (-1: idle).
-constexpr int kPlanThreads = 1024;
-
-__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t* __restrict__ cache_lens,
-                                                                   int32_t* __restrict__ plan, int num_units,
-                                                                   int nchunks, int cache_capacity, int num_waves,
-                                                                   int min_steps) {
-  __shared__ int32_t s_scan[kPlanThreads];
-  const int tid = threadIdx.x;
-  const int per_thread = (num_units + kPlanThreads - 1) / kPlanThreads;
-  const int i0 = min(tid * per_thread, num_units);
-  const int i1 = min(i0 + per_thread, num_units);
-  int local = 0;
-  for (int i = i0; i < i1; ++i) local += unit_steps(cache_lens, i, nchunks, cache_capacity);
-  s_scan[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive scan of the per-thread sums
-    const int v = tid >= off ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
-  }
-  int32_t* S0 = plan + 2;
-  int32_t* first = plan + 3 + num_units;
-  const int total = s_scan[kPlanThreads - 1];
-  const int per = max((total + num_waves - 1) / num_waves, min_steps);
-  // Each thread records the first steps of its units and, for every unit, the
-  // wavefronts whose first step w*per falls inside it: w in
-  // [ceil(S0_i / per), ceil((S0_i + steps_i) / per)).  No search, no barrier.
-  int run = s_scan[tid] - local;
-  for (int i = i0; i < i1; ++i) {
-    const int steps = unit_steps(cache_lens, i, nchunks, cache_capacity);
-    S0[i] = run;
-    const long long wlo = (static_cast<long long>(run) + per - 1) / per;
-    const long long whi = min((static_cast<long long>(run) + steps + per - 1) / per, static_cast<long long>(num_waves));
-    for (long long w = wlo; w < whi; ++w) first[w] = i;
-    run += steps;
-  }
-  if (tid == 0) {
-    plan[0] = total;
-    plan[1] = per;
-    S0[num_units] = total;
-  }
-  for (int w = tid; w < num_waves; w += kPlanThreads)  // wavefronts past the last step stay idle
-    if (static_cast<long long>(w) * per >= total) first[w] = -1;
 }
 
 // ---- 3a: one wavefront per range of steps; 4 independent wavefronts per workgroup.
@@ -399,14 +346,6 @@ hipError_t launch_mfma_dim(const DecodeAttnArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
-
-hipError_t launch_decode_plan(const DecodeAttnArgs& a, hipStream_t stream) {
-  if (a.num_units <= 0) return hipSuccess;
-  const int nchunks = a.num_kv_heads * (a.num_q_heads / a.num_kv_heads / a.heads_per_wave);
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.cache_lens, a.plan,
-                     a.num_units, nchunks, a.cache_capacity, kDecodeWaves, kDecodeMinStepsPerWave);
-  return hipGetLastError();
-}
 
 hipError_t launch_decode_mfma(const DecodeAttnArgs& a, hipStream_t stream) {
   if (a.num_units <= 0) return hipSuccess;

@@ -15,12 +15,11 @@ enum KernelId : int {
   kKernelDecodeSplit = 3,
   kKernelDecodeCombine = 4,
   kKernelQkNormRopeDecode = 5,
-  kKernelDecodePlan = 6,
-  kKernelAddRmsNorm = 7,
-  kKernelGatherLast = 8,
-  kKernelArgmaxPartial = 9,
-  kKernelArgmaxFinal = 10,
-  kNumKernels = 11,
+  kKernelAddRmsNorm = 6,
+  kKernelGatherLast = 7,
+  kKernelArgmaxPartial = 8,
+  kKernelArgmaxFinal = 9,
+  kNumKernels = 10,
 };
 
 // Kernel 1: per token row, RMSNorm + RoPE of the Q and K heads; q~ to
@@ -42,6 +41,8 @@ struct QkNormRopeArgs {
   float* rope_table;        // prefill, bf16: per row D fp32, cos then sin (order in qknorm_rope.hip); Q heads skipped
   void* k_cache;
   void* v_cache;
+  int32_t* plan;            // bf16 decode: one more block builds the split kernel's plan there (or null)
+  int plan_units, plan_nchunks;
 };
 hipError_t launch_qknorm_rope(const QkNormRopeArgs& a, hipStream_t stream);
 
@@ -78,8 +79,9 @@ inline int decode_num_splits(int max_cache_len) {
 // bf16 (decode_mfma.hip): units (request, KV head, chunk of GW query heads)
 // cut into steps of kDecodeStepKeys keys; the steps of all units are split
 // evenly over kDecodeWaves persistent wavefronts (at least
-// kDecodeMinStepsPerWave each).  Kernel 3p writes the plan
-// [T, per, S0[0..N], first_unit[0..W)] (int32), 3a one partial record
+// kDecodeMinStepsPerWave each).  One extra block of kernel 1's decode launch
+// writes the plan [T, per, S0[0..N], first_unit[0..W)] (int32, decode_plan.h),
+// 3a one partial record
 // (m, l, pad, pad, o[D]) fp32 per (unit, wavefront) that meet, at slot
 // unit + wavefront of [N + W, GW, D + 4].
 constexpr int kDecodeStepKeys = 32;
@@ -111,7 +113,6 @@ struct DecodeAttnArgs {
 };
 hipError_t launch_decode_split(const DecodeAttnArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeAttnArgs& a, hipStream_t stream);
-hipError_t launch_decode_plan(const DecodeAttnArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeAttnArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma_combine(const DecodeAttnArgs& a, hipStream_t stream);
 

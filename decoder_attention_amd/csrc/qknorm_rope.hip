@@ -24,6 +24,7 @@
 // the lanes of a head.  A wavefront's first four passes are loaded before the
 // request lookup and the angle computation, so those latencies overlap.
 
+#include "decode_plan.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
     const int32_t* __restrict__ slot_offsets, int decode_mode,
     int num_seqs, int num_q_heads, int num_kv_heads, int cache_capacity, float eps,
     double log2_base, T* __restrict__ q_out, float* __restrict__ rope_table, T* __restrict__ k_cache,
-    T* __restrict__ v_cache) {
+    T* __restrict__ v_cache, int num_rows, int32_t* __restrict__ plan, int plan_units, int plan_nchunks) {
   using Raw = typename Raw4<T>::type;
   constexpr int HALF = D / 2;
   constexpr int LPH = HALF / 4;  // lanes per head row
@@ -67,6 +68,11 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
   __shared__ float s_sin[HALF];
 
   const int row_id = blockIdx.x;
+  if (row_id == num_rows) {  // bf16 decode: the block past the rows builds the split kernel's plan
+    __shared__ int32_t s_scan[256];
+    build_decode_plan<256>(seq_info, plan, plan_units, plan_nchunks, cache_capacity, s_scan);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
@@ -205,13 +211,15 @@ hipError_t launch_typed(const QkNormRopeArgs& a, hipStream_t stream) {
   // then overlap other tokens' work on the CU (four wavefronts waiting on the
   // first one's angles made the kernel a third slower).  Otherwise four.
   const int threads = a.rope_table ? 64 : 256;
-  hipLaunchKernelGGL((qknorm_rope_kv_kernel<T, D>), dim3(a.num_rows), dim3(threads), 0, stream,
+  if (a.plan && threads != 256) return hipErrorInvalidValue;  // the plan block is written for 256 threads
+  const int blocks = a.num_rows + (a.plan ? 1 : 0);
+  hipLaunchKernelGGL((qknorm_rope_kv_kernel<T, D>), dim3(blocks), dim3(threads), 0, stream,
                      static_cast<const T*>(a.qkv), static_cast<const T*>(a.q_norm_weight),
                      static_cast<const T*>(a.k_norm_weight), a.positions, a.seq_info, a.slot_offsets,
                      a.decode_mode,
                      a.num_seqs, a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.rms_eps,
                      a.log2_rope_base, static_cast<T*>(a.q_out), a.rope_table, static_cast<T*>(a.k_cache),
-                     static_cast<T*>(a.v_cache));
+                     static_cast<T*>(a.v_cache), a.num_rows, a.plan, a.plan_units, a.plan_nchunks);
   return hipGetLastError();
 }
 
