@@ -177,3 +177,44 @@ def test_argmax_mixed_step_sampled():
     want = oracle.greedy_argmax(f64(nt.logits[rows]))
     assert np.array_equal(got[rows], want)
     assert np.array_equal(got, np.argmax(f64(nt.logits), axis=1))
+
+
+# ---- seeded sweep ---------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("i", range(8))
+def test_fused_add_rmsnorm_sweep(i, dtype):
+    # Random row counts and hidden sizes (any multiple of 8 up to 32768), eps, first or later call.
+    rng = np.random.default_rng(500 + i)
+    rows = int(rng.integers(1, 300))
+    hidden = 8 * int(rng.integers(1, 4097))
+    has_residual = bool(rng.integers(0, 2))
+    eps = float(rng.choice([1e-6, 1e-5, 1e-2]))
+    note(f"fused_add_rmsnorm sweep {i}: rows {rows} hidden {hidden} residual {has_residual} eps {eps} {dtype}")
+    n = make_norm_inputs(rows, hidden, seed=int(rng.integers(1 << 20)), dtype=dtype, device=DEV,
+                         has_residual=has_residual, rms_eps=eps)
+    x0 = n.x.clone()
+    res0 = n.residual.clone() if has_residual else None
+    res = n.residual if has_residual else torch.empty_like(n.x)
+    out = da.fused_add_rmsnorm(n.x, res, n.weight, eps, has_residual)
+    torch.cuda.synchronize()
+    check_norm(n, dtype, out, res, x0, res0, eps)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("i", range(8))
+def test_argmax_sweep(i, dtype):
+    # Random vocabularies (not multiples of anything), padded strides, planted ties and extremes.
+    rng = np.random.default_rng(600 + i)
+    rows = int(rng.integers(1, 12))  # the oracle scans in Python
+    vocab = int(rng.integers(1, 200000))
+    stride = (vocab + 7) // 8 * 8 + 8 * int(rng.integers(0, 3))
+    g = torch.Generator().manual_seed(int(rng.integers(1 << 20)))
+    buf = torch.randn((rows, stride), generator=g)
+    for r in range(rows):  # a planted maximum, sometimes repeated (ties go to the lowest index)
+        at = rng.integers(0, vocab, size=int(rng.integers(1, 4)))
+        buf[r, at] = 50.0
+    logits = buf.to(dtype).to(DEV)[:, :vocab]
+    note(f"argmax sweep {i}: rows {rows} vocab {vocab} stride {stride} {dtype}")
+    want = oracle.greedy_argmax(f64(logits))
+    assert np.array_equal(run_argmax(logits), want)
