@@ -252,6 +252,7 @@ int32_t prefill_impl(const qkra_config* cfg, const void* qkv, const void* q_norm
   pa.q = workspace;
   pa.qkv = qkv;
   pa.q_norm_weight = q_norm_weight;
+  pa.k_norm_weight = k_norm_weight;
   pa.rope_table = static_cast<const float*>(workspace);
   pa.rms_eps = cfg->rms_eps;
   pa.k_cache = k_cache;
@@ -266,9 +267,11 @@ int32_t prefill_impl(const qkra_config* cfg, const void* qkv, const void* q_norm
   pa.num_seqs = num_seqs;
   pa.max_seqlen = max_seqlen;
   pa.scale_log2 = softmax_scale_log2(cfg->head_dim);
-  if (cfg->dtype == QKRA_BF16)
-    err = timed(kKernelPrefillMfma, stream, [&] { return launch_prefill_attn_bf16(pa, stream); });
-  else
+  if (cfg->dtype == QKRA_BF16) {
+    err = timed(kKernelPrefillMfma, stream, [&] { return launch_prefill_attn_bf16(pa, true, stream); });
+    if (err == hipSuccess)
+      err = timed(kKernelPrefillMfmaShifted, stream, [&] { return launch_prefill_attn_bf16(pa, false, stream); });
+  } else
     err = timed(kKernelPrefillFp32, stream, [&] { return launch_prefill_attn_fp32(pa, stream); });
   return hip_status(err);
 }
@@ -543,6 +546,7 @@ QKRA_API const char* qknorm_rope_attn_kernel_name(int32_t kernel_id) {
     case kKernelQkNormRopePrefill: return "qknorm_rope_kv_prefill";
     case kKernelQkNormRopeDecode: return "qknorm_rope_kv_decode";
     case kKernelPrefillMfma: return "prefill_attn_mfma_bf16";
+    case kKernelPrefillMfmaShifted: return "prefill_attn_mfma_bf16_shifted";
     case kKernelPrefillFp32: return "prefill_attn_fp32";
     case kKernelDecodeSplit: return "decode_attn_split";
     case kKernelDecodeCombine: return "decode_attn_combine";

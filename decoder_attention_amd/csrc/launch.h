@@ -19,7 +19,8 @@ enum KernelId : int {
   kKernelGatherLast = 7,
   kKernelArgmaxPartial = 8,
   kKernelArgmaxFinal = 9,
-  kNumKernels = 10,
+  kKernelPrefillMfmaShifted = 10,
+  kNumKernels = 11,
 };
 
 // Kernel 1: per token row, RMSNorm + RoPE of the Q and K heads; q~ to
@@ -53,6 +54,7 @@ struct PrefillAttnArgs {
   // bf16 path: Q comes raw from qkv and is normalised and rotated on load.
   const void* qkv;          // [N, (Hq + 2Hkv) D]
   const void* q_norm_weight;
+  const void* k_norm_weight; // its largest |w| bounds every score (see prefill_mfma.hip)
   const float* rope_table;  // [N][D] fp32: cos then sin, in kernel 1's order
   float rms_eps;
   const void* k_cache;      // [B, Hkv, S, D]
@@ -63,7 +65,12 @@ struct PrefillAttnArgs {
   int num_q_heads, num_kv_heads, head_dim, cache_capacity, num_seqs, max_seqlen;
   float scale_log2;         // log2(e) / sqrt(D)
 };
-hipError_t launch_prefill_attn_bf16(const PrefillAttnArgs& a, hipStream_t stream);
+// bf16: two kernels over the same grid, both launched by every call.
+// unshifted = true launches the one that takes p = 2^s without a shift (a
+// workgroup returns at once unless its request has no cached history and the
+// norm weights bound the scores); false, the online-softmax one with a
+// running max (it returns at once where the other runs).
+hipError_t launch_prefill_attn_bf16(const PrefillAttnArgs& a, bool unshifted, hipStream_t stream);
 hipError_t launch_prefill_attn_fp32(const PrefillAttnArgs& a, hipStream_t stream);
 
 // Kernels 3a/3b: split-KV decode attention and the log-sum-exp combine.

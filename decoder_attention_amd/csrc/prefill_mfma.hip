@@ -25,9 +25,19 @@
 //    permuted so that each lane's 8 keys are one 16-byte read.  The O^T
 //    accumulator is again one query per lane, so the online-softmax rescale
 //    is a per-lane multiply.
-//  * fp32 online softmax in the log2 domain (scale log2(e)/sqrt(D) folded into
-//    the exponent's FMA); the running max is raised lazily (only when a tile
-//    max exceeds it by more than 2^8), so the O rescale is rare.  K/V tiles
+//  * Softmax in the log2 domain: q~ is multiplied by log2(e)/sqrt(D) before
+//    its bf16 rounding, so a score is already the exponent of 2 that softmax
+//    takes.  Softmax is unchanged by a common shift of a row's scores, and
+//    with normalised Q and K the scores cannot leave a small range: RMSNorm
+//    leaves a head vector of norm at most max|w| sqrt(D) and the rotation
+//    keeps norms, so |s| <= max|w_q| max|w_k| sqrt(D) log2(e) (Cauchy-
+//    Schwarz).  When that bound is at most BOUND_LOG2 and every key was
+//    written by this call (plain prefill), p = 2^s is taken with no shift at
+//    all: no row max, no rescale, no subtraction, and p, its row sum and P.V
+//    stay far inside fp32 and bf16 range.  Otherwise (larger weights, or a
+//    chunk appended onto a cache the caller filled) the fp32 online softmax
+//    subtracts a running max that is raised lazily (only when a tile max
+//    exceeds it by more than 2^8), so the O rescale is rare.  K/V tiles
 //    run only up to the causal diagonal of the workgroup's last token; tiles
 //    entirely above a wavefront's rows are skipped by that wavefront; only
 //    tiles that cross the diagonal are masked.
@@ -70,6 +80,9 @@ constexpr int BN = QKRA_PREFILL_BN;
 constexpr int NWAVES = 8 / QB;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr float TAU = 8.0f;   // lazy-rescale threshold (log2 units)
+// Largest score bound (log2 units) taken without a shift: p then lies in
+// [2^-48, 2^48], a row sum of up to 2^31 keys below 2^79.
+constexpr float BOUND_LOG2 = 48.0f;
 static_assert(QB == 1 || QB == 2, "QB");
 static_assert(BN == 32 || BN == 64, "BN");
 
@@ -79,14 +92,59 @@ __device__ __forceinline__ float half_wave_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <int D, int HC>
+constexpr int NSLOT = 3;  // LDS tile slots
+
+// Whether p = 2^s may be taken without a shift: a request with no cached
+// history (every key it reads is written by this call with k_norm_weight)
+// and max|w_q| max|w_k| at most
+// `limit` = BOUND_LOG2 / (1.02 D scale_log2).  |s| <= |q~'| |k~| with
+// |q~'| <= max|w_q| sqrt(D) scale_log2 and |k~| <= max|w_k| sqrt(D); the
+// factor 1.02 covers the bf16 roundings of q~' and k~ and the fp32
+// arithmetic before them.  Every wavefront of both prefill kernels reduces
+// the same weights the same way (max is exact, one rounded product), so the
+// answer is the same everywhere.  A NaN weight fails the test.
+// The test is split in two so that the kernel that runs can issue its first
+// loads between the weight loads and the decision.
+struct WeightMax {
+  float q, k;  // this lane's largest |w|, then the wavefront's
+};
+template <int D>
+__device__ __forceinline__ WeightMax weight_max_lane(const bf16* __restrict__ q_norm_weight,
+                                                     const bf16* __restrict__ k_norm_weight) {
+  const int lane = threadIdx.x & 63;
+  WeightMax w{0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    w.q = fmaxf(w.q, fabsf(static_cast<float>(q_norm_weight[lane + 64 * i])));
+    w.k = fmaxf(w.k, fabsf(static_cast<float>(k_norm_weight[lane + 64 * i])));
+  }
+  return w;
+}
+__device__ __forceinline__ bool scores_bounded(WeightMax w, int past, float limit) {
+  if (past != 0) return false;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    w.q = fmaxf(w.q, xor_shuffle(w.q, m));
+    w.k = fmaxf(w.k, xor_shuffle(w.k, m));
+  }
+  return __builtin_amdgcn_readfirstlane(w.q * w.k <= limit ? 1 : 0) != 0;
+}
+
+// One work item, with the softmax path fixed at compile time (kBounded: no
+// shift).  Each path is a kernel of its own: in one kernel, the register
+// allocation shared by the two tile loops spilled in the shifted one and
+// slowed both.  Every call launches both kernels over the same grid; each
+// workgroup of the one whose path its request and the weights do not select
+// returns at once.
+template <int D, int HC, bool kBounded>
 __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
-    const bf16* __restrict__ qkv, const bf16* __restrict__ q_norm_weight, const float* __restrict__ rope_table,
+    const bf16* __restrict__ qkv, const bf16* __restrict__ q_norm_weight, const bf16* __restrict__ k_norm_weight,
+    const float* __restrict__ rope_table,
     const bf16* __restrict__ k_cache, const bf16* __restrict__ v_cache,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ past_lens, bf16* __restrict__ out,
     int num_q_heads, int num_kv_heads,
     int cache_capacity, int num_seqs, int tiles_per_seq, int chunks_per_kv, int num_items,
-    float rms_eps, float scale_log2) {
+    float rms_eps, float scale_log2, float bound_limit) {
   constexpr int TBN = 8 / HC;       // token blocks (of 32) per workgroup
   constexpr int TM = 32 * TBN;      // tokens per workgroup
   constexpr int DS = D / 16;        // k-steps over D for the scores
@@ -98,8 +156,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   constexpr int KCH = BN * D / 8;   // 16-byte K chunks per tile
   constexpr int KCHUNKS = (KCH + NTHREADS - 1) / NTHREADS;
   constexpr int VITEMS = (BN / 4) * (D / 8);  // (4 keys x 8 d) V items per tile
-  constexpr int NSLOT = 3;          // LDS tile slots
-
   __shared__ __attribute__((aligned(16))) bf16 sK[NSLOT][BN * KST];
   __shared__ __attribute__((aligned(16))) bf16 sV[NSLOT][D * VST];
 
@@ -119,6 +175,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   const int seqlen = min(cu_seqlens[seq + 1] - cu0, cache_capacity - past);
   const int t0 = tile * TM;
   if (t0 >= seqlen) return;
+  // The shifted kernel decides here (its workgroup returns with nothing else
+  // loaded when the other kernel runs); the unshifted one once its first K/V
+  // tile and Q loads are in flight.
+  const WeightMax wmax = weight_max_lane<D>(q_norm_weight, k_norm_weight);
+  if constexpr (!kBounded) {
+    if (scores_bounded(wmax, past, bound_limit)) return;
+  }
   const int group = num_q_heads / num_kv_heads;
   const int g = chunk / chunks_per_kv;
   const int h0 = g * group + (chunk % chunks_per_kv) * HC;
@@ -182,7 +245,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
         for (int pc = 0; pc < 4; ++pc) qtab[qb][gi][pc] = *reinterpret_cast<const f32x4*>(tab + pc * (D / 4));
       }
   };
-  // Normalise, rotate, stage and read back as fragments.
+  // Normalise, rotate, scale by log2(e)/sqrt(D), stage and read back as
+  // fragments.
   auto q_finish = [&]() {
     const u32x4 wlo = *reinterpret_cast<const u32x4*>(q_norm_weight + 8 * qj);
     const u32x4 whi = *reinterpret_cast<const u32x4*>(q_norm_weight + D / 2 + 8 * qj);
@@ -202,7 +266,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
         }
 #pragma unroll
         for (int m = 1; m < QLPR; m <<= 1) ss += xor_shuffle(ss, m);
-        const float inv_rms = rsqrtf(ss * (1.0f / D) + rms_eps);
+        const float inv_rms = rsqrtf(ss * (1.0f / D) + rms_eps) * scale_log2;
         float y1[8], y2[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -332,9 +396,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     }
   };
 
-  // Causal mask (tiles that cross the diagonal only) and the tile's row max,
-  // taken on raw scores (the scale is positive).
-  auto tile_max = [&](int kt, f32x16 (&S)[QB][KB], float (&mx)[QB]) {
+  // Causal mask (tiles that cross the diagonal only).
+  auto tile_mask = [&](int kt, f32x16 (&S)[QB][KB]) {
     const int k0 = kt * BN;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -346,12 +409,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
           for (int j = 0; j < 16; ++j)
             if (32 * kb + 8 * (j >> 2) + (j & 3) > lim) S[qb][kb][j] = kNegInf;
       }
+    }
+  };
+
+  // The tile's row max (shifted path only).
+  auto tile_max = [&](f32x16 (&S)[QB][KB], float (&mx)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
       float m = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) m = fmaxf(m, S[qb][kb][j]);
-      mx[qb] = half_wave_max(m) * scale_log2;
+      mx[qb] = half_wave_max(m);
     }
   };
 
@@ -373,9 +443,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     }
   };
 
-  // p = 2^(s*scale - m), rounded to bf16 as the B operand of the P.V product;
-  // the row sum accumulates the same rounded values (dot with (1, 1)).
-  // 16-key step ks uses registers 8*(ks%2) .. +7 of key block ks/2.
+  // p = 2^s (bounded path) or 2^(s - m), rounded to bf16 as the B operand of
+  // the P.V product; the row sum accumulates the same rounded values (dot
+  // with (1, 1)).  16-key step ks uses registers 8*(ks%2) .. +7 of key block
+  // ks/2.
   const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
   auto probs = [&](f32x16 (&S)[QB][KB], bf16x8 (&pf)[QB][KSTEPS]) {
 #pragma unroll
@@ -388,8 +459,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(__builtin_fmaf(S[qb][kb][base + 2 * e], scale_log2, nm));
-          const float p1 = fast_exp2(__builtin_fmaf(S[qb][kb][base + 2 * e + 1], scale_log2, nm));
+          const float p0 = fast_exp2(kBounded ? S[qb][kb][base + 2 * e] : S[qb][kb][base + 2 * e] + nm);
+          const float p1 = fast_exp2(kBounded ? S[qb][kb][base + 2 * e + 1] : S[qb][kb][base + 2 * e + 1] + nm);
           w[e] = pack_bf16x2(p0, p1);
           rs = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[e]), ones, rs, false);
         }
@@ -438,9 +509,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
       probs(Scur, pf);
       pv(SlotPv{}, pf);
       if (kt + 1 < wtiles) {
-        float mx[QB];
-        tile_max(kt + 1, Snext, mx);
-        raise_max(mx);
+        tile_mask(kt + 1, Snext);
+        if constexpr (!kBounded) {
+          float mx[QB];
+          tile_max(Snext, mx);
+          raise_max(mx);
+        }
       }
     }
     if (prefetch) store_tile(SlotLd{});
@@ -455,6 +529,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   // fragments from there.
   load_tile(0);
   q_issue();
+  if constexpr (kBounded) {
+    if (!scores_bounded(wmax, past, bound_limit)) {
+      __builtin_amdgcn_s_waitcnt(0);  // leave with no load outstanding
+      return;
+    }
+  }
   store_tile(C0{});
   if (ntiles > 1) load_tile(1);
   q_finish();
@@ -462,10 +542,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   if (ntiles > 1) store_tile(C1{});
   __syncthreads();
   f32x16 sA[QB][KB], sB[QB][KB];
-  {
+  scores(C0{}, sA);
+  tile_mask(0, sA);
+  if constexpr (!kBounded) {
     float mx[QB];
-    scores(C0{}, sA);
-    tile_max(0, sA, mx);
+    tile_max(sA, mx);
     raise_max(mx);
   }
   // Unrolled by 2*NSLOT: the score buffers alternate every step and the LDS
@@ -522,7 +603,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   }
 }
 
-template <int D, int HC>
+template <int D, int HC, bool kBounded>
 hipError_t launch_typed(const PrefillAttnArgs& a, hipStream_t stream) {
   constexpr int TM = 32 * (8 / HC);
   const int group = a.num_q_heads / a.num_kv_heads;
@@ -532,29 +613,31 @@ hipError_t launch_typed(const PrefillAttnArgs& a, hipStream_t stream) {
   if (items <= 0) return hipSuccess;
   const long long grid = (items + 7) / 8 * 8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, HC>), dim3(static_cast<unsigned>(grid)), dim3(NTHREADS), 0, stream,
-                     static_cast<const bf16*>(a.qkv), static_cast<const bf16*>(a.q_norm_weight), a.rope_table,
+  const float bound_limit = BOUND_LOG2 / (1.02f * static_cast<float>(D) * a.scale_log2);
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, HC, kBounded>), dim3(static_cast<unsigned>(grid)), dim3(NTHREADS), 0, stream,
+                     static_cast<const bf16*>(a.qkv), static_cast<const bf16*>(a.q_norm_weight),
+                     static_cast<const bf16*>(a.k_norm_weight), a.rope_table,
                      static_cast<const bf16*>(a.k_cache),
                      static_cast<const bf16*>(a.v_cache), a.cu_seqlens, a.past_lens, static_cast<bf16*>(a.out),
                      a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.num_seqs, tiles, chunks_per_kv,
-                     static_cast<int>(items), a.rms_eps, a.scale_log2);
+                     static_cast<int>(items), a.rms_eps, a.scale_log2, bound_limit);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool kBounded>
 hipError_t launch_dim(const PrefillAttnArgs& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
-  if (group % 8 == 0) return launch_typed<D, 8>(a, stream);
-  if (group % 4 == 0) return launch_typed<D, 4>(a, stream);
-  if (group % 2 == 0) return launch_typed<D, 2>(a, stream);
-  return launch_typed<D, 1>(a, stream);
+  if (group % 8 == 0) return launch_typed<D, 8, kBounded>(a, stream);
+  if (group % 4 == 0) return launch_typed<D, 4, kBounded>(a, stream);
+  if (group % 2 == 0) return launch_typed<D, 2, kBounded>(a, stream);
+  return launch_typed<D, 1, kBounded>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_prefill_attn_bf16(const PrefillAttnArgs& a, hipStream_t stream) {
-  if (a.head_dim == 128) return launch_dim<128>(a, stream);
-  if (a.head_dim == 64) return launch_dim<64>(a, stream);
+hipError_t launch_prefill_attn_bf16(const PrefillAttnArgs& a, bool unshifted, hipStream_t stream) {
+  if (a.head_dim == 128) return unshifted ? launch_dim<128, true>(a, stream) : launch_dim<128, false>(a, stream);
+  if (a.head_dim == 64) return unshifted ? launch_dim<64, true>(a, stream) : launch_dim<64, false>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -40,6 +40,7 @@ def test_status_strings_and_version():
     assert da.qknorm_rope_attn_version() == 100
     assert da.qknorm_rope_attn_last_hip_error() == 0
     assert da.qknorm_rope_attn_kernel_name(1) == "prefill_attn_mfma_bf16"
+    assert da.qknorm_rope_attn_kernel_name(10) == "prefill_attn_mfma_bf16_shifted"
 
 
 def test_workspace_bytes():

@@ -1,0 +1,104 @@
+"""Both softmax paths of the bf16 prefill, on the GPU against the oracle.
+
+Softmax does not change when all scores of a row move by the same amount.
+With RMS-normalised Q and K, every score is bounded by
+max|w_q| * max|w_k| * sqrt(D) (Cauchy-Schwarz; the rotation keeps norms).
+A request with no cached history whose norm weights keep that bound small
+takes p = 2^s with no shift at all. Any other request subtracts a running row
+max. The two paths are two kernels launched over the same grid. Each
+workgroup decides from its request's history length and the weights which of
+them computes its rows.
+
+- Largest weights just below and just above the switch give oracle results, and
+  every output row is written: `out` starts as NaN, so a row that neither
+  kernel, or the wrong one, handled would show.
+- Q heads equal to their K head, with weights 4, put each row's own score near
+  2^261. Unshifted, p would overflow to inf and the row would be NaN, so this
+  case passes only when the shifted kernel ran.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import decoder_attention_amd as da
+from harness import BF16_TOL, assert_close, cfg_of, f64, note, oracle_prefill
+from workloads import HeadConfig, make_prefill_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _set_weights(p, wq: np.ndarray, wk: np.ndarray) -> None:
+    p.q_norm_weight.copy_(torch.from_numpy(wq).to(p.q_norm_weight.dtype))
+    p.k_norm_weight.copy_(torch.from_numpy(wk).to(p.k_norm_weight.dtype))
+
+
+def _run_and_check(p, what: str) -> None:
+    h = p.heads
+    out = torch.full((p.num_tokens, h.num_q_heads * h.head_dim), float("nan"), dtype=p.qkv.dtype, device=DEV)
+    da.prefill(cfg_of(h, p.qkv.dtype), p.qkv, p.q_norm_weight, p.k_norm_weight, p.positions, p.cu_seqlens,
+               p.max_seqlen, p.k_cache, p.v_cache, out=out)
+    torch.cuda.synchronize()
+    ref = oracle_prefill(p)
+    assert_close(f64(out), ref["out"], BF16_TOL, f"{what}: out")
+    # K cache: the bound 2e-2 plus half a bf16 step of the value (k~ reaches
+    # |x| >= 8 here, where one correctly rounded bf16 is off by up to 0.03).
+    cu = p.cu_seqlens.cpu().tolist()
+    for r in range(p.num_seqs):
+        lo, hi = cu[r], cu[r + 1]
+        got = f64(p.k_cache[r, :, : hi - lo])
+        want = np.transpose(ref["k_tilde"][lo:hi], (1, 0, 2))
+        assert np.all(np.abs(got - want) <= BF16_TOL + np.abs(want) * 2.0**-8), f"{what}: K cache request {r}"
+
+
+# One element of each weight vector set to c (the rest drawn as usual, |w| < 1.5), so that
+# max|w_q| max|w_k| = c^2.  The switch lies at 48 / (1.02 D log2(e) / sqrt(D)): 2.88 for D = 128
+# (c = 1.697) and 4.08 for D = 64 (c = 2.019); each list has bf16 values on both sides.  Uniform
+# weights that large would amplify every score about 2.9x, and the bf16 rounding of q~ and k~ alone
+# would then exceed the bound on either path.
+@pytest.mark.parametrize("head_dim,hq,hkv,weights", [
+    (128, 32, 8, [1.6875, 1.6953125, 1.703125, 1.7109375]),
+    (64, 8, 2, [2.0, 2.015625, 2.03125, 2.046875]),
+    (128, 16, 16, [1.6953125, 1.703125]),
+], ids=["d128_g4", "d64_g4", "d128_g1"])
+def test_weights_on_both_sides_of_the_switch(head_dim, hq, hkv, weights):
+    h = HeadConfig(hq, hkv, head_dim, 1e-6, 1e6)
+    lens = [300, 1, 0, 129]
+    for c in weights:
+        p = make_prefill_inputs(h, lens, seed=61, device=DEV, capacity=max(lens))
+        wq, wk = f64(p.q_norm_weight), f64(p.k_norm_weight)
+        assert np.abs(wq).max() < c and np.abs(wk).max() < c
+        wq[3], wk[3] = c, -c
+        _set_weights(p, wq, wk)
+        note(f"prefill D={head_dim} Hq={hq} Hkv={hkv} largest weights {c}")
+        _run_and_check(p, f"weights {c}")
+
+
+def test_one_large_weight_takes_the_shifted_path():
+    """The bound uses the largest weight: one outlier element moves the switch, while the typical scores stay
+    moderate."""
+    h = HeadConfig(32, 8, 128, 1e-6, 1e6)
+    lens = [513, 64, 7]
+    p = make_prefill_inputs(h, lens, seed=62, device=DEV, capacity=max(lens))
+    wq, wk = f64(p.q_norm_weight), f64(p.k_norm_weight)
+    wq[5], wk[77] = 2.5, -2.5
+    _set_weights(p, wq, wk)
+    note("prefill with one outlier weight per norm")
+    _run_and_check(p, "outlier weights")
+
+
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_scores_beyond_fp32_range_need_the_shift(head_dim):
+    h = HeadConfig(8, 2, head_dim, 1e-6, 1e4)
+    lens = [200, 75]
+    p = make_prefill_inputs(h, lens, seed=63, device=DEV, capacity=max(lens))
+    g = h.num_q_heads // h.num_kv_heads
+    d = head_dim
+    for q in range(h.num_q_heads):  # Q head q := its K head, so q~ = k~ at every token
+        kv = h.num_q_heads + q // g
+        p.qkv[:, q * d:(q + 1) * d] = p.qkv[:, kv * d:(kv + 1) * d]
+    _set_weights(p, np.full(d, 4.0), np.full(d, 4.0))
+    note(f"prefill D={head_dim} with q = k and weights 4 (self scores ~2^261)")
+    _run_and_check(p, "q = k, weights 4")
