@@ -209,3 +209,39 @@ def test_decode_mixed_step_part_sampled():
                                                                                                          replace=False)))
     err = _check_decode(w.decode, subset)
     note(f"mixed decode: requests {subset} (lengths {[lens[b] for b in subset]}) max-abs error {err:.3e}")
+
+
+# Units that one wavefront covers, units cut over many wavefronts, several
+# query-head chunks per KV head, and idle wavefronts.
+MERGE_CASES = [
+    (32, 8, 128, [0, 3, 17, 31, 32, 33, 64, 150]),
+    (32, 8, 128, [20000, 2, 9000]),
+    (48, 3, 128, [5000, 7]),
+    (10, 2, 64, [12000, 400, 0]),
+]
+
+
+@pytest.mark.parametrize("case", MERGE_CASES, ids=_ids)
+def test_decode_writes_every_row_once_and_reuses_its_workspace(case):
+    """`out` starts as NaN, so a head that the combine never stored shows.  Two calls share one workspace (the
+    plan and the partial records of the first call are still there) and give the same bits."""
+    import decoder_attention_amd as da
+    from harness import cfg_of
+
+    hq, hkv, d, lens = case
+    h = HeadConfig(hq, hkv, d, 1e-6, 1e6)
+    note(f"decode merge {_ids(case)}")
+    cfg = cfg_of(h, torch.bfloat16)
+    ws = None
+    outs = []
+    for _ in range(2):
+        dec = make_decode_inputs(h, lens, seed=77, device=DEV, capacity=max(lens) + 1)
+        ref = oracle.decode(f64(dec.qkv), f64(dec.q_norm_weight), f64(dec.k_norm_weight), dec.positions.cpu().numpy(),
+                            np.array(lens), f64(dec.k_cache), f64(dec.v_cache), **layer_kw(h))
+        out = torch.full((len(lens), hq * d), float("nan"), dtype=torch.bfloat16, device=DEV)
+        out, ws = da.decode(cfg, dec.qkv, dec.q_norm_weight, dec.k_norm_weight, dec.positions, dec.cache_lens,
+                            max(lens), dec.k_cache, dec.v_cache, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(f64(out), ref["out"], BF16_TOL, "decode out")
+        outs.append(out.clone())
+    assert torch.equal(bits(outs[0]), bits(outs[1]))
