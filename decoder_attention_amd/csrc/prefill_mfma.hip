@@ -168,20 +168,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   const int rem = logical - chunk * per_chunk;
   const int seq = rem / tiles_per_seq;
   const int tile = tiles_per_seq - 1 - rem % tiles_per_seq;
-  const int cu0 = cu_seqlens[seq];
   // Entries cached before the chunk (its token t sits at slot past + t).
   // Lengths are clamped to the cache so out-of-contract inputs cannot address past it.
   const int past = past_lens ? min(max(past_lens[seq], 0), cache_capacity) : 0;
+  // Which kernel runs the item.  The workgroup of the other one returns as
+  // early as it can: the unshifted kernel as soon as it sees a history, the
+  // shifted one once the weights are reduced, before anything else is
+  // loaded.  The unshifted kernel tests the weights once its first K/V tile
+  // and Q loads are in flight (below).
+  if constexpr (kBounded) {
+    if (past != 0) return;
+  } else {
+    if (past == 0 && scores_bounded(weight_max_lane<D>(q_norm_weight, k_norm_weight), 0, bound_limit)) return;
+  }
+  const int cu0 = cu_seqlens[seq];
   const int seqlen = min(cu_seqlens[seq + 1] - cu0, cache_capacity - past);
   const int t0 = tile * TM;
   if (t0 >= seqlen) return;
-  // The shifted kernel decides here (its workgroup returns with nothing else
-  // loaded when the other kernel runs); the unshifted one once its first K/V
-  // tile and Q loads are in flight.
-  const WeightMax wmax = weight_max_lane<D>(q_norm_weight, k_norm_weight);
-  if constexpr (!kBounded) {
-    if (scores_bounded(wmax, past, bound_limit)) return;
-  }
+  WeightMax wmax{0.f, 0.f};
+  if constexpr (kBounded) wmax = weight_max_lane<D>(q_norm_weight, k_norm_weight);
   const int group = num_q_heads / num_kv_heads;
   const int g = chunk / chunks_per_kv;
   const int h0 = g * group + (chunk % chunks_per_kv) * HC;
