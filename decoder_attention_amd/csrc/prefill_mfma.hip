@@ -31,13 +31,15 @@
 //    with normalised Q and K the scores cannot leave a small range: RMSNorm
 //    leaves a head vector of norm at most max|w| sqrt(D) and the rotation
 //    keeps norms, so |s| <= max|w_q| max|w_k| sqrt(D) log2(e) (Cauchy-
-//    Schwarz).  When that bound is at most BOUND_LOG2 and every key was
-//    written by this call (plain prefill), p = 2^s is taken with no shift at
-//    all: no row max, no rescale, no subtraction, and p, its row sum and P.V
-//    stay far inside fp32 and bf16 range.  Otherwise (larger weights, or a
-//    chunk appended onto a cache the caller filled) the fp32 online softmax
-//    subtracts a running max that is raised lazily (only when a tile max
-//    exceeds it by more than 2^8), so the O rescale is rare.  K/V tiles
+//    Schwarz).  When that bound is at most BOUND_LOG2 and the request has no
+//    cached history (every key it reads is written by this call), p = 2^s is
+//    taken with no shift at all: no row max, no rescale, no subtraction, and
+//    p, its row sum and P.V stay far inside fp32 and bf16 range.  Otherwise
+//    (larger weights, or a request whose history the caller wrote) the fp32
+//    online softmax subtracts a running max that is raised lazily (only when
+//    a tile max exceeds it by more than 2^8), so the O rescale is rare.  The
+//    two are separate kernels over the same grid (prefill_mfma_kernel<..,
+//    true> and <.., false>); each work item runs in one of them.  K/V tiles
 //    run only up to the causal diagonal of the workgroup's last token; tiles
 //    entirely above a wavefront's rows are skipped by that wavefront; only
 //    tiles that cross the diagonal are masked.
