@@ -294,17 +294,45 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
   const int s_first = S0[i] / per, s_last = (S0[i + 1] - 1) / per;
   const int lane = threadIdx.x;
   auto rec = [&](int s) { return partials + (static_cast<size_t>(i + s) * gw + hh) * PREC; };
-  float m = kNegInf;
-  for (int s = s_first; s <= s_last; ++s) m = fmaxf(m, rec(s)[0]);
-  float l = 0.f, acc[PER_LANE];
+  // Portions are read CH at a time, every load of a group issued before any
+  // is used (one memory latency per group instead of two per portion).  The
+  // merge keeps the portion order: a group's max first, then l and o scaled
+  // by 2^(m_s - m) and added in order; a later group first rescales what came
+  // before.  With at most CH portions this is exactly the two-pass merge
+  // (max over all, then the ordered sums).
+  constexpr int CH = 8;
+  float m = kNegInf, l = 0.f, acc[PER_LANE];
 #pragma unroll
   for (int e = 0; e < PER_LANE; ++e) acc[e] = 0.f;
-  for (int s = s_first; s <= s_last; ++s) {
-    const float* r = rec(s);
-    const float wgt = fast_exp2(r[0] - m);
-    l += r[1] * wgt;
+  for (int s0 = s_first; s0 <= s_last; s0 += CH) {
+    float ms[CH], ls[CH], os[CH][PER_LANE];
 #pragma unroll
-    for (int e = 0; e < PER_LANE; ++e) acc[e] += r[4 + lane + 64 * e] * wgt;
+    for (int j = 0; j < CH; ++j) {
+      const bool live = s0 + j <= s_last;
+      const float* r = rec(live ? s0 + j : s_first);
+      ms[j] = live ? r[0] : kNegInf;
+      ls[j] = live ? r[1] : 0.f;
+#pragma unroll
+      for (int e = 0; e < PER_LANE; ++e) os[j][e] = live ? r[4 + lane + 64 * e] : 0.f;
+    }
+    float mg = m;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) mg = fmaxf(mg, ms[j]);
+    if (s0 != s_first) {
+      const float alpha = fast_exp2(m - mg);
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < PER_LANE; ++e) acc[e] *= alpha;
+    }
+    m = mg;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      if (s0 + j > s_last) break;
+      const float wgt = fast_exp2(ms[j] - m);
+      l += ls[j] * wgt;
+#pragma unroll
+      for (int e = 0; e < PER_LANE; ++e) acc[e] += os[j][e] * wgt;
+    }
   }
   const float inv = 1.0f / l;
   bf16* dst = out + static_cast<size_t>(bh) * D;
