@@ -217,6 +217,36 @@ def _timed_region(runner, steps: int) -> float:
     return start.elapsed_time(stop) / steps
 
 
+def single_step_ms(runner, reps: int, evict: bool) -> float:
+    """Mean time of one step run alone (synchronised before and after, its own
+    events).  With `evict`, each step follows a 1 GiB read, outside the
+    events, that leaves none of the step's data in the 256 MB last-level
+    cache; without it the same protocol measures the warm step, so that the
+    two differ by the cache alone."""
+    torch = runner.torch
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    total = 0.0
+    for _ in range(reps):
+        if evict:
+            scratch.sum()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record()
+        runner.step()
+        stop.record()
+        torch.cuda.synchronize()
+        total += start.elapsed_time(stop)
+    del scratch
+    return total / reps
+
+
+def cache_effect(runner, reps: int = 10) -> dict:
+    warm = single_step_ms(runner, reps, False)
+    cold = single_step_ms(runner, reps, True)
+    return {"ms_single_step_warm": warm, "ms_single_step_after_1gib_read": cold}
+
+
 def time_steps(runner, steps: int, warmup: int):
     """Warm-up steps, then two timed regions of `steps` steps each.
 
@@ -405,6 +435,9 @@ def main(argv=None):
         side["kernel1_prefill"] = roofline_for("qknorm_rope_kv_prefill", kernels, F, B, args.workload,
                                                {"qknorm_rope_kv_prefill": k1})
 
+    # Single steps, warm and after a 1 GiB read that leaves none of their data in the last-level cache.
+    side["last_level_cache"] = cache_effect(runner)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, F, B)
@@ -419,6 +452,10 @@ def main(argv=None):
             extra[name] = {"ms_per_call": ems, "kernel": rf,
                            "call_rate": (eF / (ems / 1e3) / 1e12) if eF else (eB / (ems / 1e3) / 1e9),
                            "call_rate_unit": "TFLOP/s" if eF else "GB/s"}
+            if not eF:  # decode: the same call with nothing of its K/V left in the last-level cache
+                ce = cache_effect(er)
+                ce["call_rate_after_1gib_read"] = eB / (ce["ms_single_step_after_1gib_read"] / 1e3) / 1e9
+                extra[name]["last_level_cache"] = ce
             del er, ew
             torch.cuda.empty_cache()
         # Steps next to the attention layer, each against the HBM roofline.
