@@ -104,7 +104,9 @@ constexpr int NSLOT = 3;  // LDS tile slots
 // factor 1.02 covers the bf16 roundings of q~' and k~ and the fp32
 // arithmetic before them.  Every wavefront of both prefill kernels reduces
 // the same weights the same way (max is exact, one rounded product), so the
-// answer is the same everywhere.  A NaN weight fails the test.
+// answer is the same everywhere.  An infinite weight fails the test; a NaN
+// one is passed over by the max (IEEE maxNum), and then every score of the
+// head is NaN on either path.
 // The test is split in two so that the kernel that runs can issue its first
 // loads between the weight loads and the decision.
 struct WeightMax {
