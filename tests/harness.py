@@ -40,10 +40,14 @@ def layer_kw(heads) -> dict:
 
 
 def run_prefill(p) -> Dict[str, torch.Tensor]:
-    """HIP prefill on PrefillInputs (device tensors); caches are updated in place."""
+    """HIP prefill on PrefillInputs (device tensors); caches are updated in place.  `out` starts as NaN, so a
+    row that no kernel wrote fails any comparison."""
     cfg = cfg_of(p.heads, p.qkv.dtype)
+    h = p.heads
+    out = torch.full((p.num_tokens, h.num_q_heads * h.head_dim), float("nan"), dtype=p.qkv.dtype,
+                     device=p.qkv.device)
     out, ws = da.prefill(cfg, p.qkv, p.q_norm_weight, p.k_norm_weight, p.positions, p.cu_seqlens,
-                         p.max_seqlen, p.k_cache, p.v_cache)
+                         p.max_seqlen, p.k_cache, p.v_cache, out=out)
     torch.cuda.synchronize()
     n, h = p.num_tokens, p.heads
     if p.qkv.dtype != torch.float32:  # bf16: Q is normalised and rotated inside the attention kernel

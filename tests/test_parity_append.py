@@ -17,9 +17,12 @@ DEV = "cuda:0"
 
 
 def run_append(a):
+    """`out` starts as NaN, so a row that no kernel wrote fails the comparison."""
     cfg = cfg_of(a.heads, a.qkv.dtype)
+    h = a.heads
+    out = torch.full((a.num_tokens, h.num_q_heads * h.head_dim), float("nan"), dtype=a.qkv.dtype, device=DEV)
     out, ws = da.prefill_append(cfg, a.qkv, a.q_norm_weight, a.k_norm_weight, a.positions, a.cu_seqlens,
-                                a.cache_lens, a.max_seqlen, a.max_cache_len, a.k_cache, a.v_cache)
+                                a.cache_lens, a.max_seqlen, a.max_cache_len, a.k_cache, a.v_cache, out=out)
     torch.cuda.synchronize()
     return out
 
