@@ -94,3 +94,35 @@ def test_decode_sweep(i, dtype):
         d.positions = pos
     note(_label("decode", i, h, f"cache lengths {lens}"))
     _check_decode(d)
+
+
+@pytest.mark.parametrize("i", range(CASES))
+def test_prefill_sweep_running_max_kernel(i):
+    """The same kind of random cases in bf16, with one element of each norm weight raised to 2.5 so that
+    max|w_q| max|w_k| exceeds the bound under which the unshifted kernel runs: a plain prefill then goes through
+    the running-max kernel, for every query-head grouping it is instantiated for.  The outlier moves only the
+    bound, not the typical score."""
+    import numpy as np
+    rng = random.Random(3000 + i)
+    h = _heads(rng)
+    lens = [rng.choice([0, 1, rng.randint(2, 64), rng.randint(65, 300)]) for _ in range(rng.randint(1, 6))]
+    if sum(lens) == 0:
+        lens[0] = 1
+    p = make_prefill_inputs(h, lens, seed=rng.randrange(1 << 20), dtype=torch.bfloat16, device=DEV,
+                            capacity=max(lens) + rng.randint(0, 9))
+    d = h.head_dim
+    for w, at, sign in ((p.q_norm_weight, rng.randrange(d), 1.0), (p.k_norm_weight, rng.randrange(d), -1.0)):
+        w[at] = sign * 2.5
+    assert float(p.q_norm_weight.abs().max()) * float(p.k_norm_weight.abs().max()) > 4.1
+    note(_label("prefill (running max)", i, h, f"lens {lens}"))
+    k0, v0 = p.k_cache.clone(), p.v_cache.clone()
+    got = run_prefill(p)
+    ref = oracle_prefill(p)
+    assert_close(f64(got["out"]), ref["out"], tol_for(torch.bfloat16), "out")
+    # K cache: the bound plus half a bf16 step of the value (the outlier element of k~ can pass 8).
+    cu = p.cu_seqlens.cpu().tolist()
+    for r in range(p.num_seqs):
+        lo, hi = cu[r], cu[r + 1]
+        got_k = f64(p.k_cache[r, :, : hi - lo])
+        want = np.transpose(ref["k_tilde"][lo:hi], (1, 0, 2))
+        assert np.all(np.abs(got_k - want) <= 2e-2 + np.abs(want) * 2.0**-8), f"K cache request {r}"
