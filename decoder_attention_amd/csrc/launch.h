@@ -92,7 +92,7 @@ inline int decode_num_splits(int max_cache_len) {
 // (m, l, pad, pad, o[D]) fp32 per (unit, wavefront) that meet, at slot
 // unit + wavefront of [N + W, GW, D + 4].
 constexpr int kDecodeStepKeys = 32;
-constexpr int kDecodeWaves = 2048;          // 256 CUs x 2 workgroups x 4 wavefronts
+constexpr int kDecodeWaves = 768;  // 192 workgroups of 4: faster than 512, 1024, 1536 or 2048 on both decode workloads
 constexpr int kDecodeMinStepsPerWave = 8;
 
 // Query heads per wavefront on the matrix-core path: the whole group if it

@@ -55,7 +55,7 @@ def test_workspace_bytes():
     # bf16 decode: q~, then the int32 step plan [T, per, S0[0..N], first[0..W)]
     # over N = b * Hkv units (G = 4 heads per tile), then fp32 records
     # (m, l, pad, pad, o[D]) for N + W (unit, wavefront) slots of 4 heads.
-    b, L, W = 3, 2047, 2048
+    b, L, W = 3, 2047, 768
     n_units = b * 8
     q_bytes = up(b * 32 * 128 * 2)
     plan_bytes = up((3 + n_units + W) * 4)
