@@ -28,6 +28,7 @@ from .binding import (  # noqa: F401
     qknorm_rope_attn_prefill,
     qknorm_rope_attn_prefill_append,
     qknorm_rope_attn_decode,
+    qknorm_rope_attn_mixed_step,
     qknorm_rope_attn_workspace_bytes,
     qknorm_rope_attn_status_string,
     qknorm_rope_attn_last_hip_error,
@@ -108,6 +109,37 @@ def decode(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cache_
                                      workspace.numel() * workspace.element_size(), stream)
     check(status, "qknorm_rope_attn_decode")
     return out, workspace
+
+
+def mixed_step(cfg: QkraConfig, q_norm_weight, k_norm_weight, prefill_qkv, prefill_positions, cu_seqlens,
+               max_seqlen: int, prefill_k_cache, prefill_v_cache, decode_qkv, decode_positions, cache_lens,
+               max_cache_len: int, decode_k_cache, decode_v_cache, prefill_out=None, prefill_workspace=None,
+               decode_out=None, decode_workspace=None, stream=None):
+    """Runs ``qknorm_rope_attn_mixed_step``; returns (prefill out, decode out, prefill workspace, decode workspace)."""
+    import torch
+
+    _require_device(prefill_qkv, q_norm_weight, k_norm_weight, prefill_positions, cu_seqlens, prefill_k_cache,
+                    prefill_v_cache, decode_qkv, decode_positions, cache_lens, decode_k_cache, decode_v_cache)
+    n, b = prefill_qkv.shape[0], decode_qkv.shape[0]
+    width = cfg.num_q_heads * cfg.head_dim
+    if prefill_out is None:
+        prefill_out = torch.empty((n, width), dtype=prefill_qkv.dtype, device=prefill_qkv.device)
+    if decode_out is None:
+        decode_out = torch.empty((b, width), dtype=decode_qkv.dtype, device=decode_qkv.device)
+    if prefill_workspace is None:
+        need = qknorm_rope_attn_workspace_bytes(cfg, QKRA_MODE_PREFILL, n, max_seqlen)
+        prefill_workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=prefill_qkv.device)
+    if decode_workspace is None:
+        need = qknorm_rope_attn_workspace_bytes(cfg, QKRA_MODE_DECODE, b, max_cache_len)
+        decode_workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=decode_qkv.device)
+    status = qknorm_rope_attn_mixed_step(
+        cfg, q_norm_weight, k_norm_weight, prefill_qkv, prefill_positions, cu_seqlens, n, cu_seqlens.shape[0] - 1,
+        max_seqlen, prefill_k_cache, prefill_v_cache, prefill_k_cache.shape[2], prefill_out, prefill_workspace,
+        prefill_workspace.numel() * prefill_workspace.element_size(), decode_qkv, decode_positions, cache_lens, b,
+        max_cache_len, decode_k_cache, decode_v_cache, decode_k_cache.shape[2], decode_out, decode_workspace,
+        decode_workspace.numel() * decode_workspace.element_size(), stream)
+    check(status, "qknorm_rope_attn_mixed_step")
+    return prefill_out, decode_out, prefill_workspace, decode_workspace
 
 
 def _dtype_code(t):

@@ -64,6 +64,8 @@ _SIGNATURES = {
                                                _I32, _P, _P, _I32, _P, _P, _SZ, _P]),
     "qknorm_rope_attn_decode": (_I32, [ctypes.POINTER(QkraConfig), _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32,
                                        _P, _P, _SZ, _P]),
+    "qknorm_rope_attn_mixed_step": (_I32, [ctypes.POINTER(QkraConfig), _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P,
+                                           _I32, _P, _P, _SZ, _P, _P, _P, _I32, _I32, _P, _P, _I32, _P, _P, _SZ, _P]),
     "qknorm_rope_attn_workspace_bytes": (_SZ, [ctypes.POINTER(QkraConfig), _I32, _I32, _I32]),
     "qknorm_rope_attn_status_string": (ctypes.c_char_p, [_I32]),
     "qknorm_rope_attn_last_hip_error": (_I32, []),
@@ -147,6 +149,22 @@ def qknorm_rope_attn_prefill_append(cfg: QkraConfig, qkv, q_norm_weight, k_norm_
         ctypes.byref(cfg), _ptr(qkv), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(positions), _ptr(cu_seqlens),
         _ptr(cache_lens), int(num_tokens), int(num_seqs), int(max_seqlen), int(max_cache_len), _ptr(k_cache),
         _ptr(v_cache), int(cache_capacity), _ptr(out), _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def qknorm_rope_attn_mixed_step(cfg: QkraConfig, q_norm_weight, k_norm_weight, prefill_qkv, prefill_positions,
+                                cu_seqlens, num_tokens: int, num_prefill_seqs: int, max_seqlen: int, prefill_k_cache,
+                                prefill_v_cache, prefill_cache_capacity: int, prefill_out, prefill_workspace,
+                                prefill_workspace_bytes: int, decode_qkv, decode_positions, cache_lens,
+                                num_decode_seqs: int, max_cache_len: int, decode_k_cache, decode_v_cache,
+                                decode_cache_capacity: int, decode_out, decode_workspace, decode_workspace_bytes: int,
+                                stream=None) -> int:
+    return lib().qknorm_rope_attn_mixed_step(
+        ctypes.byref(cfg), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(prefill_qkv), _ptr(prefill_positions),
+        _ptr(cu_seqlens), int(num_tokens), int(num_prefill_seqs), int(max_seqlen), _ptr(prefill_k_cache),
+        _ptr(prefill_v_cache), int(prefill_cache_capacity), _ptr(prefill_out), _ptr(prefill_workspace),
+        int(prefill_workspace_bytes), _ptr(decode_qkv), _ptr(decode_positions), _ptr(cache_lens), int(num_decode_seqs),
+        int(max_cache_len), _ptr(decode_k_cache), _ptr(decode_v_cache), int(decode_cache_capacity), _ptr(decode_out),
+        _ptr(decode_workspace), int(decode_workspace_bytes), _stream(stream))
 
 
 def qknorm_rope_attn_decode(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cache_lens,

@@ -182,11 +182,17 @@ namespace {
 
 // Prefill of packed requests onto caches holding cache_lens[r] entries each
 // (cache_lens null: empty caches, max_cache_len 0).
+// A bf16 prefill whose attention the fused step runs (qknorm_rope_attn_mixed_step).
+struct DeferredPrefill {
+  PrefillAttnArgs args{};
+  bool set = false;
+};
+
 int32_t prefill_impl(const qkra_config* cfg, const void* qkv, const void* q_norm_weight, const void* k_norm_weight,
                      const int32_t* positions, const int32_t* cu_seqlens, const int32_t* cache_lens,
                      int32_t num_tokens, int32_t num_seqs, int32_t max_seqlen, int32_t max_cache_len,
                      void* k_cache, void* v_cache, int32_t cache_capacity, void* out, void* workspace,
-                     size_t workspace_bytes, void* hip_stream) {
+                     size_t workspace_bytes, void* hip_stream, DeferredPrefill* defer = nullptr) {
   const int32_t cs = check_config(cfg);
   if (cs != QKRA_OK) return cs;
   if (num_tokens < 0 || num_seqs < 0 || max_seqlen < 0 || max_cache_len < 0 || cache_capacity < 0)
@@ -267,6 +273,11 @@ int32_t prefill_impl(const qkra_config* cfg, const void* qkv, const void* q_norm
   pa.num_seqs = num_seqs;
   pa.max_seqlen = max_seqlen;
   pa.scale_log2 = softmax_scale_log2(cfg->head_dim);
+  if (defer && cfg->dtype == QKRA_BF16 && cache_lens == nullptr) {  // attention runs in the fused step
+    defer->args = pa;
+    defer->set = true;
+    return QKRA_OK;
+  }
   if (cfg->dtype == QKRA_BF16) {
     err = timed(kKernelPrefillMfma, stream, [&] { return launch_prefill_attn_bf16(pa, true, stream); });
     if (err == hipSuccess)
@@ -303,11 +314,15 @@ QKRA_API int32_t qknorm_rope_attn_prefill_append(const qkra_config* cfg, const v
                       workspace_bytes, hip_stream);
 }
 
-QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv, const void* q_norm_weight,
-                                         const void* k_norm_weight, const int32_t* positions,
-                                         const int32_t* cache_lens, int32_t num_seqs, int32_t max_cache_len,
-                                         void* k_cache, void* v_cache, int32_t cache_capacity, void* out,
-                                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+namespace {
+
+// The decode call.  validate_only: the argument checks alone (nothing is
+// enqueued).  fused: a bf16 prefill whose attention runs in the same launch
+// as the decode split (the fused step), then its running-max kernel.
+int32_t decode_impl(const qkra_config* cfg, const void* qkv, const void* q_norm_weight, const void* k_norm_weight,
+                    const int32_t* positions, const int32_t* cache_lens, int32_t num_seqs, int32_t max_cache_len,
+                    void* k_cache, void* v_cache, int32_t cache_capacity, void* out, void* workspace,
+                    size_t workspace_bytes, void* hip_stream, bool validate_only, const PrefillAttnArgs* fused) {
   const int32_t cs = check_config(cfg);
   if (cs != QKRA_OK) return cs;
   if (num_seqs < 0 || max_cache_len < 0 || cache_capacity < 0) return QKRA_ERR_INVALID_ARGUMENT;
@@ -341,6 +356,7 @@ QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv
   if (overlap(r_out, r_k) || overlap(r_out, r_v) || overlap(r_out, r_ws) || overlap(r_k, r_v) ||
       overlap(r_k, r_ws) || overlap(r_v, r_ws))
     return QKRA_ERR_ALIASING;
+  if (validate_only) return QKRA_OK;
 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   QkNormRopeArgs ka{};
@@ -390,7 +406,13 @@ QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv
     da.partials = reinterpret_cast<float*>(ws + decode_plan_bytes(cfg, num_seqs));
     da.num_units = static_cast<int>(decode_units(cfg, num_seqs));
     da.heads_per_wave = decode_heads_per_wave(cfg->num_q_heads / cfg->num_kv_heads);
-    err = timed(kKernelDecodeSplit, stream, [&] { return launch_decode_mfma(da, stream); });
+    if (fused) {
+      err = timed(kKernelFusedStep, stream, [&] { return launch_fused_step(*fused, da, stream); });
+      if (err != hipSuccess) return hip_status(err);
+      err = timed(kKernelPrefillMfmaShifted, stream, [&] { return launch_prefill_attn_bf16(*fused, false, stream); });
+    } else {
+      err = timed(kKernelDecodeSplit, stream, [&] { return launch_decode_mfma(da, stream); });
+    }
     if (err != hipSuccess) return hip_status(err);
     err = timed(kKernelDecodeCombine, stream, [&] { return launch_decode_mfma_combine(da, stream); });
     return hip_status(err);
@@ -401,6 +423,68 @@ QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv
   if (err != hipSuccess) return hip_status(err);
   err = timed(kKernelDecodeCombine, stream, [&] { return launch_decode_combine(da, stream); });
   return hip_status(err);
+}
+
+}  // namespace
+
+QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv, const void* q_norm_weight,
+                                         const void* k_norm_weight, const int32_t* positions,
+                                         const int32_t* cache_lens, int32_t num_seqs, int32_t max_cache_len,
+                                         void* k_cache, void* v_cache, int32_t cache_capacity, void* out,
+                                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return decode_impl(cfg, qkv, q_norm_weight, k_norm_weight, positions, cache_lens, num_seqs, max_cache_len, k_cache,
+                     v_cache, cache_capacity, out, workspace, workspace_bytes, hip_stream, false, nullptr);
+}
+
+QKRA_API int32_t qknorm_rope_attn_mixed_step(
+    const qkra_config* cfg, const void* q_norm_weight, const void* k_norm_weight,
+    const void* prefill_qkv, const int32_t* prefill_positions, const int32_t* cu_seqlens, int32_t num_tokens,
+    int32_t num_prefill_seqs, int32_t max_seqlen, void* prefill_k_cache, void* prefill_v_cache,
+    int32_t prefill_cache_capacity, void* prefill_out, void* prefill_workspace, size_t prefill_workspace_bytes,
+    const void* decode_qkv, const int32_t* decode_positions, const int32_t* cache_lens, int32_t num_decode_seqs,
+    int32_t max_cache_len, void* decode_k_cache, void* decode_v_cache, int32_t decode_cache_capacity,
+    void* decode_out, void* decode_workspace, size_t decode_workspace_bytes, void* hip_stream) {
+  // Both halves' checks come first, so that nothing is enqueued for bad arguments.
+  int32_t st = decode_impl(cfg, decode_qkv, q_norm_weight, k_norm_weight, decode_positions, cache_lens,
+                           num_decode_seqs, max_cache_len, decode_k_cache, decode_v_cache, decode_cache_capacity,
+                           decode_out, decode_workspace, decode_workspace_bytes, hip_stream, true, nullptr);
+  if (st != QKRA_OK) return st;
+  if (num_tokens < 0 || num_prefill_seqs < 0) return QKRA_ERR_INVALID_ARGUMENT;
+  // The halves run at the same time: what one writes must not overlap anything the other touches.
+  if (num_tokens > 0 && num_decode_seqs > 0) {
+    const size_t es = elem_size(cfg->dtype);
+    const size_t hq = cfg->num_q_heads, hkv = cfg->num_kv_heads, d = cfg->head_dim;
+    const size_t pcache = static_cast<size_t>(num_prefill_seqs) * hkv * static_cast<size_t>(prefill_cache_capacity) * d * es;
+    const size_t dcache = static_cast<size_t>(num_decode_seqs) * hkv * static_cast<size_t>(decode_cache_capacity) * d * es;
+    const Range p_w[] = {range_of(prefill_out, num_tokens * hq * d * es), range_of(prefill_k_cache, pcache),
+                         range_of(prefill_v_cache, pcache), range_of(prefill_workspace, prefill_workspace_bytes)};
+    const Range d_w[] = {range_of(decode_out, num_decode_seqs * hq * d * es), range_of(decode_k_cache, dcache),
+                         range_of(decode_v_cache, dcache), range_of(decode_workspace, decode_workspace_bytes)};
+    const Range p_r[] = {range_of(prefill_qkv, num_tokens * (hq + 2 * hkv) * d * es),
+                         range_of(prefill_positions, num_tokens * 4ull), range_of(cu_seqlens, (num_prefill_seqs + 1ull) * 4)};
+    const Range d_r[] = {range_of(decode_qkv, num_decode_seqs * (hq + 2 * hkv) * d * es),
+                         range_of(decode_positions, num_decode_seqs * 4ull), range_of(cache_lens, num_decode_seqs * 4ull)};
+    for (const Range& w : p_w) {
+      for (const Range& x : d_w)
+        if (overlap(w, x)) return QKRA_ERR_ALIASING;
+      for (const Range& x : d_r)
+        if (overlap(w, x)) return QKRA_ERR_ALIASING;
+    }
+    for (const Range& w : d_w)
+      for (const Range& x : p_r)
+        if (overlap(w, x)) return QKRA_ERR_ALIASING;
+  }
+  const bool fuse = cfg->dtype == QKRA_BF16 && num_tokens > 0 && num_decode_seqs > 0 &&
+                    fused_step_supported(cfg->head_dim, cfg->num_q_heads / cfg->num_kv_heads);
+  DeferredPrefill deferred;
+  st = prefill_impl(cfg, prefill_qkv, q_norm_weight, k_norm_weight, prefill_positions, cu_seqlens, nullptr, num_tokens,
+                    num_prefill_seqs, max_seqlen, 0, prefill_k_cache, prefill_v_cache, prefill_cache_capacity,
+                    prefill_out, prefill_workspace, prefill_workspace_bytes, hip_stream, fuse ? &deferred : nullptr);
+  if (st != QKRA_OK) return st;
+  return decode_impl(cfg, decode_qkv, q_norm_weight, k_norm_weight, decode_positions, cache_lens, num_decode_seqs,
+                     max_cache_len, decode_k_cache, decode_v_cache, decode_cache_capacity, decode_out,
+                     decode_workspace, decode_workspace_bytes, hip_stream, false,
+                     deferred.set ? &deferred.args : nullptr);
 }
 
 // ---- steps next to the attention layer ----------------------------------------
@@ -547,6 +631,7 @@ QKRA_API const char* qknorm_rope_attn_kernel_name(int32_t kernel_id) {
     case kKernelQkNormRopeDecode: return "qknorm_rope_kv_decode";
     case kKernelPrefillMfma: return "prefill_attn_mfma_bf16";
     case kKernelPrefillMfmaShifted: return "prefill_attn_mfma_bf16_shifted";
+    case kKernelFusedStep: return "fused_step_attn";
     case kKernelPrefillFp32: return "prefill_attn_fp32";
     case kKernelDecodeSplit: return "decode_attn_split";
     case kKernelDecodeCombine: return "decode_attn_combine";

@@ -20,7 +20,8 @@ enum KernelId : int {
   kKernelArgmaxPartial = 8,
   kKernelArgmaxFinal = 9,
   kKernelPrefillMfmaShifted = 10,
-  kNumKernels = 11,
+  kKernelFusedStep = 11,
+  kNumKernels = 12,
 };
 
 // Kernel 1: per token row, RMSNorm + RoPE of the Q and K heads; q~ to
@@ -72,6 +73,15 @@ struct PrefillAttnArgs {
 // running max (it returns at once where the other runs).
 hipError_t launch_prefill_attn_bf16(const PrefillAttnArgs& a, bool unshifted, hipStream_t stream);
 hipError_t launch_prefill_attn_fp32(const PrefillAttnArgs& a, hipStream_t stream);
+
+struct DecodeAttnArgs;
+// The fused step (bf16): one launch whose first workgroups run the decode
+// split over the plan built for kDecodeWaves wavefronts and whose other
+// workgroups run the unshifted prefill's work items; supported for D = 64
+// or 128 and G in {1, 2, 4, 8, 16} (fused_step_supported).  The running-max
+// prefill kernel and the decode combine still follow it.
+bool fused_step_supported(int head_dim, int group);
+hipError_t launch_fused_step(const PrefillAttnArgs& a, const DecodeAttnArgs& d, hipStream_t stream);
 
 // Kernels 3a/3b: split-KV decode attention and the log-sum-exp combine.
 //

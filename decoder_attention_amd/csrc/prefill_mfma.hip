@@ -60,6 +60,7 @@
 //    instead made a chunked prefill onto long caches fetch its history from
 //    HBM about 25 times); within a request the heaviest tiles go first.
 
+#include "decode_body.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -95,6 +96,24 @@ __device__ __forceinline__ float half_wave_max(float x) {
 }
 
 constexpr int NSLOT = 3;  // LDS tile slots
+
+// The decode role of the fused step kernel: the first `wgs` workgroups each
+// run kFusedDecodeWavesPerWg wavefronts of the decode split (decode_body.h)
+// over the plan built for kDecodeWaves wavefronts, with their K/V tiles in
+// this kernel's LDS slots; the other workgroups run prefill work items.
+constexpr int kFusedDecodeWavesPerWg = 6;
+constexpr int kFusedDecodeWgs = kDecodeWaves / kFusedDecodeWavesPerWg;
+static_assert(kDecodeWaves % kFusedDecodeWavesPerWg == 0 && kFusedDecodeWgs % 8 == 0,
+              "the decode workgroups keep the prefill items' XCD mapping");
+struct DecodeRole {
+  const bf16* q;
+  const bf16* k_cache;
+  const bf16* v_cache;
+  const int32_t* cache_lens;
+  const int32_t* plan;
+  float* partials;
+  int cache_capacity, chunks_per_kv, num_units, wgs;
+};
 
 // Whether p = 2^s may be taken without a shift: a request with no cached
 // history (every key it reads is written by this call with k_norm_weight)
@@ -140,7 +159,7 @@ __device__ __forceinline__ bool scores_bounded(WeightMax w, int past, float limi
 // slowed both.  Every call launches both kernels over the same grid; each
 // workgroup of the one whose path its request and the weights do not select
 // returns at once.
-template <int D, int HC, bool kBounded>
+template <int D, int HC, bool kBounded, int kDecGW = 0>
 __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ q_norm_weight, const bf16* __restrict__ k_norm_weight,
     const float* __restrict__ rope_table,
@@ -148,7 +167,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ past_lens, bf16* __restrict__ out,
     int num_q_heads, int num_kv_heads,
     int cache_capacity, int num_seqs, int tiles_per_seq, int chunks_per_kv, int num_items,
-    float rms_eps, float scale_log2, float bound_limit) {
+    float rms_eps, float scale_log2, float bound_limit, DecodeRole dec) {
   constexpr int TBN = 8 / HC;       // token blocks (of 32) per workgroup
   constexpr int TM = 32 * TBN;      // tokens per workgroup
   constexpr int DS = D / 16;        // k-steps over D for the scores
@@ -164,8 +183,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   __shared__ __attribute__((aligned(16))) bf16 sV[NSLOT][D * VST];
 
   // ---- work item (XCD-aware remap; per request, heaviest tiles first) -------
-  const int nb = gridDim.x;  // a multiple of 8
-  const int logical = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
+  int bid = blockIdx.x;
+  int nb = gridDim.x;  // a multiple of 8
+  if constexpr (kDecGW > 0) {
+    if (bid < dec.wgs) {  // decode role (the fused step): its wavefronts' tiles in the K and V slots
+      const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      constexpr int DT = kDecodeStepKeys * (D + 8);  // elements of one decode tile
+      static_assert(3 * 2 * DT <= NSLOT * BN * KST && 3 * 2 * DT <= NSLOT * D * VST &&
+                        kFusedDecodeWavesPerWg == 6 && NWAVES >= 6,
+                    "three decode wavefronts' K and V tiles fit in each of the K and V slot arrays");
+      if (wv < kFusedDecodeWavesPerWg) {
+        bf16* base = wv < 3 ? &sK[0][0] + wv * 2 * DT : &sV[0][0] + (wv - 3) * 2 * DT;
+        dbody::decode_wave<D, kDecGW>(base, base + DT, bid * kFusedDecodeWavesPerWg + wv, dec.q, dec.k_cache,
+                                      dec.v_cache, dec.cache_lens, dec.plan, dec.partials, num_q_heads, num_kv_heads,
+                                      dec.cache_capacity, dec.chunks_per_kv, dec.num_units, scale_log2);
+      }
+      return;
+    }
+    bid -= dec.wgs;  // a multiple of 8: the XCD mapping below is unchanged
+    nb -= dec.wgs;
+  }
+  const int logical = (bid & 7) * (nb >> 3) + (bid >> 3);
   if (logical >= num_items) return;
   const int per_chunk = tiles_per_seq * num_seqs;
   const int chunk = logical / per_chunk;
@@ -629,7 +667,7 @@ hipError_t launch_typed(const PrefillAttnArgs& a, hipStream_t stream) {
                      static_cast<const bf16*>(a.k_cache),
                      static_cast<const bf16*>(a.v_cache), a.cu_seqlens, a.past_lens, static_cast<bf16*>(a.out),
                      a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.num_seqs, tiles, chunks_per_kv,
-                     static_cast<int>(items), a.rms_eps, a.scale_log2, bound_limit);
+                     static_cast<int>(items), a.rms_eps, a.scale_log2, bound_limit, DecodeRole{});
   return hipGetLastError();
 }
 
@@ -643,6 +681,54 @@ hipError_t launch_dim(const PrefillAttnArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+namespace {
+
+template <int D, int G>
+hipError_t launch_fused_typed(const PrefillAttnArgs& a, const DecodeAttnArgs& d, hipStream_t stream) {
+  constexpr int HC = G < 8 ? G : 8;
+  constexpr int TM = 32 * (8 / HC);
+  const int tiles = (a.max_seqlen + TM - 1) / TM;
+  const int chunks_per_kv = G / HC;
+  const long long items = static_cast<long long>(a.num_kv_heads) * chunks_per_kv * a.num_seqs * tiles;
+  const long long grid = kFusedDecodeWgs + (items + 7) / 8 * 8;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const float bound_limit = BOUND_LOG2 / (1.02f * static_cast<float>(D) * a.scale_log2);
+  const DecodeRole dec{static_cast<const bf16*>(d.q), static_cast<const bf16*>(d.k_cache),
+                       static_cast<const bf16*>(d.v_cache), d.cache_lens, d.plan, d.partials, d.cache_capacity,
+                       1, d.num_units, kFusedDecodeWgs};
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, HC, true, G>), dim3(static_cast<unsigned>(grid)), dim3(NTHREADS), 0,
+                     stream, static_cast<const bf16*>(a.qkv), static_cast<const bf16*>(a.q_norm_weight),
+                     static_cast<const bf16*>(a.k_norm_weight), a.rope_table, static_cast<const bf16*>(a.k_cache),
+                     static_cast<const bf16*>(a.v_cache), a.cu_seqlens, a.past_lens, static_cast<bf16*>(a.out),
+                     a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.num_seqs, tiles, chunks_per_kv,
+                     static_cast<int>(items), a.rms_eps, a.scale_log2, bound_limit, dec);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_fused_dim(const PrefillAttnArgs& a, const DecodeAttnArgs& d, hipStream_t stream) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_fused_typed<D, 1>(a, d, stream);
+    case 2: return launch_fused_typed<D, 2>(a, d, stream);
+    case 4: return launch_fused_typed<D, 4>(a, d, stream);
+    case 8: return launch_fused_typed<D, 8>(a, d, stream);
+    case 16: return launch_fused_typed<D, 16>(a, d, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool fused_step_supported(int head_dim, int group) {
+  return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
+}
+
+hipError_t launch_fused_step(const PrefillAttnArgs& a, const DecodeAttnArgs& d, hipStream_t stream) {
+  if (a.head_dim == 128) return launch_fused_dim<128>(a, d, stream);
+  if (a.head_dim == 64) return launch_fused_dim<64>(a, d, stream);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_prefill_attn_bf16(const PrefillAttnArgs& a, bool unshifted, hipStream_t stream) {
   if (a.head_dim == 128) return unshifted ? launch_dim<128, true>(a, stream) : launch_dim<128, false>(a, stream);

@@ -186,6 +186,31 @@ QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv
                                          void* hip_stream);
 
 /*
+ * One serving step with both kinds of request: exactly what
+ * qknorm_rope_attn_prefill(prefill arguments) followed by
+ * qknorm_rope_attn_decode(decode arguments) on the same stream computes
+ * (the pages' prefill and decode stages, "Chapter 3 Forward Pass and
+ * Generation", sections 4.1-4.2, run as one packed step), with the same
+ * arguments, layouts, checks and status codes.  Both halves share cfg and
+ * the norm weights.  In bf16, with D = 64 or 128 and Hq / Hkv in
+ * {1, 2, 4, 8, 16}, the prefill attention and the decode split run in one
+ * launch: some workgroups stream the decode requests' caches while the rest
+ * run the prefill on the matrix cores.  Otherwise the two calls run in turn.
+ * Because the halves run at the same time, what one half writes (its out,
+ * caches and workspace) must not overlap anything the other half reads or
+ * writes: QKRA_ERR_ALIASING otherwise.  All arguments of both halves are
+ * checked before anything is enqueued.
+ */
+QKRA_API int32_t qknorm_rope_attn_mixed_step(
+    const qkra_config* cfg, const void* q_norm_weight, const void* k_norm_weight,
+    const void* prefill_qkv, const int32_t* prefill_positions, const int32_t* cu_seqlens, int32_t num_tokens,
+    int32_t num_prefill_seqs, int32_t max_seqlen, void* prefill_k_cache, void* prefill_v_cache,
+    int32_t prefill_cache_capacity, void* prefill_out, void* prefill_workspace, size_t prefill_workspace_bytes,
+    const void* decode_qkv, const int32_t* decode_positions, const int32_t* cache_lens, int32_t num_decode_seqs,
+    int32_t max_cache_len, void* decode_k_cache, void* decode_v_cache, int32_t decode_cache_capacity,
+    void* decode_out, void* decode_workspace, size_t decode_workspace_bytes, void* hip_stream);
+
+/*
  * Workspace size in bytes for a call (0 when the configuration is invalid).
  * mode QKRA_MODE_PREFILL: n = num_tokens, max_len = max_seqlen.
  * mode QKRA_MODE_DECODE:  n = num_seqs,   max_len = max_cache_len.

@@ -325,3 +325,49 @@ def test_argmax_argument_checks(over, status):
 
 def test_argmax_empty_batch_is_noop():
     assert call_argmax(argmax_args(num_rows=0, logits=None, out_index=None, workspace=None)) == da.QKRA_OK
+
+
+def mixed_args(**over):
+    """A prefill half at BASE and a decode half 1 GiB above it (fake device addresses: only the host checks run)."""
+    cfg = over.pop("cfg", da.make_config(32, 8, 128, da.QKRA_BF16))
+    g = 1024 * MB
+    a = dict(q_norm_weight=BASE + 64 * MB, k_norm_weight=BASE + 65 * MB,
+             p_qkv=BASE, p_positions=BASE + 66 * MB, cu_seqlens=BASE + 67 * MB, num_tokens=64, num_prefill_seqs=1,
+             max_seqlen=64, p_k=BASE + 100 * MB, p_v=BASE + 200 * MB, p_cap=64, p_out=BASE + 300 * MB,
+             p_ws=BASE + 400 * MB, p_ws_bytes=1 << 20,
+             d_qkv=BASE + g, d_positions=BASE + g + 66 * MB, cache_lens=BASE + g + 67 * MB, num_decode_seqs=4,
+             max_cache_len=100, d_k=BASE + g + 100 * MB, d_v=BASE + g + 200 * MB, d_cap=101, d_out=BASE + g + 300 * MB,
+             d_ws=BASE + g + 400 * MB, d_ws_bytes=16 * MB, stream=0)
+    a.update(over)
+    return cfg, a
+
+
+def call_mixed(cfg, a):
+    return da.qknorm_rope_attn_mixed_step(
+        cfg, a["q_norm_weight"], a["k_norm_weight"], a["p_qkv"], a["p_positions"], a["cu_seqlens"], a["num_tokens"],
+        a["num_prefill_seqs"], a["max_seqlen"], a["p_k"], a["p_v"], a["p_cap"], a["p_out"], a["p_ws"],
+        a["p_ws_bytes"], a["d_qkv"], a["d_positions"], a["cache_lens"], a["num_decode_seqs"], a["max_cache_len"],
+        a["d_k"], a["d_v"], a["d_cap"], a["d_out"], a["d_ws"], a["d_ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(d_cap=100), da.QKRA_ERR_CAPACITY),                                   # decode half: no room for the token
+    (dict(d_ws_bytes=1024), da.QKRA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(max_seqlen=65), da.QKRA_ERR_INVALID_ARGUMENT),                       # prefill half
+    (dict(p_cap=63), da.QKRA_ERR_CAPACITY),
+    (dict(num_tokens=-1), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(d_out=BASE + 300 * MB), da.QKRA_ERR_ALIASING),                       # both outputs in one buffer
+    (dict(d_k=BASE + 100 * MB + 4096), da.QKRA_ERR_ALIASING),                  # decode cache over the prefill cache
+    (dict(p_ws=BASE + 1024 * MB), da.QKRA_ERR_ALIASING),                       # prefill workspace over decode qkv
+    (dict(d_ws=BASE + 4096), da.QKRA_ERR_ALIASING),                            # decode workspace over prefill qkv
+])
+def test_mixed_step_argument_checks(over, status):
+    cfg, a = mixed_args(**over)
+    assert call_mixed(cfg, a) == status
+    assert da.qknorm_rope_attn_last_hip_error() == 0  # rejected before any launch
+
+
+def test_mixed_step_with_both_halves_empty_is_noop():
+    cfg, a = mixed_args(num_tokens=0, num_decode_seqs=0)
+    assert call_mixed(cfg, a) == da.QKRA_OK
+    assert da.qknorm_rope_attn_kernel_name(11) == "fused_step_attn"
