@@ -40,9 +40,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # includes): a counter summary applies only to the source it was taken on.
 _COMMON = ["decoder_attention_amd/csrc/device_common.h", "decoder_attention_amd/csrc/launch.h"]
 KERNEL_SOURCES = {
-    "prefill_attn_mfma_bf16": ["decoder_attention_amd/csrc/prefill_mfma.hip"] + _COMMON,
-    "prefill_attn_mfma_bf16_shifted": ["decoder_attention_amd/csrc/prefill_mfma.hip"] + _COMMON,
-    "decode_attn_split": ["decoder_attention_amd/csrc/decode_mfma.hip"] + _COMMON,
+    "prefill_attn_mfma_bf16": ["decoder_attention_amd/csrc/prefill_mfma.hip", "decoder_attention_amd/csrc/decode_body.h"]
+    + _COMMON,
+    "prefill_attn_mfma_bf16_shifted": ["decoder_attention_amd/csrc/prefill_mfma.hip",
+                                       "decoder_attention_amd/csrc/decode_body.h"] + _COMMON,
+    "fused_step_attn": ["decoder_attention_amd/csrc/prefill_mfma.hip", "decoder_attention_amd/csrc/decode_body.h"]
+    + _COMMON,
+    "decode_attn_split": ["decoder_attention_amd/csrc/decode_mfma.hip", "decoder_attention_amd/csrc/decode_body.h"]
+    + _COMMON,
     "decode_attn_combine": ["decoder_attention_amd/csrc/decode_mfma.hip"] + _COMMON,
     "qknorm_rope_kv_prefill": ["decoder_attention_amd/csrc/qknorm_rope.hip"] + _COMMON,
     "qknorm_rope_kv_decode": ["decoder_attention_amd/csrc/qknorm_rope.hip", "decoder_attention_amd/csrc/decode_plan.h"]
@@ -112,7 +117,7 @@ def measured_traffic(kernel: str, workload: str):
 class Runner:
     """Holds device inputs/outputs/workspaces of a workload and issues its step."""
 
-    def __init__(self, w, torch, da):
+    def __init__(self, w, torch, da, fused: bool = False):
         self.torch, self.da, self.w = torch, da, w
         self.calls = []
         if w.prefill is not None:
@@ -164,6 +169,13 @@ class Runner:
             ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=nt.logits.device)
             args = (da_dtype(da, nt.logits), nt.logits, b, v, nt.logits.stride(0), idx, ws, ws_bytes)
             self.calls.append((da.qknorm_rope_attn_argmax, args, (idx, ws)))
+
+        if fused and w.prefill is not None and w.decode is not None:
+            # The same step through qknorm_rope_attn_mixed_step: one call, the prefill attention and the decode
+            # split in one launch (both halves share the norm weights, as one layer's do).
+            (_, pa, pkeep), (_, dargs, dkeep) = self.calls[0], self.calls[1]
+            mixed = (pa[0], pa[2], pa[3]) + pa[1:2] + pa[4:] + dargs[1:2] + dargs[4:]
+            self.calls = [(da.qknorm_rope_attn_mixed_step, mixed, pkeep + dkeep)] + self.calls[2:]
 
     def step(self):
         for fn, args, _ in self.calls:
@@ -281,6 +293,15 @@ def roofline_for(name, kernels, F, B, workload, layer_bytes=None):
         achieved = F / avg_s / 1e12
         rf = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
               "frac": achieved / PEAK_MFMA_TFLOPS}
+    elif name == "fused_step_attn":
+        # One launch doing both halves: stated against HBM for the decode K/V it streams, with the MFMA share of
+        # the prefill FLOP it computes at the same time beside it; their sum is the step's ideal-time fraction.
+        achieved = B / avg_s / 1e9
+        rf = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+              "frac": achieved / PEAK_HBM_GBPS,
+              "mfma_share": {"achieved": F / avg_s / 1e12, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                             "frac": F / avg_s / 1e12 / PEAK_MFMA_TFLOPS},
+              "combined_frac": achieved / PEAK_HBM_GBPS + F / avg_s / 1e12 / PEAK_MFMA_TFLOPS}
     elif name == "decode_attn_split":
         achieved = B / avg_s / 1e9
         rf = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -386,20 +407,32 @@ def main(argv=None):
     da.lib()
     dev = "cuda:0"
 
-    def measure(name, steps, warmup):
+    def measure(name, steps, warmup, fused=False):
         w = build_workload(name, device=dev, parity=False)
-        runner = Runner(w, torch, da)
+        runner = Runner(w, torch, da, fused)
         ms, ms_events, kernels = time_steps(runner, steps, warmup)
         F, B = runner.work()
         return w, runner, ms, ms_events, kernels, F, B
 
-    w, runner, ms, ms_events, kernels, F, B = measure(args.workload, args.steps, args.warmup)
+    # The step as the library runs it best: a workload with both a prefill and a decode batch goes through
+    # qknorm_rope_attn_mixed_step.  The same step as two calls (prefill, then decode) is timed in the same run; its
+    # per-kernel figures fill `parts`.
+    w, runner, ms, ms_events, kernels, F, B = measure(args.workload, args.steps, args.warmup, fused=True)
     t = ms / 1e3
     value = 100.0 * (F / (PEAK_MFMA_TFLOPS * 1e12) + B / (PEAK_HBM_GBPS * 1e9)) / t
     per_kernel = {k: {"avg_ms": v[0] / v[1], "launches_per_step": v[1] / args.steps} for k, v in kernels.items()}
     dominant = max(kernels, key=lambda k: kernels[k][0])
     roof = roofline_for(dominant, kernels, F, B, args.workload)
+    fused_kernels = kernels
+    separate = None
+    if w.prefill is not None and w.decode is not None:
+        _, srunner, sms, _, kernels, _, _ = measure(args.workload, args.steps, args.warmup, fused=False)
+        separate = {"ms_per_step": sms, "value": 100.0 * (F / (PEAK_MFMA_TFLOPS * 1e12) + B / (PEAK_HBM_GBPS * 1e9))
+                    / (sms / 1e3), "kernels": {k: {"avg_ms": v[0] / v[1]} for k, v in kernels.items()}}
+        del srunner
     side = {}
+    if separate is not None:
+        side["separate_calls"] = separate
     pre_ms = sum(kernels[k][0] for k in ("qknorm_rope_kv_prefill",) + PREFILL_KERNELS if k in kernels)
     dec_ms = sum(kernels[k][0] for k in ("qknorm_rope_kv_decode", "decode_attn_split", "decode_attn_combine")
                  if k in kernels)
