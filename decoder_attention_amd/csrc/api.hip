@@ -174,7 +174,7 @@ QKRA_API const char* qknorm_rope_attn_status_string(int32_t status) {
 
 QKRA_API int32_t qknorm_rope_attn_last_hip_error(void) { return g_last_hip_error; }
 
-QKRA_API int32_t qknorm_rope_attn_version(void) { return 100; }
+QKRA_API int32_t qknorm_rope_attn_version(void) { return 200; }
 
 }  // extern "C"
 

@@ -37,7 +37,7 @@ def test_status_strings_and_version():
     for code in range(7):
         assert da.qknorm_rope_attn_status_string(code)
     assert da.qknorm_rope_attn_status_string(99) == "unknown status"
-    assert da.qknorm_rope_attn_version() == 100
+    assert da.qknorm_rope_attn_version() == 200  # 0.2.0: qknorm_rope_attn_mixed_step
     assert da.qknorm_rope_attn_last_hip_error() == 0
     assert da.qknorm_rope_attn_kernel_name(1) == "prefill_attn_mfma_bf16"
     assert da.qknorm_rope_attn_kernel_name(10) == "prefill_attn_mfma_bf16_shifted"
