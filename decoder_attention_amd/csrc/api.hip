@@ -15,6 +15,9 @@
 #include "launch.h"
 
 namespace qkra {
+
+thread_local LaunchEvents g_launch_events;
+
 namespace {
 
 thread_local int32_t g_last_hip_error = 0;
@@ -84,6 +87,10 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.l
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ---- per-kernel timing (benchmark instrumentation) ------------------------
+// Process-wide: a pool of events is created when timing is switched on
+// (qknorm_rope_attn_set_kernel_timing), so no call creates an event; a launch
+// that finds the pool empty runs untimed.
+constexpr int kTimingEvents = 8192;
 struct TimingRecord {
   int kernel;
   hipEvent_t start, stop;
@@ -92,40 +99,30 @@ std::mutex g_timing_mu;
 bool g_timing_enabled = false;
 std::vector<TimingRecord> g_timing_records;
 std::vector<hipEvent_t> g_event_pool;
-
-hipEvent_t take_event() {
-  if (!g_event_pool.empty()) {
-    hipEvent_t e = g_event_pool.back();
-    g_event_pool.pop_back();
-    return e;
-  }
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
-  return e;
-}
+int g_events_created = 0;
 
 template <typename Launch>
 hipError_t timed(int kernel, hipStream_t stream, Launch&& launch) {
-  bool enabled;
+  (void)stream;
+  hipEvent_t start = nullptr, stop = nullptr;
   {
     std::lock_guard<std::mutex> lock(g_timing_mu);
-    enabled = g_timing_enabled;
+    if (!g_timing_enabled || g_event_pool.size() < 2) return launch();
+    start = g_event_pool.back();
+    g_event_pool.pop_back();
+    stop = g_event_pool.back();
+    g_event_pool.pop_back();
   }
-  if (!enabled) return launch();
-  hipEvent_t start, stop;
-  {
-    std::lock_guard<std::mutex> lock(g_timing_mu);
-    start = take_event();
-    stop = take_event();
-  }
-  if (start == nullptr || stop == nullptr) return hipErrorOutOfMemory;
-  hipError_t err = hipEventRecord(start, stream);
-  if (err != hipSuccess) return err;
-  err = launch();
-  if (err != hipSuccess) return err;
-  err = hipEventRecord(stop, stream);
-  if (err != hipSuccess) return err;
+  g_launch_events = LaunchEvents{start, stop, false};
+  const hipError_t err = launch();
+  const bool used = g_launch_events.used;
+  g_launch_events = LaunchEvents{};
   std::lock_guard<std::mutex> lock(g_timing_mu);
+  if (err != hipSuccess || !used) {  // nothing launched (or the launch failed): the events go back
+    g_event_pool.push_back(start);
+    g_event_pool.push_back(stop);
+    return err;
+  }
   g_timing_records.push_back(TimingRecord{kernel, start, stop});
   return hipSuccess;
 }
@@ -456,10 +453,14 @@ QKRA_API int32_t qknorm_rope_attn_mixed_step(
     const size_t hq = cfg->num_q_heads, hkv = cfg->num_kv_heads, d = cfg->head_dim;
     const size_t pcache = static_cast<size_t>(num_prefill_seqs) * hkv * static_cast<size_t>(prefill_cache_capacity) * d * es;
     const size_t dcache = static_cast<size_t>(num_decode_seqs) * hkv * static_cast<size_t>(decode_cache_capacity) * d * es;
+    // Each workspace counts with the bytes its half uses, as in that half's own checks (a caller may pass the
+    // rest of one scratch arena as both workspaces).
+    const size_t p_ws = std::min(qkra::prefill_workspace(cfg, num_tokens), prefill_workspace_bytes);
+    const size_t d_ws = std::min(qkra::decode_workspace(cfg, num_decode_seqs, max_cache_len), decode_workspace_bytes);
     const Range p_w[] = {range_of(prefill_out, num_tokens * hq * d * es), range_of(prefill_k_cache, pcache),
-                         range_of(prefill_v_cache, pcache), range_of(prefill_workspace, prefill_workspace_bytes)};
+                         range_of(prefill_v_cache, pcache), range_of(prefill_workspace, p_ws)};
     const Range d_w[] = {range_of(decode_out, num_decode_seqs * hq * d * es), range_of(decode_k_cache, dcache),
-                         range_of(decode_v_cache, dcache), range_of(decode_workspace, decode_workspace_bytes)};
+                         range_of(decode_v_cache, dcache), range_of(decode_workspace, d_ws)};
     const Range p_r[] = {range_of(prefill_qkv, num_tokens * (hq + 2 * hkv) * d * es),
                          range_of(prefill_positions, num_tokens * 4ull), range_of(cu_seqlens, (num_prefill_seqs + 1ull) * 4)};
     const Range d_r[] = {range_of(decode_qkv, num_decode_seqs * (hq + 2 * hkv) * d * es),
@@ -590,6 +591,14 @@ QKRA_API int32_t qknorm_rope_attn_argmax(int32_t dtype, const void* logits, int3
 
 QKRA_API int32_t qknorm_rope_attn_set_kernel_timing(int32_t enable) {
   std::lock_guard<std::mutex> lock(g_timing_mu);
+  if (enable) {  // the pool is created once, here, and kept until the process ends
+    for (; g_events_created < kTimingEvents; ++g_events_created) {
+      hipEvent_t e = nullptr;
+      const hipError_t err = hipEventCreate(&e);
+      if (err != hipSuccess) return hip_status(err);
+      g_event_pool.push_back(e);
+    }
+  }
   g_timing_enabled = enable != 0;
   return QKRA_OK;
 }

@@ -304,7 +304,7 @@ hipError_t launch_split_typed(const DecodeAttnArgs& a, hipStream_t stream) {
   const long long items = static_cast<long long>(a.num_seqs) * a.num_kv_heads * chunks_per_kv * a.num_splits;
   if (items <= 0) return hipSuccess;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((decode_split_kernel<D, GW>), dim3(static_cast<unsigned>(items)), dim3(256), 0, stream,
+  launch_kernel((decode_split_kernel<D, GW>), dim3(static_cast<unsigned>(items)), dim3(256), 0, stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k_cache),
                      static_cast<const float*>(a.v_cache), a.cache_lens, a.partials, a.num_q_heads, a.num_kv_heads,
                      a.cache_capacity, a.num_splits, chunks_per_kv, a.scale_log2);
@@ -324,7 +324,7 @@ hipError_t launch_combine_typed(const DecodeAttnArgs& a, hipStream_t stream) {
   const long long items = static_cast<long long>(a.num_seqs) * a.num_q_heads;
   if (items <= 0) return hipSuccess;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(static_cast<unsigned>(items)), dim3(64), 0, stream,
+  launch_kernel((decode_combine_kernel<D>), dim3(static_cast<unsigned>(items)), dim3(64), 0, stream,
                      a.partials, a.cache_lens, static_cast<float*>(a.out), a.num_q_heads, a.num_splits);
   return hipGetLastError();
 }

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
 template <int D, int GW>
 hipError_t launch_mfma_typed(const DecodeAttnArgs& a, hipStream_t stream) {
   const int chunks_per_kv = (a.num_q_heads / a.num_kv_heads) / GW;
-  hipLaunchKernelGGL((decode_mfma_kernel<D, GW>), dim3(kDecodeWaves / 4), dim3(256), 0, stream,
+  launch_kernel((decode_mfma_kernel<D, GW>), dim3(kDecodeWaves / 4), dim3(256), 0, stream,
                      static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k_cache),
                      static_cast<const bf16*>(a.v_cache), a.cache_lens, a.plan, a.partials, a.num_q_heads,
                      a.num_kv_heads, a.cache_capacity, chunks_per_kv, a.num_units, a.scale_log2);
@@ -171,11 +171,11 @@ hipError_t launch_decode_mfma_combine(const DecodeAttnArgs& a, hipStream_t strea
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int chunks_per_kv = (a.num_q_heads / a.num_kv_heads) / a.heads_per_wave;
   if (a.head_dim == 128) {
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(static_cast<unsigned>(items)), dim3(64), 0, stream,
+    launch_kernel(decode_combine_kernel<128>, dim3(static_cast<unsigned>(items)), dim3(64), 0, stream,
                        a.partials, a.plan, static_cast<bf16*>(a.out), a.num_q_heads, a.num_kv_heads, chunks_per_kv,
                        a.heads_per_wave);
   } else if (a.head_dim == 64) {
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(static_cast<unsigned>(items)), dim3(64), 0, stream,
+    launch_kernel(decode_combine_kernel<64>, dim3(static_cast<unsigned>(items)), dim3(64), 0, stream,
                        a.partials, a.plan, static_cast<bf16*>(a.out), a.num_q_heads, a.num_kv_heads, chunks_per_kv,
                        a.heads_per_wave);
   } else {

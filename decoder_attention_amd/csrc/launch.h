@@ -2,11 +2,31 @@
 // on the given stream and returns the hipError_t of the launch.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace qkra {
+
+// Kernel-timing instrumentation: the C ABI sets these events on the calling
+// thread around one launcher call, and the launch records them on its own
+// dispatch (start and end of the kernel's execution), so timing inserts no
+// packet between kernels.  Null events: an untimed launch.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false;  // set by launch_kernel when a kernel took the events
+};
+extern thread_local LaunchEvents g_launch_events;
+
+// Every kernel of the library is launched through here.
+template <typename Kernel, typename... Args>
+inline void launch_kernel(Kernel kernel, dim3 grid, dim3 block, uint32_t shared_bytes, hipStream_t stream,
+                          Args... args) {
+  LaunchEvents& ev = g_launch_events;
+  hipExtLaunchKernelGGL(kernel, grid, block, shared_bytes, stream, ev.start, ev.stop, 0, args...);
+  if (ev.start != nullptr) ev.used = true;
+}
 
 enum KernelId : int {
   kKernelQkNormRopePrefill = 0,

@@ -147,7 +147,7 @@ hipError_t launch_norm_typed(const AddRmsNormArgs& a, hipStream_t s) {
   T* o = static_cast<T*>(a.out);
 #define QKRA_NORM_CASE(N)                                                                                   \
   if (pieces_per_thread <= N) {                                                                             \
-    hipLaunchKernelGGL((fused_add_rmsnorm_kernel<T, N>), grid, block, 0, s, x, r, w, o, a.hidden_size,      \
+    launch_kernel((fused_add_rmsnorm_kernel<T, N>), grid, block, 0, s, x, r, w, o, a.hidden_size,      \
                        a.has_residual ? 1 : 0, a.copy_residual ? 1 : 0, a.rms_eps);                         \
     return hipGetLastError();                                                                               \
   }
@@ -305,7 +305,7 @@ hipError_t launch_gather_last(const GatherLastArgs& a, hipStream_t stream) {
   const int pieces = row_bytes / 16;
   const dim3 grid(static_cast<unsigned>((pieces + kGatherThreads - 1) / kGatherThreads),
                   static_cast<unsigned>(a.num_seqs));
-  hipLaunchKernelGGL(gather_last_kernel, grid, dim3(kGatherThreads), 0, stream,
+  launch_kernel(gather_last_kernel, grid, dim3(kGatherThreads), 0, stream,
                      static_cast<const uint8_t*>(a.hidden), a.cu_seqlens, static_cast<uint8_t*>(a.out), row_bytes,
                      a.num_rows);
   return hipGetLastError();
@@ -329,17 +329,17 @@ hipError_t launch_argmax_partial(const ArgmaxArgs& a, hipStream_t stream) {
   const int seg_len = argmax_segment_length(a.vocab, a.segments);
   const dim3 grid(static_cast<unsigned>(a.segments), static_cast<unsigned>(a.num_rows));
   if (a.dtype == 0)
-    hipLaunchKernelGGL((argmax_partial_kernel<bf16>), grid, dim3(kArgmaxThreads), 0, stream,
+    launch_kernel((argmax_partial_kernel<bf16>), grid, dim3(kArgmaxThreads), 0, stream,
                        static_cast<const bf16*>(a.logits), a.row_stride, a.vocab, seg_len, a.part_v, a.part_i);
   else
-    hipLaunchKernelGGL((argmax_partial_kernel<float>), grid, dim3(kArgmaxThreads), 0, stream,
+    launch_kernel((argmax_partial_kernel<float>), grid, dim3(kArgmaxThreads), 0, stream,
                        static_cast<const float*>(a.logits), a.row_stride, a.vocab, seg_len, a.part_v, a.part_i);
   return hipGetLastError();
 }
 
 hipError_t launch_argmax_final(const ArgmaxArgs& a, hipStream_t stream) {
   if (a.num_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(argmax_final_kernel, dim3(static_cast<unsigned>(a.num_rows)), dim3(64), 0, stream, a.part_v,
+  launch_kernel(argmax_final_kernel, dim3(static_cast<unsigned>(a.num_rows)), dim3(64), 0, stream, a.part_v,
                      a.part_i, a.segments, a.out);
   return hipGetLastError();
 }

@@ -112,7 +112,7 @@ hipError_t launch_typed(const PrefillAttnArgs& a, hipStream_t stream) {
   const long long items = static_cast<long long>(tiles) * a.num_seqs * a.num_q_heads;
   if (items <= 0) return hipSuccess;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_fp32_kernel<D>), dim3(static_cast<unsigned>(items)), dim3(NT), 0, stream,
+  launch_kernel((prefill_fp32_kernel<D>), dim3(static_cast<unsigned>(items)), dim3(NT), 0, stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k_cache),
                      static_cast<const float*>(a.v_cache), a.cu_seqlens, a.past_lens, static_cast<float*>(a.out),
                      a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.num_seqs, tiles, a.scale_log2);

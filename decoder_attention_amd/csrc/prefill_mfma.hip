@@ -661,7 +661,7 @@ hipError_t launch_typed(const PrefillAttnArgs& a, hipStream_t stream) {
   const long long grid = (items + 7) / 8 * 8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float bound_limit = BOUND_LOG2 / (1.02f * static_cast<float>(D) * a.scale_log2);
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, HC, kBounded>), dim3(static_cast<unsigned>(grid)), dim3(NTHREADS), 0, stream,
+  launch_kernel((prefill_mfma_kernel<D, HC, kBounded>), dim3(static_cast<unsigned>(grid)), dim3(NTHREADS), 0, stream,
                      static_cast<const bf16*>(a.qkv), static_cast<const bf16*>(a.q_norm_weight),
                      static_cast<const bf16*>(a.k_norm_weight), a.rope_table,
                      static_cast<const bf16*>(a.k_cache),
@@ -697,7 +697,7 @@ hipError_t launch_fused_typed(const PrefillAttnArgs& a, const DecodeAttnArgs& d,
   const DecodeRole dec{static_cast<const bf16*>(d.q), static_cast<const bf16*>(d.k_cache),
                        static_cast<const bf16*>(d.v_cache), d.cache_lens, d.plan, d.partials, d.cache_capacity,
                        1, d.num_units, kFusedDecodeWgs};
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, HC, true, G>), dim3(static_cast<unsigned>(grid)), dim3(NTHREADS), 0,
+  launch_kernel((prefill_mfma_kernel<D, HC, true, G>), dim3(static_cast<unsigned>(grid)), dim3(NTHREADS), 0,
                      stream, static_cast<const bf16*>(a.qkv), static_cast<const bf16*>(a.q_norm_weight),
                      static_cast<const bf16*>(a.k_norm_weight), a.rope_table, static_cast<const bf16*>(a.k_cache),
                      static_cast<const bf16*>(a.v_cache), a.cu_seqlens, a.past_lens, static_cast<bf16*>(a.out),

@@ -213,7 +213,7 @@ hipError_t launch_typed(const QkNormRopeArgs& a, hipStream_t stream) {
   const int threads = a.rope_table ? 64 : 256;
   if (a.plan && threads != 256) return hipErrorInvalidValue;  // the plan block is written for 256 threads
   const int blocks = a.num_rows + (a.plan ? 1 : 0);
-  hipLaunchKernelGGL((qknorm_rope_kv_kernel<T, D>), dim3(blocks), dim3(threads), 0, stream,
+  launch_kernel((qknorm_rope_kv_kernel<T, D>), dim3(blocks), dim3(threads), 0, stream,
                      static_cast<const T*>(a.qkv), static_cast<const T*>(a.q_norm_weight),
                      static_cast<const T*>(a.k_norm_weight), a.positions, a.seq_info, a.slot_offsets,
                      a.decode_mode,

@@ -1,10 +1,11 @@
 """Independent CPU evaluators used to pin the oracle (they share no code with it).
 
-* ``expanded_attention`` -- the pages' teaching form of the attention step
-  (zero-to-sglang code walkthrough, section 3.3): every KV head repeated for
-  its group of query heads, the full T x T score matrix scaled by 1/sqrt(D),
-  positions after the query masked to -inf, a float softmax, then the product
-  with V.  Written here with torch float64 on the CPU.
+* ``grouped_attention`` -- the attention step stated as its definition
+  (zero-to-sglang code walkthrough, section 3.3): row i of query head h takes
+  softmax over the visible keys j <= i of q_i . k_j / sqrt(D), with k and v
+  from KV head h // G, and sums the visible values with those weights.  The KV
+  heads are indexed by group (one contraction per group of query heads) and
+  the visible set is built from the indices; torch float64 on the CPU.
 * ``library_attention`` -- torch's own ``scaled_dot_product_attention`` with
   ``is_causal=True`` (a library routine), float64 on the CPU.
 * ``brute_force_layer`` -- the whole layer (split, RMSNorm, RoPE, causal GQA
@@ -19,21 +20,24 @@ from typing import List, Sequence
 import torch
 
 
-def expanded_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
-    """q: [1, Hq, T, D]; k, v: [1, Hkv, T, D] (float64).  Returns (out, probs)."""
-    group = q.shape[1] // k.shape[1]
-    k_full = torch.repeat_interleave(k, group, dim=1)
-    v_full = torch.repeat_interleave(v, group, dim=1)
-    t = q.shape[2]
-    scores = torch.matmul(q, k_full.transpose(-2, -1)) / math.sqrt(q.shape[-1])
-    future = torch.triu(torch.ones((t, t), dtype=torch.bool), diagonal=1)
-    scores = scores.masked_fill(future, float("-inf"))
-    probs = torch.softmax(scores.to(torch.float64), dim=-1)
-    return torch.matmul(probs, v_full), probs
+def grouped_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+    """q: [1, Hq, T, D]; k, v: [1, Hkv, T, D] (float64).  Returns (out [1, Hq, T, D], probs [1, Hq, T, T])."""
+    hq, t, d = q.shape[1], q.shape[2], q.shape[3]
+    hkv = k.shape[1]
+    group = hq // hkv
+    # Query head h = g * group + c belongs to KV head g: view the heads as [g, c].
+    qg = q[0].reshape(hkv, group, t, d)
+    logits = torch.einsum("gcid,gjd->gcij", qg, k[0]) / math.sqrt(d)        # [Hkv, G, query i, key j]
+    visible = torch.arange(t)[None, :] <= torch.arange(t)[:, None]          # [i, j]: key j at or before row i
+    top = torch.where(visible, logits, torch.full_like(logits, -math.inf)).amax(dim=-1, keepdim=True)
+    weight = torch.where(visible, torch.exp(logits - top), torch.zeros_like(logits))
+    probs = weight / weight.sum(dim=-1, keepdim=True)
+    out = torch.einsum("gcij,gjd->gcid", probs, v[0])
+    return out.reshape(1, hq, t, d), probs.reshape(1, hq, t, t)
 
 
 def library_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, native_gqa: bool = False):
-    """torch SDPA, causal.  Layouts as in ``expanded_attention``."""
+    """torch SDPA, causal.  Layouts as in ``grouped_attention``."""
     f = torch.nn.functional.scaled_dot_product_attention
     if native_gqa:
         return f(q, k, v, is_causal=True, enable_gqa=True)

@@ -160,12 +160,12 @@ def _teaching_layout(x):
     return torch.from_numpy(np.ascontiguousarray(np.transpose(x, (1, 0, 2))))[None]
 
 
-def check_attention_vs_expansion(orc):
+def check_attention_vs_definition(orc):
     for seed, (t, hq, hkv, d) in enumerate([(1, 4, 2, 8), (3, 4, 2, 8), (17, 8, 2, 16), (40, 6, 3, 32),
                                             (33, 4, 4, 16), (9, 8, 1, 8)]):
         q, k, v = _attn_case(10 + seed, t, hq, hkv, d)
         out, probs = orc.causal_gqa_attention(q, k, v, return_probs=True)
-        want, want_p = evaluators.expanded_attention(_teaching_layout(q), _teaching_layout(k), _teaching_layout(v))
+        want, want_p = evaluators.grouped_attention(_teaching_layout(q), _teaching_layout(k), _teaching_layout(v))
         np.testing.assert_allclose(out, want[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
         np.testing.assert_allclose(probs, want_p[0].numpy(), rtol=0, atol=1e-12)
 
@@ -453,7 +453,7 @@ ALL_CHECKS = [
     check_rope_d4_frequencies,
     check_rope_complex_form,
     check_rope_norm_and_relativity,
-    check_attention_vs_expansion,
+    check_attention_vs_definition,
     check_attention_vs_library,
     check_layer_brute_force,
     check_single_token_returns_v,
@@ -592,3 +592,4 @@ LAYER_OPS_CHECKS = [
     check_argmax_library,
     check_argmax_ties_and_nan,
 ]
+

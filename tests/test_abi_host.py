@@ -8,6 +8,7 @@ import pathlib
 import re
 
 import pytest
+import torch
 
 import decoder_attention_amd as da
 
@@ -211,10 +212,37 @@ def test_append_empty_batch_is_noop():
     assert call_append(cfg, a) == da.QKRA_OK
 
 
+def on_own_thread(fn):
+    """Runs fn on a thread of its own and returns its result: a HIP error it records stays in that thread's
+    last-error slot, which the other tests read as 'nothing was launched'."""
+    import threading
+
+    box = {}
+
+    def run():
+        try:
+            box["value"] = fn()
+        except BaseException as e:  # re-raised on the calling thread
+            box["error"] = e
+
+    t = threading.Thread(target=run)
+    t.start()
+    t.join()
+    if "error" in box:
+        raise box["error"]
+    return box["value"]
+
+
 def test_kernel_timing_toggle_without_launches():
-    assert da.qknorm_rope_attn_set_kernel_timing(True) == 0
-    assert da.qknorm_rope_attn_read_kernel_timing() == {}
-    assert da.qknorm_rope_attn_set_kernel_timing(False) == 0
+    # Switching timing on creates the event pool (no call creates events); without a GPU that fails cleanly.
+    def toggle():
+        st = da.qknorm_rope_attn_set_kernel_timing(True)
+        assert st in (da.QKRA_OK, da.QKRA_ERR_HIP)
+        if st == da.QKRA_OK:
+            assert da.qknorm_rope_attn_read_kernel_timing() == {}
+        assert da.qknorm_rope_attn_set_kernel_timing(False) == 0
+
+    on_own_thread(toggle)
 
 
 # ---- steps next to the attention layer ------------------------------------------
@@ -371,3 +399,21 @@ def test_mixed_step_with_both_halves_empty_is_noop():
     cfg, a = mixed_args(num_tokens=0, num_decode_seqs=0)
     assert call_mixed(cfg, a) == da.QKRA_OK
     assert da.qknorm_rope_attn_kernel_name(11) == "fused_step_attn"
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="the fake addresses would reach a kernel launch on a GPU")
+def test_mixed_step_workspaces_from_one_arena():
+    """Both workspaces carved from one arena, each declared as the rest of it: the declared ranges overlap, the
+    bytes each half uses do not, so the checks pass as they do for prefill then decode (here the launch itself
+    then fails, as there is no GPU)."""
+    cfg, a = mixed_args()
+    p_need = da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_PREFILL, a["num_tokens"], a["max_seqlen"])
+    arena, arena_bytes = BASE + 400 * MB, 64 * MB
+    a.update(p_ws=arena, p_ws_bytes=arena_bytes, d_ws=arena + p_need, d_ws_bytes=arena_bytes - p_need)
+    status = on_own_thread(lambda: call_mixed(cfg, a))
+    assert status != da.QKRA_ERR_ALIASING
+    assert status in (da.QKRA_OK, da.QKRA_ERR_HIP)
+    # The decode workspace starting inside the bytes the prefill half uses is still refused.
+    a.update(d_ws=arena + p_need - 256)
+    assert call_mixed(cfg, a) == da.QKRA_ERR_ALIASING
+
