@@ -19,6 +19,7 @@ from .qknorm_rope_attn import (  # noqa: F401
     prefill_append,
     round_to_bf16,
 )
+from . import paged  # noqa: F401
 from .layer_ops import (  # noqa: F401
     fused_add_rms_norm,
     last_positions,

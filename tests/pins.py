@@ -593,3 +593,184 @@ LAYER_OPS_CHECKS = [
     check_argmax_ties_and_nan,
 ]
 
+
+# ---------------------------------------------------------------------------
+# Paged K/V cache (oracle/paged.py).  The reading: a paged cache is the
+# per-request cache with its slots stored in pages of a pool, found through a
+# block table; every result is the contiguous cache's.  These checks pin the
+# paged oracle to the flat-address formula written out here, to the already
+# pinned contiguous oracle, and to scalar brute force of the whole layer over
+# the tokens (which knows nothing about pages).
+# ---------------------------------------------------------------------------
+
+def _shuffled_table(r, num_seqs, pages_per_seq, num_pages):
+    """Distinct random pages for every (request, page index); the unused pages of the pool are holes."""
+    assert num_pages >= num_seqs * pages_per_seq
+    return r.permutation(num_pages)[: num_seqs * pages_per_seq].reshape(num_seqs, pages_per_seq)
+
+
+def check_paged_flat_address(pg):
+    # Element (b, g, s, d) of the logical cache sits at ((table[b][s // P] * Hkv + g) * P + s % P) * D + d of the
+    # flat pool: scatter then gather through the oracle agree with that formula written out as scalar loops.
+    r = _rng(70)
+    hkv, d, page, num_pages = 2, 3, 4, 13
+    table = _shuffled_table(r, 3, 3, num_pages)
+    lens = [5, 12, 0]
+    flat = np.full(num_pages * hkv * page * d, np.nan)
+    pool = np.full((num_pages, hkv, page, d), np.nan)
+    for b, n in enumerate(lens):
+        vals = r.standard_normal((hkv, n, d))
+        pg.scatter(pool, table, b, list(range(n)), vals, page)
+        for s in range(n):
+            for g in range(hkv):
+                for e in range(d):
+                    flat[((int(table[b, s // page]) * hkv + g) * page + s % page) * d + e] = vals[g, s, e]
+        np.testing.assert_array_equal(pg.gather(pool, table, b, n, page), vals)
+    np.testing.assert_array_equal(pool.reshape(-1), flat)  # NaN where no slot was written (the holes)
+
+
+def _paged_layer(r, hq, hkv, d, base=1e4):
+    return dict(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, rms_eps=1e-6, rope_base=base)
+
+
+def check_paged_identity_table_is_contiguous(pg):
+    # One page per request holding its whole cache (P = capacity, table[b] = [b]): the pool is the contiguous
+    # cache [B, Hkv, S, D] itself, and both modes give the contiguous oracle's results bit for bit.
+    import oracle.qknorm_rope_attn as orc
+
+    r = _rng(71)
+    hq, hkv, d, cap = 4, 2, 8, 9
+    lens = [3, 0, 8]
+    kc = r.standard_normal((3, hkv, cap, d))
+    vc = r.standard_normal((3, hkv, cap, d))
+    qkv = r.standard_normal((3, (hq + 2 * hkv) * d))
+    wq, wk = 1 + 0.1 * r.standard_normal(d), 1 + 0.1 * r.standard_normal(d)
+    table = np.arange(3).reshape(3, 1)
+    got = pg.decode(qkv, wq, wk, lens, lens, kc, vc, table, cap, **_paged_layer(r, hq, hkv, d))
+    want = orc.decode(qkv, wq, wk, lens, lens, kc, vc, **_paged_layer(r, hq, hkv, d))
+    np.testing.assert_array_equal(got["out"], want["out"])
+    np.testing.assert_array_equal(got["k_pool"], want["k_cache"])
+    np.testing.assert_array_equal(got["v_pool"], want["v_cache"])
+    chunks = [2, 1, 0]
+    cu = np.concatenate([[0], np.cumsum(chunks)])
+    rows = r.standard_normal((3, (hq + 2 * hkv) * d))
+    pos = np.array([3, 4, 0])
+    got = pg.prefill_append(rows, wq, wk, pos, cu, [3, 0, 8], kc, vc, table, cap, **_paged_layer(r, hq, hkv, d))
+    want = orc.prefill_append(rows, wq, wk, pos, cu, [3, 0, 8], kc, vc, **_paged_layer(r, hq, hkv, d))
+    np.testing.assert_array_equal(got["out"], want["out"])
+    np.testing.assert_array_equal(got["k_pool"], want["k_cache"])
+
+
+def check_paged_brute_force(pg):
+    # Prefill through a shuffled table with holes, then one decode step per request: every output equals the
+    # scalar brute force of the whole layer over the request's tokens (no pages involved).  Page sizes 1, 2, 3
+    # put page boundaries everywhere; pages no request owns stay NaN.
+    import evaluators
+
+    for seed, (page, hq, hkv, d) in enumerate([(2, 4, 2, 8), (3, 2, 1, 4), (1, 4, 4, 8)]):
+        r = _rng(72 + seed)
+        seqlens = [5, 1, 4]
+        cap_pages = (max(seqlens) + 1 + page - 1) // page
+        num_pages = 3 * cap_pages + 5
+        table = _shuffled_table(r, 3, cap_pages, num_pages)
+        width = (hq + 2 * hkv) * d
+        tokens = [r.standard_normal((t + 1, width)) for t in seqlens]  # the prompt and then the decoded token
+        wq, wk = 1 + 0.1 * r.standard_normal(d), 1 + 0.1 * r.standard_normal(d)
+        kp = np.full((num_pages, hkv, page, d), np.nan)
+        vp = np.full((num_pages, hkv, page, d), np.nan)
+        prompt = np.concatenate([x[:-1] for x in tokens])
+        cu = np.concatenate([[0], np.cumsum(seqlens)])
+        pos = np.concatenate([np.arange(t) for t in seqlens])
+        pre = pg.prefill_append(prompt, wq, wk, pos, cu, [0, 0, 0], kp, vp, table, page, **_paged_layer(r, hq, hkv, d))
+        dec = pg.decode(np.stack([x[-1] for x in tokens]), wq, wk, seqlens, seqlens, pre["k_pool"], pre["v_pool"],
+                        table, page, **_paged_layer(r, hq, hkv, d))
+        used = set(int(p) for p in table[:, :].reshape(-1))
+        for p in range(num_pages):
+            if p not in used:
+                assert np.all(np.isnan(dec["k_pool"][p])) and np.all(np.isnan(dec["v_pool"][p])), f"hole {p} written"
+        for b, t in enumerate(seqlens):
+            want = evaluators.brute_force_layer(tokens[b].tolist(), wq.tolist(), wk.tolist(), list(range(t + 1)),
+                                                [t + 1], hq, hkv, d, 1e-6, 1e4)
+            want = np.array(want).reshape(t + 1, hq * d)
+            np.testing.assert_allclose(pre["out"][cu[b]:cu[b + 1]], want[:t], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(dec["out"][b], want[t], rtol=0, atol=1e-12)
+
+
+def check_paged_page_permutation(pg):
+    # Renaming the pool's pages (pool permuted, table mapped the same way) changes no result, and the written
+    # pool is the permuted written pool.
+    r = _rng(75)
+    hq, hkv, d, page, num_pages = 4, 2, 8, 2, 11
+    lens = [3, 6]
+    table = _shuffled_table(r, 2, 4, num_pages)
+    kp, vp = r.standard_normal((num_pages, hkv, page, d)), r.standard_normal((num_pages, hkv, page, d))
+    qkv = r.standard_normal((2, (hq + 2 * hkv) * d))
+    wq, wk = 1 + 0.1 * r.standard_normal(d), 1 + 0.1 * r.standard_normal(d)
+    perm = r.permutation(num_pages)            # page p moves to perm[p]
+    kq, vq = np.empty_like(kp), np.empty_like(vp)
+    kq[perm], vq[perm] = kp, vp
+    a = pg.decode(qkv, wq, wk, lens, lens, kp, vp, table, page, **_paged_layer(r, hq, hkv, d))
+    b = pg.decode(qkv, wq, wk, lens, lens, kq, vq, perm[table], page, **_paged_layer(r, hq, hkv, d))
+    np.testing.assert_array_equal(a["out"], b["out"])
+    np.testing.assert_array_equal(a["k_pool"], b["k_pool"][perm])
+    np.testing.assert_array_equal(a["v_pool"], b["v_pool"][perm])
+
+
+def check_paged_shared_prefix(pg):
+    # Two requests whose tables share their first pages (a prefix cached once) read the same history: each
+    # decode equals the contiguous decode over its own copy of that history.  Their new slots land in pages of
+    # their own, and the shared pages are not written.
+    import oracle.qknorm_rope_attn as orc
+
+    r = _rng(76)
+    hq, hkv, d, page = 4, 2, 8, 2
+    L = 4                                      # two full shared pages, new token in page index 2
+    table = np.array([[5, 1, 3], [5, 1, 0]])
+    kp, vp = r.standard_normal((6, hkv, page, d)), r.standard_normal((6, hkv, page, d))
+    qkv = r.standard_normal((2, (hq + 2 * hkv) * d))
+    wq, wk = 1 + 0.1 * r.standard_normal(d), 1 + 0.1 * r.standard_normal(d)
+    got = pg.decode(qkv, wq, wk, [L, L], [L, L], kp, vp, table, page, **_paged_layer(r, hq, hkv, d))
+    hist_k = np.concatenate([kp[5], kp[1]], axis=1)   # slots 0..3 of either request
+    hist_v = np.concatenate([vp[5], vp[1]], axis=1)
+    for b in range(2):
+        kc = np.concatenate([hist_k, np.zeros((hkv, 1, d))], axis=1)[None]
+        vc = np.concatenate([hist_v, np.zeros((hkv, 1, d))], axis=1)[None]
+        want = orc.decode(qkv[b:b + 1], wq, wk, [L], [L], kc, vc, **_paged_layer(r, hq, hkv, d))
+        np.testing.assert_array_equal(got["out"][b], want["out"][0])
+    np.testing.assert_array_equal(got["k_pool"][[5, 1]], kp[[5, 1]])
+    assert not np.array_equal(got["k_pool"][3][:, 0], kp[3][:, 0]) and not np.array_equal(got["k_pool"][0][:, 0],
+                                                                                           kp[0][:, 0])
+
+
+def check_paged_chunks_equal_full_prefill(pg):
+    # A prompt appended in two chunks through a shuffled table gives the rows of one contiguous prefill of the
+    # whole prompt, and the pool read back through the table is that prefill's cache.
+    import oracle.qknorm_rope_attn as orc
+
+    r = _rng(77)
+    hq, hkv, d, page, num_pages = 4, 2, 8, 3, 9
+    t1, t2 = 4, 5
+    qkv = r.standard_normal((t1 + t2, (hq + 2 * hkv) * d))
+    wq, wk = 1 + 0.1 * r.standard_normal(d), 1 + 0.1 * r.standard_normal(d)
+    table = _shuffled_table(r, 1, 3, num_pages)
+    kp = np.full((num_pages, hkv, page, d), np.nan)
+    vp = np.full((num_pages, hkv, page, d), np.nan)
+    a = pg.prefill_append(qkv[:t1], wq, wk, np.arange(t1), [0, t1], [0], kp, vp, table, page,
+                          **_paged_layer(r, hq, hkv, d))
+    b = pg.prefill_append(qkv[t1:], wq, wk, np.arange(t1, t1 + t2), [0, t2], [t1], a["k_pool"], a["v_pool"], table,
+                          page, **_paged_layer(r, hq, hkv, d))
+    full = orc.prefill(qkv, wq, wk, np.arange(t1 + t2), [0, t1 + t2], cache_capacity=t1 + t2,
+                       **_paged_layer(r, hq, hkv, d))
+    np.testing.assert_allclose(np.concatenate([a["out"], b["out"]]), full["out"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(pg.gather(b["k_pool"], table, 0, t1 + t2, page), full["k_cache"][0], rtol=0, atol=0)
+    np.testing.assert_array_equal(pg.gather(b["v_pool"], table, 0, t1 + t2, page), full["v_cache"][0])
+
+
+PAGED_CHECKS = [
+    check_paged_flat_address,
+    check_paged_identity_table_is_contiguous,
+    check_paged_brute_force,
+    check_paged_page_permutation,
+    check_paged_shared_prefix,
+    check_paged_chunks_equal_full_prefill,
+]

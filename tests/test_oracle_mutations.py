@@ -222,3 +222,54 @@ def test_planted_layer_ops_mistake_is_caught(name, monkeypatch):
             caught.append((check.__name__, type(exc).__name__))
             break
     assert caught, f"mutant {name} passed every pin"
+
+
+# ---- paged cache (oracle/paged.py) -------------------------------------------
+import oracle.paged as pg  # noqa: E402
+
+PG_REAL = {name: getattr(pg, name) for name in ("page_of", "scatter", "gather")}
+
+
+def _page_and_row_swapped(table, b, s, page_size):
+    return int(np.asarray(table)[b, s % page_size]), s // page_size
+
+
+def _first_request_table(table, b, s, page_size):
+    return int(np.asarray(table)[0, s // page_size]), s % page_size
+
+
+def _next_page(table, b, s, page_size):
+    t = np.asarray(table)
+    return int(t[b, (s // page_size + 1) % t.shape[1]]), s % page_size
+
+
+def _scatter_one_slot_late(pool, table, request, slots, values, page_size):
+    return PG_REAL["scatter"](pool, table, request, [int(s) + 1 for s in slots], values, page_size)
+
+
+def _gather_reversed_rows(pool, table, request, num_slots, page_size):
+    out = PG_REAL["gather"](pool, table, request, num_slots, page_size)
+    return out[:, ::-1, :].copy()
+
+
+PG_MUTANTS = {
+    "page_and_row_swapped": ("page_of", _page_and_row_swapped),
+    "table_of_request_0": ("page_of", _first_request_table),
+    "next_page": ("page_of", _next_page),
+    "scatter_one_slot_late": ("scatter", _scatter_one_slot_late),
+    "gather_reversed": ("gather", _gather_reversed_rows),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PG_MUTANTS))
+def test_planted_paged_mistake_is_caught(name, monkeypatch):
+    attr, fn = PG_MUTANTS[name]
+    monkeypatch.setattr(pg, attr, fn)
+    caught = []
+    for check in pins.PAGED_CHECKS:
+        try:
+            check(pg)
+        except Exception as exc:
+            caught.append((check.__name__, type(exc).__name__))
+            break
+    assert caught, f"mutant {name} passed every pin"
