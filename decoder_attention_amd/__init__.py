@@ -17,6 +17,8 @@ from .binding import (  # noqa: F401
     QKRA_ERR_WORKSPACE_TOO_SMALL,
     QKRA_ERR_ALIASING,
     QKRA_ERR_HIP,
+    QKRA_ERR_SCRATCH_LIMIT,
+    QKRA_NOALLOC_SCRATCH_BYTES,
     QKRA_MODE_PREFILL,
     QKRA_MODE_DECODE,
     QkraConfig,
@@ -28,6 +30,7 @@ from .binding import (  # noqa: F401
     qknorm_rope_attn_prefill,
     qknorm_rope_attn_prefill_append,
     qknorm_rope_attn_decode,
+    qknorm_rope_attn_decode_noalloc,
     qknorm_rope_attn_mixed_step,
     qknorm_rope_attn_workspace_bytes,
     qknorm_rope_attn_status_string,
@@ -109,6 +112,18 @@ def decode(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cache_
                                      workspace.numel() * workspace.element_size(), stream)
     check(status, "qknorm_rope_attn_decode")
     return out, workspace
+
+
+def decode_noalloc(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cache_lens, max_cache_len: int,
+                   k_cache, v_cache, out, stream=None):
+    """Runs ``qknorm_rope_attn_decode_noalloc`` into the caller's ``out`` (the library's fixed scratch serves as
+    the workspace; nothing is allocated); returns out."""
+    _require_device(qkv, q_norm_weight, k_norm_weight, positions, cache_lens, k_cache, v_cache, out)
+    status = qknorm_rope_attn_decode_noalloc(cfg, qkv, q_norm_weight, k_norm_weight, positions, cache_lens,
+                                             qkv.shape[0], max_cache_len, k_cache, v_cache, k_cache.shape[2], out,
+                                             stream)
+    check(status, "qknorm_rope_attn_decode_noalloc")
+    return out
 
 
 def mixed_step(cfg: QkraConfig, q_norm_weight, k_norm_weight, prefill_qkv, prefill_positions, cu_seqlens,

@@ -24,6 +24,9 @@ QKRA_ERR_CAPACITY = 3
 QKRA_ERR_WORKSPACE_TOO_SMALL = 4
 QKRA_ERR_ALIASING = 5
 QKRA_ERR_HIP = 6
+QKRA_ERR_SCRATCH_LIMIT = 7
+
+QKRA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 QKRA_MODE_PREFILL = 0
 QKRA_MODE_DECODE = 1
@@ -64,6 +67,8 @@ _SIGNATURES = {
                                                _I32, _P, _P, _I32, _P, _P, _SZ, _P]),
     "qknorm_rope_attn_decode": (_I32, [ctypes.POINTER(QkraConfig), _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32,
                                        _P, _P, _SZ, _P]),
+    "qknorm_rope_attn_decode_noalloc": (_I32, [ctypes.POINTER(QkraConfig), _P, _P, _P, _P, _P, _I32, _I32, _P, _P,
+                                               _I32, _P, _P]),
     "qknorm_rope_attn_mixed_step": (_I32, [ctypes.POINTER(QkraConfig), _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P,
                                            _I32, _P, _P, _SZ, _P, _P, _P, _I32, _I32, _P, _P, _I32, _P, _P, _SZ, _P]),
     "qknorm_rope_attn_workspace_bytes": (_SZ, [ctypes.POINTER(QkraConfig), _I32, _I32, _I32]),
@@ -174,6 +179,15 @@ def qknorm_rope_attn_decode(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, 
         ctypes.byref(cfg), _ptr(qkv), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(positions), _ptr(cache_lens),
         int(num_seqs), int(max_cache_len), _ptr(k_cache), _ptr(v_cache), int(cache_capacity), _ptr(out),
         _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def qknorm_rope_attn_decode_noalloc(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cache_lens,
+                                    num_seqs: int, max_cache_len: int, k_cache, v_cache, cache_capacity: int, out,
+                                    stream=None) -> int:
+    return lib().qknorm_rope_attn_decode_noalloc(
+        ctypes.byref(cfg), _ptr(qkv), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(positions), _ptr(cache_lens),
+        int(num_seqs), int(max_cache_len), _ptr(k_cache), _ptr(v_cache), int(cache_capacity), _ptr(out),
+        _stream(stream))
 
 
 def qknorm_rope_attn_workspace_bytes(cfg: QkraConfig, mode: int, n: int, max_len: int) -> int:

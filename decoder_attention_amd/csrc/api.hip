@@ -165,13 +165,14 @@ QKRA_API const char* qknorm_rope_attn_status_string(int32_t status) {
     case QKRA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case QKRA_ERR_ALIASING: return "output or cache buffers overlap another buffer";
     case QKRA_ERR_HIP: return "HIP runtime error";
+    case QKRA_ERR_SCRATCH_LIMIT: return "the call needs more than the fixed scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }
 
 QKRA_API int32_t qknorm_rope_attn_last_hip_error(void) { return g_last_hip_error; }
 
-QKRA_API int32_t qknorm_rope_attn_version(void) { return 200; }
+QKRA_API int32_t qknorm_rope_attn_version(void) { return 300; }
 
 }  // extern "C"
 
@@ -431,6 +432,58 @@ QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv
                                          void* workspace, size_t workspace_bytes, void* hip_stream) {
   return decode_impl(cfg, qkv, q_norm_weight, k_norm_weight, positions, cache_lens, num_seqs, max_cache_len, k_cache,
                      v_cache, cache_capacity, out, workspace, workspace_bytes, hip_stream, false, nullptr);
+}
+
+// ---- the decode entry point that allocates nothing ------------------------
+// Its workspace is this file-scope device array: each GPU the library runs on
+// holds its own copy (QKRA_NOALLOC_SCRATCH_BYTES) until the process ends.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// the device address comes from hipGetSymbolAddress, taken once per device
+// (with that device current) on the entry point's first call there.
+static __device__ __align__(256) unsigned char scratch[QKRA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (QKRA_OK), or the HIP error.
+int32_t device_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return hip_status(err);
+  if (dev < 0 || dev >= kMaxDevices) return QKRA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return hip_status(err);
+    if (p == nullptr) return QKRA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return QKRA_OK;
+}
+}  // namespace
+
+QKRA_API int32_t qknorm_rope_attn_decode_noalloc(const qkra_config* cfg, const void* qkv, const void* q_norm_weight,
+                                                 const void* k_norm_weight, const int32_t* positions,
+                                                 const int32_t* cache_lens, int32_t num_seqs, int32_t max_cache_len,
+                                                 void* k_cache, void* v_cache, int32_t cache_capacity, void* out,
+                                                 void* hip_stream) {
+  const int32_t cs = check_config(cfg);
+  if (cs != QKRA_OK) return cs;
+  if (num_seqs < 0 || max_cache_len < 0) return QKRA_ERR_INVALID_ARGUMENT;
+  if (num_seqs == 0) return QKRA_OK;
+  // Sizes past the fixed scratch are refused before anything touches the GPU.
+  if (qkra::decode_workspace(cfg, num_seqs, max_cache_len) > QKRA_NOALLOC_SCRATCH_BYTES) return QKRA_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  const int32_t st = device_scratch(&ws);
+  if (st != QKRA_OK) return st;
+  // Nothing in the decode workspace needs to start at zero: every plan entry,
+  // q~ row and partial record the kernels read is written earlier in the call.
+  return decode_impl(cfg, qkv, q_norm_weight, k_norm_weight, positions, cache_lens, num_seqs, max_cache_len, k_cache,
+                     v_cache, cache_capacity, out, ws, QKRA_NOALLOC_SCRATCH_BYTES, hip_stream, false, nullptr);
 }
 
 QKRA_API int32_t qknorm_rope_attn_mixed_step(

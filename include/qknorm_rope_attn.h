@@ -71,6 +71,7 @@ extern "C" {
 #define QKRA_ERR_WORKSPACE_TOO_SMALL 4
 #define QKRA_ERR_ALIASING 5           /* out overlaps an input, a cache or the workspace, or buffers overlap each other */
 #define QKRA_ERR_HIP 6                /* a HIP launch or runtime call failed */
+#define QKRA_ERR_SCRATCH_LIMIT 7      /* qknorm_rope_attn_decode_noalloc: the call needs more than its fixed scratch */
 
 /* Workspace query modes. */
 #define QKRA_MODE_PREFILL 0
@@ -184,6 +185,36 @@ QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv
                                          void* k_cache, void* v_cache, int32_t cache_capacity,
                                          void* out, void* workspace, size_t workspace_bytes,
                                          void* hip_stream);
+
+/*
+ * Decode without allocation or workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, checks, layouts and
+ * kernels as qknorm_rope_attn_decode, with the workspace in a fixed device
+ * array inside the library, QKRA_NOALLOC_SCRATCH_BYTES per GPU, held from the
+ * first call on a GPU until the process ends.  It calls no hipMalloc or
+ * hipFree and creates no HIP objects; its first call on a device looks up that
+ * device's copy of the array (the calling thread's current device, which
+ * must be the stream's).
+ *
+ * Calls whose decode workspace (qknorm_rope_attn_workspace_bytes(cfg,
+ * QKRA_MODE_DECODE, num_seqs, max_cache_len)) exceeds the scratch return
+ * QKRA_ERR_SCRATCH_LIMIT before anything is enqueued.  With Qwen3 heads (32
+ * query, 8 KV, D = 128) in bf16 that is about 1000 requests; fp32 partials
+ * grow with max_cache_len.
+ *
+ * Every call on a GPU shares that GPU's scratch, which keeps the last call's
+ * contents (nothing in it needs to start at zero).  Calls that overlap on one
+ * GPU, on different streams or from different threads, race on it: the caller
+ * must order them (one stream, or events).
+ */
+#define QKRA_NOALLOC_SCRATCH_BYTES (16u << 20)
+QKRA_API int32_t qknorm_rope_attn_decode_noalloc(const qkra_config* cfg, const void* qkv,
+                                                 const void* q_norm_weight, const void* k_norm_weight,
+                                                 const int32_t* positions, const int32_t* cache_lens,
+                                                 int32_t num_seqs, int32_t max_cache_len,
+                                                 void* k_cache, void* v_cache, int32_t cache_capacity,
+                                                 void* out, void* hip_stream);
 
 /*
  * One serving step with both kinds of request: exactly what

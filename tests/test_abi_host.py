@@ -35,10 +35,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    for code in range(7):
+    for code in range(8):
         assert da.qknorm_rope_attn_status_string(code)
     assert da.qknorm_rope_attn_status_string(99) == "unknown status"
-    assert da.qknorm_rope_attn_version() == 200  # 0.2.0: qknorm_rope_attn_mixed_step
+    assert da.qknorm_rope_attn_version() == 300  # 0.3.0: qknorm_rope_attn_decode_noalloc
     assert da.qknorm_rope_attn_last_hip_error() == 0
     assert da.qknorm_rope_attn_kernel_name(1) == "prefill_attn_mfma_bf16"
     assert da.qknorm_rope_attn_kernel_name(10) == "prefill_attn_mfma_bf16_shifted"
@@ -417,3 +417,25 @@ def test_mixed_step_workspaces_from_one_arena():
     a.update(d_ws=arena + p_need - 256)
     assert call_mixed(cfg, a) == da.QKRA_ERR_ALIASING
 
+
+def test_decode_noalloc_refuses_sizes_past_its_scratch():
+    """The no-allocation decode takes its workspace from a fixed array; a call that needs more is refused with its
+    own status before anything touches the GPU (so this runs without one)."""
+    cfg = da.make_config(32, 8, 128, da.QKRA_BF16)
+    need = da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_DECODE, 4096, 100)
+    assert need > da.QKRA_NOALLOC_SCRATCH_BYTES
+    st = da.qknorm_rope_attn_decode_noalloc(cfg, BASE, BASE + 64 * MB, BASE + 65 * MB, BASE + 66 * MB, BASE + 67 * MB,
+                                            4096, 100, BASE + 100 * MB, BASE + 200 * MB, 101, BASE + 300 * MB, 0)
+    assert st == da.QKRA_ERR_SCRATCH_LIMIT
+    assert "scratch" in da.qknorm_rope_attn_status_string(st)
+    # fp32 partials grow with the longest cache: a handful of long requests is already too much.
+    cfg32 = da.make_config(32, 8, 128, da.QKRA_FP32)
+    assert da.qknorm_rope_attn_workspace_bytes(cfg32, da.QKRA_MODE_DECODE, 64, 65536) > da.QKRA_NOALLOC_SCRATCH_BYTES
+    st = da.qknorm_rope_attn_decode_noalloc(cfg32, BASE, BASE + 64 * MB, BASE + 65 * MB, BASE + 66 * MB,
+                                            BASE + 67 * MB, 64, 65536, BASE + 100 * MB, BASE + 200 * MB, 65537,
+                                            BASE + 300 * MB, 0)
+    assert st == da.QKRA_ERR_SCRATCH_LIMIT
+    # An empty batch is a no-op; bad arguments keep their own status.
+    assert da.qknorm_rope_attn_decode_noalloc(cfg, None, None, None, None, None, 0, 0, None, None, 1, None, 0) == 0
+    assert da.qknorm_rope_attn_decode_noalloc(cfg, BASE, BASE, BASE, BASE, BASE, -1, 0, BASE, BASE, 1, BASE, 0) == \
+        da.QKRA_ERR_INVALID_ARGUMENT
