@@ -23,6 +23,8 @@ from .binding import (  # noqa: F401
     QKRA_MODE_DECODE,
     QkraConfig,
     QkraError,
+    QkraPagedCache,
+    make_paged_cache,
     check,
     exported_symbols,
     lib,
@@ -31,6 +33,8 @@ from .binding import (  # noqa: F401
     qknorm_rope_attn_prefill_append,
     qknorm_rope_attn_decode,
     qknorm_rope_attn_decode_noalloc,
+    qknorm_rope_attn_decode_paged,
+    qknorm_rope_attn_prefill_append_paged,
     qknorm_rope_attn_mixed_step,
     qknorm_rope_attn_workspace_bytes,
     qknorm_rope_attn_status_string,
@@ -124,6 +128,52 @@ def decode_noalloc(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions
                                              stream)
     check(status, "qknorm_rope_attn_decode_noalloc")
     return out
+
+
+def decode_paged(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cache_lens, max_cache_len: int,
+                 k_pool, v_pool, block_table, page_size: int, out=None, workspace=None, stream=None):
+    """Runs ``qknorm_rope_attn_decode_paged`` (pools [num_pages, Hkv, page_size, D], block_table int32
+    [B, pages_per_seq]); returns (out [B, Hq*D], workspace)."""
+    import torch
+
+    _require_device(qkv, q_norm_weight, k_norm_weight, positions, cache_lens, k_pool, v_pool, block_table)
+    b = qkv.shape[0]
+    if out is None:
+        out = torch.empty((b, cfg.num_q_heads * cfg.head_dim), dtype=qkv.dtype, device=qkv.device)
+    need = qknorm_rope_attn_workspace_bytes(cfg, QKRA_MODE_DECODE, b, max_cache_len)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=qkv.device)
+    cache = make_paged_cache(k_pool, v_pool, block_table, k_pool.shape[0], page_size, block_table.shape[1])
+    status = qknorm_rope_attn_decode_paged(cfg, qkv, q_norm_weight, k_norm_weight, positions, cache_lens, b,
+                                           max_cache_len, cache, out, workspace,
+                                           workspace.numel() * workspace.element_size(), stream)
+    check(status, "qknorm_rope_attn_decode_paged")
+    return out, workspace
+
+
+def prefill_append_paged(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens, cache_lens,
+                         max_seqlen: int, max_cache_len: int, k_pool, v_pool, block_table, page_size: int, out=None,
+                         workspace=None, stream=None):
+    """Runs ``qknorm_rope_attn_prefill_append_paged`` (cache_lens None: a prefill into the paged cache); returns
+    (out [N, Hq*D], workspace)."""
+    import torch
+
+    _require_device(qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens, k_pool, v_pool, block_table)
+    if cache_lens is not None:
+        _require_device(cache_lens)
+    n = qkv.shape[0]
+    b = cu_seqlens.shape[0] - 1
+    if out is None:
+        out = torch.empty((n, cfg.num_q_heads * cfg.head_dim), dtype=qkv.dtype, device=qkv.device)
+    need = qknorm_rope_attn_workspace_bytes(cfg, QKRA_MODE_PREFILL, n, max_seqlen)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=qkv.device)
+    cache = make_paged_cache(k_pool, v_pool, block_table, k_pool.shape[0], page_size, block_table.shape[1])
+    status = qknorm_rope_attn_prefill_append_paged(cfg, qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens,
+                                                   cache_lens, n, b, max_seqlen, max_cache_len, cache, out,
+                                                   workspace, workspace.numel() * workspace.element_size(), stream)
+    check(status, "qknorm_rope_attn_prefill_append_paged")
+    return out, workspace
 
 
 def mixed_step(cfg: QkraConfig, q_norm_weight, k_norm_weight, prefill_qkv, prefill_positions, cu_seqlens,

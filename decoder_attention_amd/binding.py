@@ -44,6 +44,18 @@ class QkraConfig(ctypes.Structure):
     ]
 
 
+class QkraPagedCache(ctypes.Structure):
+    _fields_ = [
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("pages_per_seq", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
 class QkraError(RuntimeError):
     def __init__(self, status: int, where: str = ""):
         self.status = status
@@ -69,6 +81,10 @@ _SIGNATURES = {
                                        _P, _P, _SZ, _P]),
     "qknorm_rope_attn_decode_noalloc": (_I32, [ctypes.POINTER(QkraConfig), _P, _P, _P, _P, _P, _I32, _I32, _P, _P,
                                                _I32, _P, _P]),
+    "qknorm_rope_attn_decode_paged": (_I32, [ctypes.POINTER(QkraConfig), _P, _P, _P, _P, _P, _I32, _I32,
+                                             ctypes.POINTER(QkraPagedCache), _P, _P, _SZ, _P]),
+    "qknorm_rope_attn_prefill_append_paged": (_I32, [ctypes.POINTER(QkraConfig), _P, _P, _P, _P, _P, _P, _I32, _I32,
+                                                     _I32, _I32, ctypes.POINTER(QkraPagedCache), _P, _P, _SZ, _P]),
     "qknorm_rope_attn_mixed_step": (_I32, [ctypes.POINTER(QkraConfig), _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P,
                                            _I32, _P, _P, _SZ, _P, _P, _P, _I32, _I32, _P, _P, _I32, _P, _P, _SZ, _P]),
     "qknorm_rope_attn_workspace_bytes": (_SZ, [ctypes.POINTER(QkraConfig), _I32, _I32, _I32]),
@@ -190,6 +206,32 @@ def qknorm_rope_attn_decode_noalloc(cfg: QkraConfig, qkv, q_norm_weight, k_norm_
         _stream(stream))
 
 
+def make_paged_cache(k_pool, v_pool, block_table, num_pages: int, page_size: int,
+                     pages_per_seq: int) -> QkraPagedCache:
+    return QkraPagedCache(_ptr(k_pool), _ptr(v_pool), _ptr(block_table), int(num_pages), int(page_size),
+                          int(pages_per_seq), 0)
+
+
+def qknorm_rope_attn_decode_paged(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cache_lens,
+                                  num_seqs: int, max_cache_len: int, cache: Optional[QkraPagedCache], out, workspace,
+                                  workspace_bytes: int, stream=None) -> int:
+    return lib().qknorm_rope_attn_decode_paged(
+        ctypes.byref(cfg), _ptr(qkv), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(positions), _ptr(cache_lens),
+        int(num_seqs), int(max_cache_len), None if cache is None else ctypes.byref(cache), _ptr(out), _ptr(workspace),
+        int(workspace_bytes), _stream(stream))
+
+
+def qknorm_rope_attn_prefill_append_paged(cfg: QkraConfig, qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens,
+                                          cache_lens, num_tokens: int, num_seqs: int, max_seqlen: int,
+                                          max_cache_len: int, cache: Optional[QkraPagedCache], out, workspace,
+                                          workspace_bytes: int, stream=None) -> int:
+    return lib().qknorm_rope_attn_prefill_append_paged(
+        ctypes.byref(cfg), _ptr(qkv), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(positions), _ptr(cu_seqlens),
+        _ptr(cache_lens), int(num_tokens), int(num_seqs), int(max_seqlen), int(max_cache_len),
+        None if cache is None else ctypes.byref(cache), _ptr(out), _ptr(workspace), int(workspace_bytes),
+        _stream(stream))
+
+
 def qknorm_rope_attn_workspace_bytes(cfg: QkraConfig, mode: int, n: int, max_len: int) -> int:
     return int(lib().qknorm_rope_attn_workspace_bytes(ctypes.byref(cfg), int(mode), int(n), int(max_len)))
 
@@ -206,8 +248,10 @@ def qknorm_rope_attn_version() -> int:
     return int(lib().qknorm_rope_attn_version())
 
 
-def qknorm_rope_attn_set_kernel_timing(enable: bool) -> int:
-    return int(lib().qknorm_rope_attn_set_kernel_timing(1 if enable else 0))
+def qknorm_rope_attn_set_kernel_timing(enable) -> int:
+    """enable: True (every kernel), False (off), or an int mask over kernel ids."""
+    mask = -1 if enable is True else 0 if enable is False else int(enable)
+    return int(lib().qknorm_rope_attn_set_kernel_timing(mask))
 
 
 def qknorm_rope_attn_kernel_name(kernel_id: int) -> str:

@@ -86,6 +86,36 @@ Range range_of(const void* p, size_t bytes) {
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Paged caches (qkra_paged_cache).
+size_t pool_bytes(const qkra_config* cfg, const PagedTable& pt) {
+  return static_cast<size_t>(pt.num_pages) * cfg->num_kv_heads * (static_cast<size_t>(1) << pt.page_shift) *
+         cfg->head_dim * elem_size(cfg->dtype);
+}
+size_t table_bytes(int32_t num_seqs, const PagedTable& pt) {
+  return static_cast<size_t>(num_seqs) * pt.pages_per_seq * sizeof(int32_t);
+}
+// Checks the descriptor; on QKRA_OK, `pt` describes it and `capacity` is the
+// slots each request's table row covers.
+int32_t paged_view(const qkra_paged_cache* c, int32_t num_seqs, PagedTable* pt, int32_t* capacity) {
+  if (c == nullptr || c->reserved != 0) return QKRA_ERR_INVALID_ARGUMENT;
+  if (c->num_pages <= 0 || c->pages_per_seq <= 0) return QKRA_ERR_INVALID_ARGUMENT;
+  int shift = -1;
+  for (int k = 6; k <= 10; ++k)
+    if (c->page_size == (1 << k)) shift = k;
+  if (shift < 0) return QKRA_ERR_UNSUPPORTED;  // 64, 128, 256, 512 or 1024 slots per page
+  const long long cap = static_cast<long long>(c->pages_per_seq) * c->page_size;
+  if (cap > 0x7fffffffLL || static_cast<long long>(num_seqs) * c->pages_per_seq > 0x7fffffffLL)
+    return QKRA_ERR_UNSUPPORTED;
+  if (!c->k_pool || !c->v_pool || (num_seqs > 0 && !c->block_table)) return QKRA_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(c->block_table) & 3u) != 0) return QKRA_ERR_INVALID_ARGUMENT;
+  pt->table = c->block_table;
+  pt->pages_per_seq = c->pages_per_seq;
+  pt->page_shift = shift;
+  pt->num_pages = c->num_pages;
+  *capacity = static_cast<int32_t>(cap);
+  return QKRA_OK;
+}
+
 // ---- per-kernel timing (benchmark instrumentation) ------------------------
 // Process-wide: a pool of events is created when timing is switched on
 // (qknorm_rope_attn_set_kernel_timing), so no call creates an event; a launch
@@ -96,7 +126,7 @@ struct TimingRecord {
   hipEvent_t start, stop;
 };
 std::mutex g_timing_mu;
-bool g_timing_enabled = false;
+uint32_t g_timing_mask = 0;  // bit k: time kernel id k
 std::vector<TimingRecord> g_timing_records;
 std::vector<hipEvent_t> g_event_pool;
 int g_events_created = 0;
@@ -107,7 +137,7 @@ hipError_t timed(int kernel, hipStream_t stream, Launch&& launch) {
   hipEvent_t start = nullptr, stop = nullptr;
   {
     std::lock_guard<std::mutex> lock(g_timing_mu);
-    if (!g_timing_enabled || g_event_pool.size() < 2) return launch();
+    if (((g_timing_mask >> kernel) & 1u) == 0 || g_event_pool.size() < 2) return launch();
     start = g_event_pool.back();
     g_event_pool.pop_back();
     stop = g_event_pool.back();
@@ -190,7 +220,8 @@ int32_t prefill_impl(const qkra_config* cfg, const void* qkv, const void* q_norm
                      const int32_t* positions, const int32_t* cu_seqlens, const int32_t* cache_lens,
                      int32_t num_tokens, int32_t num_seqs, int32_t max_seqlen, int32_t max_cache_len,
                      void* k_cache, void* v_cache, int32_t cache_capacity, void* out, void* workspace,
-                     size_t workspace_bytes, void* hip_stream, DeferredPrefill* defer = nullptr) {
+                     size_t workspace_bytes, void* hip_stream, DeferredPrefill* defer = nullptr,
+                     const PagedTable* paged = nullptr) {
   const int32_t cs = check_config(cfg);
   if (cs != QKRA_OK) return cs;
   if (num_tokens < 0 || num_seqs < 0 || max_seqlen < 0 || max_cache_len < 0 || cache_capacity < 0)
@@ -213,14 +244,15 @@ int32_t prefill_impl(const qkra_config* cfg, const void* qkv, const void* q_norm
   const size_t hq = cfg->num_q_heads, hkv = cfg->num_kv_heads, d = cfg->head_dim;
   const Range r_qkv = range_of(qkv, num_tokens * (hq + 2 * hkv) * d * es);
   const Range r_out = range_of(out, num_tokens * hq * d * es);
-  const size_t cache_bytes = static_cast<size_t>(num_seqs) * hkv * cache_capacity * d * es;
+  const size_t cache_bytes = paged ? pool_bytes(cfg, *paged) : static_cast<size_t>(num_seqs) * hkv * cache_capacity * d * es;
   const Range r_k = range_of(k_cache, cache_bytes), r_v = range_of(v_cache, cache_bytes);
   const Range r_ws = range_of(workspace, need);
   const Range r_wq = range_of(q_norm_weight, d * es), r_wk = range_of(k_norm_weight, d * es);
   const Range r_pos = range_of(positions, num_tokens * 4ull), r_cu = range_of(cu_seqlens, (num_seqs + 1ull) * 4);
   const Range r_len = range_of(cache_lens, cache_lens ? num_seqs * 4ull : 0);
+  const Range r_tab = paged ? range_of(paged->table, table_bytes(num_seqs, *paged)) : Range{0, 0};
   for (Range w : {r_out, r_k, r_v, r_ws})
-    for (Range r : {r_qkv, r_wq, r_wk, r_pos, r_cu, r_len})
+    for (Range r : {r_qkv, r_wq, r_wk, r_pos, r_cu, r_len, r_tab})
       if (overlap(w, r)) return QKRA_ERR_ALIASING;
   if (overlap(r_out, r_k) || overlap(r_out, r_v) || overlap(r_out, r_ws) || overlap(r_k, r_v) ||
       overlap(r_k, r_ws) || overlap(r_v, r_ws))
@@ -249,6 +281,7 @@ int32_t prefill_impl(const qkra_config* cfg, const void* qkv, const void* q_norm
   ka.rope_table = fused_q ? static_cast<float*>(workspace) : nullptr;
   ka.k_cache = k_cache;
   ka.v_cache = v_cache;
+  if (paged) ka.paged = *paged;
   hipError_t err = timed(kKernelQkNormRopePrefill, stream, [&] { return launch_qknorm_rope(ka, stream); });
   if (err != hipSuccess) return hip_status(err);
 
@@ -271,7 +304,8 @@ int32_t prefill_impl(const qkra_config* cfg, const void* qkv, const void* q_norm
   pa.num_seqs = num_seqs;
   pa.max_seqlen = max_seqlen;
   pa.scale_log2 = softmax_scale_log2(cfg->head_dim);
-  if (defer && cfg->dtype == QKRA_BF16 && cache_lens == nullptr) {  // attention runs in the fused step
+  if (paged) pa.paged = *paged;
+  if (defer && !paged && cfg->dtype == QKRA_BF16 && cache_lens == nullptr) {  // attention runs in the fused step
     defer->args = pa;
     defer->set = true;
     return QKRA_OK;
@@ -320,7 +354,8 @@ namespace {
 int32_t decode_impl(const qkra_config* cfg, const void* qkv, const void* q_norm_weight, const void* k_norm_weight,
                     const int32_t* positions, const int32_t* cache_lens, int32_t num_seqs, int32_t max_cache_len,
                     void* k_cache, void* v_cache, int32_t cache_capacity, void* out, void* workspace,
-                    size_t workspace_bytes, void* hip_stream, bool validate_only, const PrefillAttnArgs* fused) {
+                    size_t workspace_bytes, void* hip_stream, bool validate_only, const PrefillAttnArgs* fused,
+                    const PagedTable* paged = nullptr) {
   const int32_t cs = check_config(cfg);
   if (cs != QKRA_OK) return cs;
   if (num_seqs < 0 || max_cache_len < 0 || cache_capacity < 0) return QKRA_ERR_INVALID_ARGUMENT;
@@ -343,13 +378,14 @@ int32_t decode_impl(const qkra_config* cfg, const void* qkv, const void* q_norm_
   const size_t hq = cfg->num_q_heads, hkv = cfg->num_kv_heads, d = cfg->head_dim;
   const Range r_qkv = range_of(qkv, num_seqs * (hq + 2 * hkv) * d * es);
   const Range r_out = range_of(out, num_seqs * hq * d * es);
-  const size_t cache_bytes = static_cast<size_t>(num_seqs) * hkv * cache_capacity * d * es;
+  const size_t cache_bytes = paged ? pool_bytes(cfg, *paged) : static_cast<size_t>(num_seqs) * hkv * cache_capacity * d * es;
   const Range r_k = range_of(k_cache, cache_bytes), r_v = range_of(v_cache, cache_bytes);
   const Range r_ws = range_of(workspace, need);
   const Range r_wq = range_of(q_norm_weight, d * es), r_wk = range_of(k_norm_weight, d * es);
   const Range r_pos = range_of(positions, num_seqs * 4ull), r_len = range_of(cache_lens, num_seqs * 4ull);
+  const Range r_tab = paged ? range_of(paged->table, table_bytes(num_seqs, *paged)) : Range{0, 0};
   for (Range w : {r_out, r_k, r_v, r_ws})
-    for (Range r : {r_qkv, r_wq, r_wk, r_pos, r_len})
+    for (Range r : {r_qkv, r_wq, r_wk, r_pos, r_len, r_tab})
       if (overlap(w, r)) return QKRA_ERR_ALIASING;
   if (overlap(r_out, r_k) || overlap(r_out, r_v) || overlap(r_out, r_ws) || overlap(r_k, r_v) ||
       overlap(r_k, r_ws) || overlap(r_v, r_ws))
@@ -376,6 +412,7 @@ int32_t decode_impl(const qkra_config* cfg, const void* qkv, const void* q_norm_
   ka.q_out = workspace;
   ka.k_cache = k_cache;
   ka.v_cache = v_cache;
+  if (paged) ka.paged = *paged;
   char* ws = static_cast<char*>(workspace) + decode_q_bytes(cfg, num_seqs);
   if (cfg->dtype == QKRA_BF16) {  // kernel 1's launch also builds the split kernel's plan (one extra block)
     const int group = cfg->num_q_heads / cfg->num_kv_heads;
@@ -399,6 +436,7 @@ int32_t decode_impl(const qkra_config* cfg, const void* qkv, const void* q_norm_
   da.cache_capacity = cache_capacity;
   da.num_seqs = num_seqs;
   da.scale_log2 = softmax_scale_log2(cfg->head_dim);
+  if (paged) da.paged = *paged;
   if (cfg->dtype == QKRA_BF16) {
     da.plan = reinterpret_cast<int32_t*>(ws);
     da.partials = reinterpret_cast<float*>(ws + decode_plan_bytes(cfg, num_seqs));
@@ -432,6 +470,45 @@ QKRA_API int32_t qknorm_rope_attn_decode(const qkra_config* cfg, const void* qkv
                                          void* workspace, size_t workspace_bytes, void* hip_stream) {
   return decode_impl(cfg, qkv, q_norm_weight, k_norm_weight, positions, cache_lens, num_seqs, max_cache_len, k_cache,
                      v_cache, cache_capacity, out, workspace, workspace_bytes, hip_stream, false, nullptr);
+}
+
+QKRA_API int32_t qknorm_rope_attn_decode_paged(const qkra_config* cfg, const void* qkv, const void* q_norm_weight,
+                                               const void* k_norm_weight, const int32_t* positions,
+                                               const int32_t* cache_lens, int32_t num_seqs, int32_t max_cache_len,
+                                               const qkra_paged_cache* cache, void* out, void* workspace,
+                                               size_t workspace_bytes, void* hip_stream) {
+  const int32_t cs = check_config(cfg);
+  if (cs != QKRA_OK) return cs;
+  if (num_seqs < 0 || max_cache_len < 0) return QKRA_ERR_INVALID_ARGUMENT;
+  if (num_seqs == 0) return QKRA_OK;
+  PagedTable pt;
+  int32_t capacity = 0;
+  const int32_t st = paged_view(cache, num_seqs, &pt, &capacity);
+  if (st != QKRA_OK) return st;
+  return decode_impl(cfg, qkv, q_norm_weight, k_norm_weight, positions, cache_lens, num_seqs, max_cache_len,
+                     cache->k_pool, cache->v_pool, capacity, out, workspace, workspace_bytes, hip_stream, false,
+                     nullptr, &pt);
+}
+
+QKRA_API int32_t qknorm_rope_attn_prefill_append_paged(const qkra_config* cfg, const void* qkv,
+                                                       const void* q_norm_weight, const void* k_norm_weight,
+                                                       const int32_t* positions, const int32_t* cu_seqlens,
+                                                       const int32_t* cache_lens, int32_t num_tokens,
+                                                       int32_t num_seqs, int32_t max_seqlen, int32_t max_cache_len,
+                                                       const qkra_paged_cache* cache, void* out, void* workspace,
+                                                       size_t workspace_bytes, void* hip_stream) {
+  const int32_t cs = check_config(cfg);
+  if (cs != QKRA_OK) return cs;
+  if (num_tokens < 0 || num_seqs < 0 || max_cache_len < 0) return QKRA_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return QKRA_OK;
+  if (cache_lens == nullptr && max_cache_len != 0) return QKRA_ERR_INVALID_ARGUMENT;
+  PagedTable pt;
+  int32_t capacity = 0;
+  const int32_t st = paged_view(cache, num_seqs, &pt, &capacity);
+  if (st != QKRA_OK) return st;
+  return prefill_impl(cfg, qkv, q_norm_weight, k_norm_weight, positions, cu_seqlens, cache_lens, num_tokens, num_seqs,
+                      max_seqlen, max_cache_len, cache->k_pool, cache->v_pool, capacity, out, workspace,
+                      workspace_bytes, hip_stream, nullptr, &pt);
 }
 
 // ---- the decode entry point that allocates nothing ------------------------
@@ -652,7 +729,7 @@ QKRA_API int32_t qknorm_rope_attn_set_kernel_timing(int32_t enable) {
       g_event_pool.push_back(e);
     }
   }
-  g_timing_enabled = enable != 0;
+  g_timing_mask = static_cast<uint32_t>(enable);
   return QKRA_OK;
 }
 

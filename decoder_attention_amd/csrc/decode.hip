@@ -62,7 +62,7 @@ template <int D, int GW>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     const float* __restrict__ q, const float* __restrict__ k_cache, const float* __restrict__ v_cache,
     const int32_t* __restrict__ cache_lens, float* __restrict__ partials, int num_q_heads, int num_kv_heads,
-    int cache_capacity, int num_splits, int chunks_per_kv, float scale_log2) {
+    int cache_capacity, int num_splits, int chunks_per_kv, float scale_log2, PagedTable paged) {
   typedef float T;
   constexpr int ES = sizeof(T);
   constexpr int E16 = 16 / ES;          // elements per 16-byte load
@@ -115,8 +115,6 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   }
 
   const size_t head_off = (static_cast<size_t>(b) * num_kv_heads + g) * cache_capacity * D;
-  const T* kb = k_cache + head_off;
-  const T* vb = v_cache + head_off;
 
   // Four register buffers in a ring: three steps' loads stay in flight while
   // the fourth step is consumed.  Loads are unconditional (rows past the
@@ -126,8 +124,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   u32x4 kr0[NL], vr0[NL], kr1[NL], vr1[NL], kr2[NL], vr2[NL], kr3[NL], vr3[NL];
   auto load = [&](u32x4 (&kr)[NL], u32x4 (&vr)[NL], int base) {
     const int key = min(base + kl, ke - 1);
-    const T* kp = kb + static_cast<size_t>(key) * D;
-    const T* vp = vb + static_cast<size_t>(key) * D;
+    // A paged cache: the key's row through the block table.
+    const size_t row = paged.table ? paged_row(paged, b, g, key, num_kv_heads, D) : head_off + static_cast<size_t>(key) * D;
+    const T* kp = k_cache + row;
+    const T* vp = v_cache + row;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + elem_off(i)));
@@ -307,7 +307,7 @@ hipError_t launch_split_typed(const DecodeAttnArgs& a, hipStream_t stream) {
   launch_kernel((decode_split_kernel<D, GW>), dim3(static_cast<unsigned>(items)), dim3(256), 0, stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k_cache),
                      static_cast<const float*>(a.v_cache), a.cache_lens, a.partials, a.num_q_heads, a.num_kv_heads,
-                     a.cache_capacity, a.num_splits, chunks_per_kv, a.scale_log2);
+                     a.cache_capacity, a.num_splits, chunks_per_kv, a.scale_log2, a.paged);
   return hipGetLastError();
 }
 

@@ -31,12 +31,15 @@ __device__ __forceinline__ float quarter_max(float x) {
 }
 
 // ---- 3a: one wavefront per range of steps.
-template <int D, int GW>
+// kPaged: k_cache and v_cache are pools read through `paged` (a step's 32
+// rows always lie in one page: pages hold a multiple of 32 slots).
+template <int D, int GW, bool kPaged = false>
 __device__ __forceinline__ void decode_wave(
     bf16* ktile, bf16* vtile, const int w,
     const bf16* __restrict__ q, const bf16* __restrict__ k_cache, const bf16* __restrict__ v_cache,
     const int32_t* __restrict__ cache_lens, const int32_t* __restrict__ plan, float* __restrict__ partials,
-    int num_q_heads, int num_kv_heads, int cache_capacity, int chunks_per_kv, int num_units, float scale_log2) {
+    int num_q_heads, int num_kv_heads, int cache_capacity, int chunks_per_kv, int num_units, float scale_log2,
+    PagedTable paged = PagedTable{}) {
   constexpr int KS = D / 32;               // 32-d steps of the score product
   constexpr int DBLK = D / 16;             // 16-d blocks of the output
   constexpr int CPR = D / 8;               // 16-byte chunks per key row
@@ -65,8 +68,8 @@ __device__ __forceinline__ void decode_wave(
 
   // Unit geometry (all wave-uniform).
   struct Unit {
-    int s0, s1, nkeys, b, h0;
-    const bf16* kb;
+    int s0, s1, nkeys, b, g, h0;
+    const bf16* kb;  // contiguous caches: the unit's first row
     const bf16* vb;
   };
   auto unit_at = [&](int i) {
@@ -76,6 +79,7 @@ __device__ __forceinline__ void decode_wave(
     u.b = i / nchunks;
     const int hc = i % nchunks;
     const int g = hc / chunks_per_kv;
+    u.g = g;
     u.h0 = g * group + (hc % chunks_per_kv) * GW;
     u.nkeys = min(cache_lens[u.b] + 1, cache_capacity);
     const size_t head_off = (static_cast<size_t>(u.b) * num_kv_heads + g) * cache_capacity * D;
@@ -114,10 +118,20 @@ __device__ __forceinline__ void decode_wave(
   const uint32_t lin = static_cast<uint32_t>(16 * lane);
   u32x4 kst[VLOADS], vst[VLOADS];
   auto load_step = [&](const Unit& u, int t, bool live) {
-    const uint32_t range = live ? static_cast<uint32_t>(u.nkeys) * (D * 2) : 0u;
-    const auto krs = buffer_rsrc(u.kb, range);
-    const auto vrs = buffer_rsrc(u.vb, range);
-    const uint32_t off = lin + static_cast<uint32_t>(t - u.s0) * (STEP * D * 2);
+    const bf16* kb = u.kb;
+    const bf16* vb = u.vb;
+    uint32_t range = live ? static_cast<uint32_t>(u.nkeys) * (D * 2) : 0u;
+    uint32_t off = lin + static_cast<uint32_t>(t - u.s0) * (STEP * D * 2);
+    if constexpr (kPaged) {  // the step's rows, from the page that holds them
+      const int key0 = (t - u.s0) * STEP;
+      const size_t row = paged_row(paged, u.b, u.g, key0, num_kv_heads, D);
+      kb = k_cache + row;
+      vb = v_cache + row;
+      range = live ? static_cast<uint32_t>(min(u.nkeys - key0, STEP)) * (D * 2) : 0u;
+      off = lin;
+    }
+    const auto krs = buffer_rsrc(kb, range);
+    const auto vrs = buffer_rsrc(vb, range);
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {  // 16-byte chunk 64*i + lane of the step's rows
       kst[i] = buffer_load16<true>(krs, off + 1024 * i);

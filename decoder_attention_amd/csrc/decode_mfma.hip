@@ -46,16 +46,19 @@ namespace qkra {
 namespace {
 
 // ---- 3a: one wavefront per range of steps; 4 independent wavefronts per workgroup.
-template <int D, int GW>
+// kPaged: the caches are pools read through `paged`.
+template <int D, int GW, bool kPaged>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k_cache, const bf16* __restrict__ v_cache,
     const int32_t* __restrict__ cache_lens, const int32_t* __restrict__ plan, float* __restrict__ partials,
-    int num_q_heads, int num_kv_heads, int cache_capacity, int chunks_per_kv, int num_units, float scale_log2) {
+    int num_q_heads, int num_kv_heads, int cache_capacity, int chunks_per_kv, int num_units, float scale_log2,
+    PagedTable paged) {
   constexpr int TILE = kDecodeStepKeys * (D + 8);
   __shared__ __attribute__((aligned(16))) bf16 lds[4][2 * TILE];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  dbody::decode_wave<D, GW>(lds[wave], lds[wave] + TILE, blockIdx.x * 4 + wave, q, k_cache, v_cache, cache_lens, plan,
-                            partials, num_q_heads, num_kv_heads, cache_capacity, chunks_per_kv, num_units, scale_log2);
+  dbody::decode_wave<D, GW, kPaged>(lds[wave], lds[wave] + TILE, blockIdx.x * 4 + wave, q, k_cache, v_cache,
+                                    cache_lens, plan, partials, num_q_heads, num_kv_heads, cache_capacity,
+                                    chunks_per_kv, num_units, scale_log2, paged);
 }
 
 // ---- 3b: merge the portions of one (request, head); one wavefront each.
@@ -123,14 +126,19 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
   for (int e = 0; e < PER_LANE; ++e) dst[lane + 64 * e] = static_cast<bf16>(acc[e] * inv);
 }
 
+template <int D, int GW, bool kPaged>
+hipError_t launch_mfma_paged(const DecodeAttnArgs& a, hipStream_t stream) {
+  const int chunks_per_kv = (a.num_q_heads / a.num_kv_heads) / GW;
+  launch_kernel((decode_mfma_kernel<D, GW, kPaged>), dim3(kDecodeWaves / 4), dim3(256), 0, stream,
+                static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k_cache),
+                static_cast<const bf16*>(a.v_cache), a.cache_lens, a.plan, a.partials, a.num_q_heads,
+                a.num_kv_heads, a.cache_capacity, chunks_per_kv, a.num_units, a.scale_log2, a.paged);
+  return hipGetLastError();
+}
+
 template <int D, int GW>
 hipError_t launch_mfma_typed(const DecodeAttnArgs& a, hipStream_t stream) {
-  const int chunks_per_kv = (a.num_q_heads / a.num_kv_heads) / GW;
-  launch_kernel((decode_mfma_kernel<D, GW>), dim3(kDecodeWaves / 4), dim3(256), 0, stream,
-                     static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k_cache),
-                     static_cast<const bf16*>(a.v_cache), a.cache_lens, a.plan, a.partials, a.num_q_heads,
-                     a.num_kv_heads, a.cache_capacity, chunks_per_kv, a.num_units, a.scale_log2);
-  return hipGetLastError();
+  return a.paged.table ? launch_mfma_paged<D, GW, true>(a, stream) : launch_mfma_paged<D, GW, false>(a, stream);
 }
 
 template <int D>

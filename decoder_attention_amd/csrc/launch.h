@@ -44,6 +44,28 @@ enum KernelId : int {
   kNumKernels = 12,
 };
 
+// Paged K/V caches: slot s of request b is row s % P of page table[b][s / P]
+// of a pool [num_pages, Hkv, P, D] (P = 1 << page_shift).  A null table means
+// the contiguous caches [B, Hkv, S_cap, D].  Page numbers are clamped to the
+// pool, so out-of-contract tables cannot address past it.
+struct PagedTable {
+  const int32_t* table = nullptr;  // int32 [num_seqs, pages_per_seq]
+  int pages_per_seq = 0, page_shift = 0, num_pages = 0;
+};
+
+// Element offset of the first element of row s of request b, KV head g.
+__device__ __forceinline__ size_t paged_row(const PagedTable& pt, int b, int g, int s, int num_kv_heads, int head_dim) {
+  int page = pt.table[static_cast<size_t>(b) * pt.pages_per_seq + (s >> pt.page_shift)];
+  page = min(max(page, 0), pt.num_pages - 1);
+  return ((static_cast<size_t>(page) * num_kv_heads + g) * (static_cast<size_t>(1) << pt.page_shift) +
+          (s & ((1 << pt.page_shift) - 1))) * head_dim;
+}
+__device__ __forceinline__ size_t cache_row(const PagedTable& pt, int b, int g, int s, int num_kv_heads,
+                                            int cache_capacity, int head_dim) {
+  if (pt.table != nullptr) return paged_row(pt, b, g, s, num_kv_heads, head_dim);
+  return ((static_cast<size_t>(b) * num_kv_heads + g) * cache_capacity + s) * head_dim;
+}
+
 // Kernel 1: per token row, RMSNorm + RoPE of the Q and K heads; q~ to
 // q_out[row, Hq, D], k~ and v to the cache at (request, slot).
 struct QkNormRopeArgs {
@@ -65,6 +87,7 @@ struct QkNormRopeArgs {
   void* v_cache;
   int32_t* plan;            // bf16 decode: one more block builds the split kernel's plan there (or null)
   int plan_units, plan_nchunks;
+  PagedTable paged;         // table null: contiguous caches
 };
 hipError_t launch_qknorm_rope(const QkNormRopeArgs& a, hipStream_t stream);
 
@@ -85,6 +108,7 @@ struct PrefillAttnArgs {
   void* out;                // [N, Hq*D]
   int num_q_heads, num_kv_heads, head_dim, cache_capacity, num_seqs, max_seqlen;
   float scale_log2;         // log2(e) / sqrt(D)
+  PagedTable paged;         // table null: contiguous caches (k_cache/v_cache are the pools otherwise)
 };
 // bf16: two kernels over the same grid, both launched by every call.
 // unshifted = true launches the one that takes p = 2^s without a shift (a
@@ -147,6 +171,7 @@ struct DecodeAttnArgs {
   int num_splits;           // fp32 path
   int num_units, heads_per_wave;  // bf16 path
   float scale_log2;
+  PagedTable paged;         // table null: contiguous caches (k_cache/v_cache are the pools otherwise)
 };
 hipError_t launch_decode_split(const DecodeAttnArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeAttnArgs& a, hipStream_t stream);

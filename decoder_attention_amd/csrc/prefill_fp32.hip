@@ -23,7 +23,8 @@ template <int D>
 __global__ __launch_bounds__(NT) void prefill_fp32_kernel(
     const float* __restrict__ q, const float* __restrict__ k_cache, const float* __restrict__ v_cache,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ past_lens, float* __restrict__ out,
-    int num_q_heads, int num_kv_heads, int cache_capacity, int num_seqs, int tiles_per_seq, float scale_log2) {
+    int num_q_heads, int num_kv_heads, int cache_capacity, int num_seqs, int tiles_per_seq, float scale_log2,
+    PagedTable paged) {
   constexpr int HD = D / 2;
   __shared__ float sK[KT][D + 1];
   __shared__ float sV[KT][D + 1];
@@ -63,8 +64,12 @@ __global__ __launch_bounds__(NT) void prefill_fp32_kernel(
     for (int i = tid; i < KT * D; i += NT) {
       const int r = i / D, c = i % D;
       const int key = k0 + r;
-      sK[r][c] = key < kv_end ? k_cache[head_off + static_cast<size_t>(key) * D + c] : 0.f;
-      sV[r][c] = key < kv_end ? v_cache[head_off + static_cast<size_t>(key) * D + c] : 0.f;
+      // A paged cache: the key's row through the block table.
+      const size_t row = key >= kv_end ? 0
+                         : paged.table ? paged_row(paged, seq, g, key, num_kv_heads, D)
+                                       : head_off + static_cast<size_t>(key) * D;
+      sK[r][c] = key < kv_end ? k_cache[row + c] : 0.f;
+      sV[r][c] = key < kv_end ? v_cache[row + c] : 0.f;
     }
     __syncthreads();
     float s[KT];
@@ -115,7 +120,7 @@ hipError_t launch_typed(const PrefillAttnArgs& a, hipStream_t stream) {
   launch_kernel((prefill_fp32_kernel<D>), dim3(static_cast<unsigned>(items)), dim3(NT), 0, stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k_cache),
                      static_cast<const float*>(a.v_cache), a.cu_seqlens, a.past_lens, static_cast<float*>(a.out),
-                     a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.num_seqs, tiles, a.scale_log2);
+                     a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.num_seqs, tiles, a.scale_log2, a.paged);
   return hipGetLastError();
 }
 

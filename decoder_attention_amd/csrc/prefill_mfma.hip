@@ -159,7 +159,9 @@ __device__ __forceinline__ bool scores_bounded(WeightMax w, int past, float limi
 // slowed both.  Every call launches both kernels over the same grid; each
 // workgroup of the one whose path its request and the weights do not select
 // returns at once.
-template <int D, int HC, bool kBounded, int kDecGW = 0>
+// kPaged: k_cache and v_cache are pools read through `paged` (a K/V tile of
+// BN keys always lies in one page: pages hold a multiple of BN slots).
+template <int D, int HC, bool kBounded, int kDecGW = 0, bool kPaged = false>
 __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ q_norm_weight, const bf16* __restrict__ k_norm_weight,
     const float* __restrict__ rope_table,
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ past_lens, bf16* __restrict__ out,
     int num_q_heads, int num_kv_heads,
     int cache_capacity, int num_seqs, int tiles_per_seq, int chunks_per_kv, int num_items,
-    float rms_eps, float scale_log2, float bound_limit, DecodeRole dec) {
+    float rms_eps, float scale_log2, float bound_limit, DecodeRole dec, PagedTable paged) {
   constexpr int TBN = 8 / HC;       // token blocks (of 32) per workgroup
   constexpr int TM = 32 * TBN;      // tokens per workgroup
   constexpr int DS = D / 16;        // k-steps over D for the scores
@@ -379,9 +381,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
 
   auto load_tile = [&](int kt) {
     const int k0 = kt * BN;
-    const uint32_t bytes = static_cast<uint32_t>(kv_end - k0) * D * 2;
-    const auto rk = buffer_rsrc(kbase + static_cast<size_t>(k0) * D, bytes);
-    const auto rv = buffer_rsrc(vbase + static_cast<size_t>(k0) * D, bytes);
+    uint32_t bytes = static_cast<uint32_t>(kv_end - k0) * D * 2;
+    const bf16* kt_base = kbase + static_cast<size_t>(k0) * D;
+    const bf16* vt_base = vbase + static_cast<size_t>(k0) * D;
+    if constexpr (kPaged) {  // the tile's rows, from the page that holds them
+      const size_t row = paged_row(paged, seq, g, k0, num_kv_heads, D);
+      kt_base = k_cache + row;
+      vt_base = v_cache + row;
+      bytes = static_cast<uint32_t>(min(kv_end - k0, BN)) * D * 2;
+    }
+    const auto rk = buffer_rsrc(kt_base, bytes);
+    const auto rv = buffer_rsrc(vt_base, bytes);
     static_for<KCHUNKS>([&](auto i) {
       const int c = tid + NTHREADS * i;  // 16-byte chunk c of the tile's contiguous rows
       if (KCH % NTHREADS == 0 || c < KCH) kreg[i] = buffer_load16<false>(rk, static_cast<uint32_t>(c) * 16);
@@ -650,7 +660,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   }
 }
 
-template <int D, int HC, bool kBounded>
+template <int D, int HC, bool kBounded, bool kPaged>
 hipError_t launch_typed(const PrefillAttnArgs& a, hipStream_t stream) {
   constexpr int TM = 32 * (8 / HC);
   const int group = a.num_q_heads / a.num_kv_heads;
@@ -661,23 +671,28 @@ hipError_t launch_typed(const PrefillAttnArgs& a, hipStream_t stream) {
   const long long grid = (items + 7) / 8 * 8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float bound_limit = BOUND_LOG2 / (1.02f * static_cast<float>(D) * a.scale_log2);
-  launch_kernel((prefill_mfma_kernel<D, HC, kBounded>), dim3(static_cast<unsigned>(grid)), dim3(NTHREADS), 0, stream,
+  launch_kernel((prefill_mfma_kernel<D, HC, kBounded, 0, kPaged>), dim3(static_cast<unsigned>(grid)), dim3(NTHREADS), 0, stream,
                      static_cast<const bf16*>(a.qkv), static_cast<const bf16*>(a.q_norm_weight),
                      static_cast<const bf16*>(a.k_norm_weight), a.rope_table,
                      static_cast<const bf16*>(a.k_cache),
                      static_cast<const bf16*>(a.v_cache), a.cu_seqlens, a.past_lens, static_cast<bf16*>(a.out),
                      a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.num_seqs, tiles, chunks_per_kv,
-                     static_cast<int>(items), a.rms_eps, a.scale_log2, bound_limit, DecodeRole{});
+                     static_cast<int>(items), a.rms_eps, a.scale_log2, bound_limit, DecodeRole{}, a.paged);
   return hipGetLastError();
+}
+
+template <int D, bool kBounded, bool kPaged>
+hipError_t launch_grouped(const PrefillAttnArgs& a, hipStream_t stream) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  if (group % 8 == 0) return launch_typed<D, 8, kBounded, kPaged>(a, stream);
+  if (group % 4 == 0) return launch_typed<D, 4, kBounded, kPaged>(a, stream);
+  if (group % 2 == 0) return launch_typed<D, 2, kBounded, kPaged>(a, stream);
+  return launch_typed<D, 1, kBounded, kPaged>(a, stream);
 }
 
 template <int D, bool kBounded>
 hipError_t launch_dim(const PrefillAttnArgs& a, hipStream_t stream) {
-  const int group = a.num_q_heads / a.num_kv_heads;
-  if (group % 8 == 0) return launch_typed<D, 8, kBounded>(a, stream);
-  if (group % 4 == 0) return launch_typed<D, 4, kBounded>(a, stream);
-  if (group % 2 == 0) return launch_typed<D, 2, kBounded>(a, stream);
-  return launch_typed<D, 1, kBounded>(a, stream);
+  return a.paged.table ? launch_grouped<D, kBounded, true>(a, stream) : launch_grouped<D, kBounded, false>(a, stream);
 }
 
 }  // namespace
@@ -702,7 +717,7 @@ hipError_t launch_fused_typed(const PrefillAttnArgs& a, const DecodeAttnArgs& d,
                      static_cast<const bf16*>(a.k_norm_weight), a.rope_table, static_cast<const bf16*>(a.k_cache),
                      static_cast<const bf16*>(a.v_cache), a.cu_seqlens, a.past_lens, static_cast<bf16*>(a.out),
                      a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.num_seqs, tiles, chunks_per_kv,
-                     static_cast<int>(items), a.rms_eps, a.scale_log2, bound_limit, dec);
+                     static_cast<int>(items), a.rms_eps, a.scale_log2, bound_limit, dec, PagedTable{});
   return hipGetLastError();
 }
 

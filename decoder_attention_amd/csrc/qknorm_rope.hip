@@ -22,7 +22,9 @@
 // cross-lane traffic; only the sum of squares is reduced across the D/8 lanes.
 // Loads and stores are 8 B (bf16) or 16 B (fp32) per lane, contiguous across
 // the lanes of a head.  A wavefront's first four passes are loaded before the
-// request lookup and the angle computation, so those latencies overlap.
+// request lookup and the angle computation, so those latencies overlap.  With
+// a block table the cache rows are found through it (a paged pool); slots
+// still count from the request's first entry.
 
 #include "decode_plan.h"
 #include "device_common.h"
@@ -59,7 +61,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
     const int32_t* __restrict__ slot_offsets, int decode_mode,
     int num_seqs, int num_q_heads, int num_kv_heads, int cache_capacity, float eps,
     double log2_base, T* __restrict__ q_out, float* __restrict__ rope_table, T* __restrict__ k_cache,
-    T* __restrict__ v_cache, int num_rows, int32_t* __restrict__ plan, int plan_units, int plan_nchunks) {
+    T* __restrict__ v_cache, int num_rows, int32_t* __restrict__ plan, int plan_units, int plan_nchunks,
+    PagedTable paged) {
   using Raw = typename Raw4<T>::type;
   constexpr int HALF = D / 2;
   constexpr int LPH = HALF / 4;  // lanes per head row
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
     if (head >= num_q_heads + num_kv_heads) {  // V head: bit copy into the cache
       if (!slot_ok) continue;
       const int g = head - num_q_heads - num_kv_heads;
-      T* dst = v_cache + ((static_cast<size_t>(req) * num_kv_heads + g) * cache_capacity + slot) * D;
+      T* dst = v_cache + cache_row(paged, req, g, slot, num_kv_heads, cache_capacity, D);
       *reinterpret_cast<Raw*>(dst + i0) = r1;
       *reinterpret_cast<Raw*>(dst + HALF + i0) = r2;
       continue;
@@ -194,8 +197,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
       y2[e] = b * cs[e] + a * sn[e];
     }
     T* dst = is_q ? q_out + (static_cast<size_t>(row_id) * num_q_heads + head) * D
-                  : k_cache + ((static_cast<size_t>(req) * num_kv_heads + (head - num_q_heads)) *
-                                   cache_capacity + slot) * D;
+                  : k_cache + cache_row(paged, req, head - num_q_heads, slot, num_kv_heads, cache_capacity, D);
     Raw o1, o2;
     pack4(y1, &o1);
     pack4(y2, &o2);
@@ -219,7 +221,7 @@ hipError_t launch_typed(const QkNormRopeArgs& a, hipStream_t stream) {
                      a.decode_mode,
                      a.num_seqs, a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.rms_eps,
                      a.log2_rope_base, static_cast<T*>(a.q_out), a.rope_table, static_cast<T*>(a.k_cache),
-                     static_cast<T*>(a.v_cache), a.num_rows, a.plan, a.plan_units, a.plan_nchunks);
+                     static_cast<T*>(a.v_cache), a.num_rows, a.plan, a.plan_units, a.plan_nchunks, a.paged);
   return hipGetLastError();
 }
 

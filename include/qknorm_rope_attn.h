@@ -242,6 +242,78 @@ QKRA_API int32_t qknorm_rope_attn_mixed_step(
     void* decode_out, void* decode_workspace, size_t decode_workspace_bytes, void* hip_stream);
 
 /*
+ * ---- Paged K/V cache -------------------------------------------------------
+ * The pages defer the optimised cache to a chapter they only name (zero-to-
+ * sglang, "Chapter 3 Forward Pass and Generation (Code Walkthrough)", opening
+ * paragraph and references: "Chapter 4: KV Cache Optimization"; concept
+ * chapter, section 4).  The reading here: a paged cache is the same
+ * per-request cache with its slots stored in fixed-size pages of a shared
+ * pool, found through a block table, so every result equals the contiguous
+ * calls' on the logical cache the table describes.
+ *
+ *   k_pool, v_pool [num_pages, Hkv, page_size, D] in the dtype, 16-byte
+ *                  aligned: element (p, g, r, d) at ((p * Hkv + g) * page_size
+ *                  + r) * D + d.  A page holds page_size consecutive slots of
+ *                  one request for every KV head.
+ *   block_table    int32 [num_seqs, pages_per_seq] (device): slot s of
+ *                  request b is row s % page_size of page
+ *                  block_table[b * pages_per_seq + s / page_size].  Each
+ *                  request can hold pages_per_seq * page_size slots (the
+ *                  capacity checked as cache_capacity is for the contiguous
+ *                  calls).  Entries the call does not reach may hold anything.
+ *   page_size      64, 128, 256, 512 or 1024 (QKRA_ERR_UNSUPPORTED otherwise):
+ *                  a page then holds whole 64-key prefill tiles and 32-key
+ *                  decode steps.
+ * Pages a call writes (the slots of its new tokens) must belong to one request
+ * each; pages may be shared between requests for reading (a common prefix).
+ * Table entries the call reaches must lie in [0, num_pages) (the caller's
+ * contract, like cu_seqlens; the kernels clamp them to the pool, so a bad
+ * entry gives wrong values, never an access outside the pool).  The pools and
+ * the table may not overlap out, the workspace or each other's written
+ * ranges (QKRA_ERR_ALIASING).
+ */
+typedef struct qkra_paged_cache {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* block_table;
+  int32_t num_pages;       /* > 0 */
+  int32_t page_size;       /* 64, 128, 256, 512 or 1024 */
+  int32_t pages_per_seq;   /* > 0: row length of block_table */
+  int32_t reserved;        /* must be 0 */
+} qkra_paged_cache;
+
+/*
+ * qknorm_rope_attn_decode on a paged cache: the new token's k~ and v go to
+ * slot L_b of request b through the table, then its query attends over slots
+ * 0..L_b.  Requires max_cache_len + 1 <= pages_per_seq * page_size
+ * (QKRA_ERR_CAPACITY).  Workspace as for qknorm_rope_attn_decode (the same
+ * size query, QKRA_MODE_DECODE).
+ */
+QKRA_API int32_t qknorm_rope_attn_decode_paged(const qkra_config* cfg, const void* qkv,
+                                               const void* q_norm_weight, const void* k_norm_weight,
+                                               const int32_t* positions, const int32_t* cache_lens,
+                                               int32_t num_seqs, int32_t max_cache_len,
+                                               const qkra_paged_cache* cache, void* out, void* workspace,
+                                               size_t workspace_bytes, void* hip_stream);
+
+/*
+ * qknorm_rope_attn_prefill_append on a paged cache: request r's new token j is
+ * written to slot P_r + j through the table and attends over slots
+ * 0..P_r + j.  cache_lens may be NULL (with max_cache_len 0): every P_r = 0,
+ * a prefill into the paged cache.  Requires max_cache_len + max_seqlen <=
+ * pages_per_seq * page_size.  Workspace as for qknorm_rope_attn_prefill
+ * (QKRA_MODE_PREFILL).
+ */
+QKRA_API int32_t qknorm_rope_attn_prefill_append_paged(const qkra_config* cfg, const void* qkv,
+                                                       const void* q_norm_weight, const void* k_norm_weight,
+                                                       const int32_t* positions, const int32_t* cu_seqlens,
+                                                       const int32_t* cache_lens, int32_t num_tokens,
+                                                       int32_t num_seqs, int32_t max_seqlen,
+                                                       int32_t max_cache_len, const qkra_paged_cache* cache,
+                                                       void* out, void* workspace, size_t workspace_bytes,
+                                                       void* hip_stream);
+
+/*
  * Workspace size in bytes for a call (0 when the configuration is invalid).
  * mode QKRA_MODE_PREFILL: n = num_tokens, max_len = max_seqlen.
  * mode QKRA_MODE_DECODE:  n = num_seqs,   max_len = max_cache_len.
@@ -332,8 +404,13 @@ QKRA_API int32_t qknorm_rope_attn_argmax(int32_t dtype, const void* logits, int3
                                          size_t workspace_bytes, void* hip_stream);
 
 /*
- * Per-kernel timing, for benchmarks.  While enabled, every kernel launch is
- * bracketed by two hipEvents recorded on the launch stream.
+ * Per-kernel timing, for benchmarks.  `enable` is a mask over kernel ids (bit k
+ * times kernel id k; -1 times every kernel, 0 switches timing off).  A timed
+ * launch records two hipEvents on its own dispatch, at the start and the end
+ * of the kernel's execution.  The events come from a pool created by the first
+ * call that enables timing (QKRA_ERR_HIP if that fails), never by the
+ * attention calls; a launch that finds the pool empty runs untimed.  This is
+ * process-wide benchmark instrumentation.
  * qknorm_rope_attn_read_kernel_timing() waits for those events, writes for each
  * kernel id k < max_kernels the summed duration in milliseconds (ms_total[k])
  * and the number of launches (launches[k]), clears the record and returns the

@@ -439,3 +439,65 @@ def test_decode_noalloc_refuses_sizes_past_its_scratch():
     assert da.qknorm_rope_attn_decode_noalloc(cfg, None, None, None, None, None, 0, 0, None, None, 1, None, 0) == 0
     assert da.qknorm_rope_attn_decode_noalloc(cfg, BASE, BASE, BASE, BASE, BASE, -1, 0, BASE, BASE, 1, BASE, 0) == \
         da.QKRA_ERR_INVALID_ARGUMENT
+
+
+# ---- paged caches -------------------------------------------------------------------
+
+def paged_decode_args(**over):
+    """Four decodes on a paged pool of 40 pages of 64 slots (fake device addresses: host checks only)."""
+    cfg = over.pop("cfg", da.make_config(32, 8, 128, da.QKRA_BF16))
+    cache = dict(k_pool=BASE + 100 * MB, v_pool=BASE + 200 * MB, block_table=BASE + 68 * MB, num_pages=40,
+                 page_size=64, pages_per_seq=10)
+    for k in list(over):
+        if k in cache:
+            cache[k] = over.pop(k)
+    a = dict(qkv=BASE, q_norm_weight=BASE + 64 * MB, k_norm_weight=BASE + 65 * MB, positions=BASE + 66 * MB,
+             cache_lens=BASE + 67 * MB, num_seqs=4, max_cache_len=639, out=BASE + 300 * MB, workspace=BASE + 400 * MB,
+             workspace_bytes=64 * MB, stream=0)
+    a.update(over)
+    return cfg, da.make_paged_cache(**cache), a
+
+
+def call_paged_decode(cfg, cache, a):
+    return da.qknorm_rope_attn_decode_paged(cfg, a["qkv"], a["q_norm_weight"], a["k_norm_weight"], a["positions"],
+                                            a["cache_lens"], a["num_seqs"], a["max_cache_len"], cache, a["out"],
+                                            a["workspace"], a["workspace_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(page_size=32), da.QKRA_ERR_UNSUPPORTED),                 # pages must hold 64..1024 slots
+    (dict(page_size=96), da.QKRA_ERR_UNSUPPORTED),                 # and a power of two
+    (dict(page_size=2048), da.QKRA_ERR_UNSUPPORTED),
+    (dict(num_pages=0), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(pages_per_seq=0), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(block_table=None), da.QKRA_ERR_INVALID_ARGUMENT),
+    (dict(block_table=BASE + 68 * MB + 2), da.QKRA_ERR_INVALID_ARGUMENT),   # misaligned table
+    (dict(max_cache_len=640), da.QKRA_ERR_CAPACITY),               # 10 pages of 64 hold 640 slots: no room
+    (dict(out=BASE + 68 * MB), da.QKRA_ERR_ALIASING),              # out over the block table
+    (dict(workspace=BASE + 100 * MB + 4096), da.QKRA_ERR_ALIASING),  # workspace inside the K pool
+    (dict(v_pool=BASE + 100 * MB + 64), da.QKRA_ERR_ALIASING),     # pools overlap
+])
+def test_paged_decode_argument_checks(over, status):
+    cfg, cache, a = paged_decode_args(**over)
+    assert call_paged_decode(cfg, cache, a) == status
+    assert da.qknorm_rope_attn_last_hip_error() == 0
+
+
+def test_paged_calls_need_a_descriptor_and_accept_empty_batches():
+    cfg, cache, a = paged_decode_args()
+    assert da.qknorm_rope_attn_decode_paged(cfg, a["qkv"], a["q_norm_weight"], a["k_norm_weight"], a["positions"],
+                                            a["cache_lens"], 4, 100, None, a["out"], a["workspace"],
+                                            a["workspace_bytes"], 0) == da.QKRA_ERR_INVALID_ARGUMENT
+    assert da.qknorm_rope_attn_decode_paged(cfg, None, None, None, None, None, 0, 0, None, None, None, 0, 0) == 0
+    bad = da.make_paged_cache(BASE, BASE, BASE, 1, 64, 1)
+    bad.reserved = 1
+    assert call_paged_decode(cfg, bad, a) == da.QKRA_ERR_INVALID_ARGUMENT
+    # The append: capacity counts the history plus the chunk; a null cache_lens (a prefill) needs max_cache_len 0.
+    f = da.qknorm_rope_attn_prefill_append_paged
+    args = (cfg, BASE, BASE + 64 * MB, BASE + 65 * MB, BASE + 66 * MB, BASE + 69 * MB)
+    assert f(*args, BASE + 67 * MB, 64, 1, 64, 577, cache, BASE + 300 * MB, BASE + 400 * MB, 64 * MB, 0) == \
+        da.QKRA_ERR_CAPACITY
+    assert f(*args, None, 64, 1, 64, 5, cache, BASE + 300 * MB, BASE + 400 * MB, 64 * MB, 0) == \
+        da.QKRA_ERR_INVALID_ARGUMENT
+    assert f(*args, None, 0, 0, 0, 0, None, None, None, 0, 0) == 0
+    assert da.qknorm_rope_attn_last_hip_error() == 0

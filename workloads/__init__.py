@@ -21,5 +21,8 @@ from .synth import (  # noqa: F401
     make_append_inputs,
     make_norm_inputs,
     make_next_token_inputs,
+    PagedCache,
+    make_block_table,
+    paged_from_contiguous,
     qkv_width,
 )

@@ -271,6 +271,70 @@ def make_append_inputs(h: HeadConfig, past_lens: Sequence[int], chunk_lens: Sequ
 
 
 # ---------------------------------------------------------------------------
+# Paged caches: the same per-request cache contents stored in pages of a pool
+# [num_pages, Hkv, P, D], found through a block table [B, pages_per_seq].
+# Tables are random permutations of the pool's pages, so pages are out of
+# order and the pool has pages no request owns (holes, filled like unused
+# slots).  Values are the seeded contiguous contents, copied page by page.
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class PagedCache:
+    page_size: int
+    block_table: torch.Tensor   # int32 [B, pages_per_seq]
+    k_pool: torch.Tensor        # [num_pages, Hkv, page_size, D]
+    v_pool: torch.Tensor
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    @property
+    def pages_per_seq(self) -> int:
+        return int(self.block_table.shape[1])
+
+
+def make_block_table(num_seqs: int, pages_per_seq: int, num_pages: int, seed: int,
+                     shared_prefix_pages: int = 0) -> torch.Tensor:
+    """Distinct random pages for every (request, page index); with shared_prefix_pages = k every request's
+    first k entries name the same k pages (a prefix stored once)."""
+    own = pages_per_seq - shared_prefix_pages
+    need = shared_prefix_pages + num_seqs * own
+    if num_pages < need:
+        raise ValueError(f"{num_pages} pages cannot hold {need}")
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(num_pages, generator=g)
+    shared = perm[:shared_prefix_pages]
+    rest = perm[shared_prefix_pages:need].reshape(num_seqs, own)
+    table = torch.cat([shared.expand(num_seqs, shared_prefix_pages), rest], dim=1)
+    return table.to(torch.int32).contiguous()
+
+
+def paged_from_contiguous(k_cache: torch.Tensor, v_cache: torch.Tensor, page_size: int, seed: int,
+                          spare_pages: int = 3, parity: bool = True, shared_prefix_pages: int = 0) -> PagedCache:
+    """A paged copy of contiguous caches [B, Hkv, S, D]: request b's slot s goes to row s % P of page
+    table[b, s // P].  The pool holds `spare_pages` pages that no request owns.  With shared_prefix_pages = k the
+    first k * P slots of request 0 are the shared prefix every request reads (the other requests' own values
+    there are not kept)."""
+    b, hkv, cap, d = k_cache.shape
+    pps = max(1, -(-cap // page_size))
+    num_pages = shared_prefix_pages + b * (pps - shared_prefix_pages) + spare_pages
+    table = make_block_table(b, pps, num_pages, seed, shared_prefix_pages)
+    fill = _sentinel(parity)
+    pools = []
+    for c in (k_cache, v_cache):
+        pool = torch.full((num_pages, hkv, page_size, d), fill, dtype=c.dtype, device=c.device)
+        padded = torch.full((b, hkv, pps * page_size, d), fill, dtype=c.dtype, device=c.device)
+        padded[:, :, :cap] = c
+        pages = padded.reshape(b, hkv, pps, page_size, d).permute(0, 2, 1, 3, 4)  # [B, pps, Hkv, P, D]
+        tab = table.to(c.device).long()
+        for r in reversed(range(b)):  # request 0 last: the shared pages hold its values
+            pool[tab[r]] = pages[r]
+        pools.append(pool)
+    return PagedCache(page_size, table.to(k_cache.device), pools[0], pools[1])
+
+
+# ---------------------------------------------------------------------------
 # Named workloads.  Head shapes follow the Qwen3 configurations the pages
 # trace (Qwen3-4B: 32 query heads, 8 KV heads, head_dim 128 -- "transformer
 # basics", "Qwen3 analogies"); lengths and mixes are the benchmark's.
