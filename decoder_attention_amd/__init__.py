@@ -27,6 +27,11 @@ from .binding import (  # noqa: F401
     make_paged_cache,
     check,
     exported_symbols,
+    calibration_lib,
+    calibration_symbols,
+    qkra_calibrate_stream_read,
+    qkra_calibrate_mfma_bf16,
+    qkra_calibrate_mfma_flop,
     lib,
     make_config,
     qknorm_rope_attn_prefill,

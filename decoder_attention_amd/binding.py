@@ -123,6 +123,49 @@ def exported_symbols():
     return sorted(_SIGNATURES)
 
 
+# ---- the roofline calibration library (include/qkra_calibrate.h) ---------------
+_calib = None
+_CALIB_SIGNATURES = {
+    "qkra_calibrate_stream_read": (_I32, [_P, _SZ, _P, _I32, _P]),
+    "qkra_calibrate_mfma_bf16": (_I32, [ctypes.c_int64, _P, _I32, _P]),
+    "qkra_calibrate_mfma_flop": (_SZ, [ctypes.c_int64, _I32]),
+}
+
+
+def calibration_lib() -> ctypes.CDLL:
+    """Load libqkra_calibrate.so (raises if it has not been built)."""
+    global _calib
+    if _calib is None:
+        from .build import CALIB_LIB_PATH
+
+        if not os.path.exists(CALIB_LIB_PATH):
+            raise RuntimeError(f"calibration library {CALIB_LIB_PATH} is missing; build it first")
+        handle = ctypes.CDLL(CALIB_LIB_PATH)
+        for name, (res, args) in _CALIB_SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _calib = handle
+    return _calib
+
+
+def calibration_symbols():
+    return sorted(_CALIB_SIGNATURES)
+
+
+def qkra_calibrate_stream_read(buf, nbytes: int, sink, workgroups: int, stream=None) -> int:
+    return calibration_lib().qkra_calibrate_stream_read(_ptr(buf), int(nbytes), _ptr(sink), int(workgroups),
+                                                        _stream(stream))
+
+
+def qkra_calibrate_mfma_bf16(iterations: int, sink, workgroups: int, stream=None) -> int:
+    return calibration_lib().qkra_calibrate_mfma_bf16(int(iterations), _ptr(sink), int(workgroups), _stream(stream))
+
+
+def qkra_calibrate_mfma_flop(iterations: int, workgroups: int) -> int:
+    return int(calibration_lib().qkra_calibrate_mfma_flop(int(iterations), int(workgroups)))
+
+
 def _ptr(x) -> Optional[int]:
     if x is None:
         return None

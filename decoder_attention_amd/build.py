@@ -22,6 +22,9 @@ LIB_NAME = "libqknorm_rope_attn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 SOURCES = ["qknorm_rope.hip", "prefill_mfma.hip", "prefill_fp32.hip", "decode.hip", "decode_mfma.hip", "layer_ops.hip", "api.hip"]
+# The benchmark's roofline calibration kernels: a library of their own, outside the attention ABI.
+CALIB_SOURCES = ["calibrate.hip"]
+CALIB_LIB_PATH = os.path.join(PKG_DIR, "libqkra_calibrate.so")
 ARCH = "gfx950"
 CFLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-fvisibility=hidden",
@@ -49,7 +52,7 @@ def _run(cmd, verbose):
 
 
 def build_library(verbose: bool = False, jobs: int | None = None, extra_flags=None, out_path: str | None = None,
-                  build_dir: str | None = None) -> str:
+                  build_dir: str | None = None, sources=None) -> str:
     """Compile every HIP source for gfx950 and link the shared library; returns its path."""
     hipcc = _hipcc()
     build_dir = build_dir or BUILD_DIR
@@ -58,7 +61,7 @@ def build_library(verbose: bool = False, jobs: int | None = None, extra_flags=No
     flags = CFLAGS + list(extra_flags or [])
     objs = []
     cmds = []
-    for src in SOURCES:
+    for src in sources or SOURCES:
         obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmds.append([hipcc] + flags + ["-c", os.path.join(CSRC, src), "-o", obj])
@@ -72,5 +75,11 @@ def build_library(verbose: bool = False, jobs: int | None = None, extra_flags=No
     return out_path
 
 
+def build_calibration(verbose: bool = False) -> str:
+    """The roofline calibration library (libqkra_calibrate.so); returns its path."""
+    return build_library(verbose, out_path=CALIB_LIB_PATH, sources=CALIB_SOURCES)
+
+
 if __name__ == "__main__":
     print(build_library(verbose="-v" in sys.argv))
+    print(build_calibration(verbose="-v" in sys.argv))

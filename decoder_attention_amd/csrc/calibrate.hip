@@ -1,0 +1,105 @@
+// Roofline calibration for the benchmark: what this part sustains on a plain
+// streaming read of HBM and on back-to-back bf16 matrix-core instructions,
+// measured beside the attention kernels so that their roofline fractions can
+// also be stated against what is reachable here, not only against the
+// published peaks.  (The concept chapter's section 4.3 splits the work into
+// compute-bound prefill and bandwidth-bound decode; these are the two
+// ceilings.)
+//
+// * stream read: every wavefront reads a contiguous share of the buffer in
+//   16-byte non-temporal pieces, 1 KB per instruction, eight instructions in
+//   flight (the access shape of the decode's K/V stream).  The XOR of
+//   everything read is stored only if it equals a value it cannot take, so no
+//   load is removed and nothing is written.
+// * MFMA loop: each wavefront runs four independent chains of
+//   v_mfma_f32_32x32x16_bf16 on register operands (32768 FLOP each), two
+//   wavefronts per SIMD, as the prefill kernel runs.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qkra_calibrate.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kReadThreads = 256;
+constexpr int kReadUnroll = 8;
+
+// Each wavefront streams a contiguous share of the buffer, 1 KB per load
+// instruction (16 bytes per lane, lane-linear) and eight instructions in
+// flight, as the decode's K/V stream does.
+__global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* __restrict__ buf, size_t pieces,
+                                                                   uint32_t* __restrict__ sink) {
+  constexpr size_t kStep = 64 * kReadUnroll;  // pieces per wavefront iteration
+  const size_t waves = static_cast<size_t>(gridDim.x) * (kReadThreads / 64);
+  const size_t wave = static_cast<size_t>(blockIdx.x) * (kReadThreads / 64) + (threadIdx.x >> 6);
+  const size_t lane = threadIdx.x & 63;
+  const size_t share = (pieces / waves) / kStep * kStep;  // whole iterations per wavefront
+  const u32x4* p = buf + wave * share + lane;
+  uint32_t acc = 0;
+  for (size_t i = 0; i < share; i += kStep) {
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(p + i + 64 * u);
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (size_t i = waves * share + wave * 64 + lane; i < pieces; i += waves * 64) {  // the remainder
+    const u32x4 v = __builtin_nontemporal_load(buf + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9e3779b9u && threadIdx.x == 1023) sink[0] = acc;  // never taken: threadIdx.x < 256
+}
+
+__global__ __launch_bounds__(256, 2) void mfma_loop_kernel(int64_t iterations, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = static_cast<__bf16>(static_cast<float>((lane + e) & 7) * 0.125f);
+    b[e] = static_cast<__bf16>(static_cast<float>((lane * 3 + e) & 7) * 0.0625f);
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int64_t it = 0; it < iterations; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s += c0[e] + c1[e] + c2[e] + c3[e];
+  if (s == -1.0f) sink[blockIdx.x] = s;  // never taken: every product is non-negative
+}
+
+}  // namespace
+
+extern "C" {
+
+QKRA_CALIB_API size_t qkra_calibrate_mfma_flop(int64_t iterations, int32_t workgroups) {
+  return static_cast<size_t>(iterations) * workgroups * (256 / 64) * 4 * (2ull * 32 * 32 * 16);
+}
+
+QKRA_CALIB_API int32_t qkra_calibrate_stream_read(const void* buf, size_t bytes, void* sink, int32_t workgroups,
+                                                  void* hip_stream) {
+  if (buf == nullptr || sink == nullptr || workgroups <= 0 || bytes % 16 != 0 ||
+      (reinterpret_cast<uintptr_t>(buf) & 15u) != 0)
+    return 1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(workgroups)), dim3(kReadThreads), 0,
+                     static_cast<hipStream_t>(hip_stream), static_cast<const u32x4*>(buf), bytes / 16,
+                     static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+QKRA_CALIB_API int32_t qkra_calibrate_mfma_bf16(int64_t iterations, void* sink, int32_t workgroups, void* hip_stream) {
+  if (sink == nullptr || workgroups <= 0 || iterations <= 0) return 1;
+  hipLaunchKernelGGL(mfma_loop_kernel, dim3(static_cast<unsigned>(workgroups)), dim3(256), 0,
+                     static_cast<hipStream_t>(hip_stream), iterations, static_cast<float*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+}  // extern "C"

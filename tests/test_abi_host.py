@@ -34,6 +34,20 @@ def test_library_exports_every_declared_symbol():
     assert sorted(da.exported_symbols()) == declared_symbols()
 
 
+def test_calibration_library_exports_every_declared_symbol():
+    # The benchmark's roofline calibration kernels live in a library of their own (include/qkra_calibrate.h).
+    text = (HEADER.parent / "qkra_calibrate.h").read_text()
+    names = sorted(set(re.findall(r"QKRA_CALIB_API\s+[\w\s\*]*?\b(qkra_calibrate_\w+)\s*\(", text)))
+    assert names == da.calibration_symbols() and len(names) == 3
+    lib = da.calibration_lib()
+    for name in names:
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+    assert da.qkra_calibrate_mfma_flop(10, 512) == 10 * 512 * 4 * 4 * 32768
+    assert da.qkra_calibrate_stream_read(None, 16, BASE, 8, 0) == 1   # refused before any launch
+    assert da.qkra_calibrate_stream_read(BASE, 17, BASE, 8, 0) == 1
+    assert da.qkra_calibrate_mfma_bf16(0, BASE, 8, 0) == 1
+
+
 def test_status_strings_and_version():
     for code in range(8):
         assert da.qknorm_rope_attn_status_string(code)
