@@ -122,16 +122,23 @@ def spread(times):
     return t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2]), t[(n - 1) // 10], t[((n - 1) * 9) // 10]
 
 
+def weight_bound(q_norm_weight, k_norm_weight) -> float:
+    """max|w_q| * max|w_k|: fixed for a layer, so a caller computes it once (qkra_config.qk_weight_bound)."""
+    return float(q_norm_weight.float().abs().max()) * float(k_norm_weight.float().abs().max())
+
+
 class Runner:
     """Holds device inputs/outputs/workspaces of a workload and issues its calls (one step = every call)."""
 
-    def __init__(self, w, torch, da, fused: bool = False, paged_page_size: int = 0):
+    def __init__(self, w, torch, da, fused: bool = False, paged_page_size: int = 0, use_bound: bool = True):
         self.torch, self.da, self.w = torch, da, w
         self.calls = []
         if w.prefill is not None:
             p = w.prefill
             h = p.heads
-            cfg = da.make_config(h.num_q_heads, h.num_kv_heads, h.head_dim, p.qkv.dtype, h.rms_eps, h.rope_base)
+            bound = weight_bound(p.q_norm_weight, p.k_norm_weight) if use_bound else 0.0
+            cfg = da.make_config(h.num_q_heads, h.num_kv_heads, h.head_dim, p.qkv.dtype, h.rms_eps, h.rope_base,
+                                 qk_weight_bound=bound)
             out = torch.empty((p.num_tokens, h.num_q_heads * h.head_dim), dtype=p.qkv.dtype, device=p.qkv.device)
             ws_bytes = da.qknorm_rope_attn_workspace_bytes(cfg, da.QKRA_MODE_PREFILL, p.num_tokens, p.max_seqlen)
             ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=p.qkv.device)
@@ -442,6 +449,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="mixed_qwen3_8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the side workloads and the calibration")
+    ap.add_argument("--no-weight-bound", action="store_true",
+                    help="do not pass the norm weights' bound (every bf16 prefill then launches both softmax kernels)")
     ap.add_argument("--page-size", type=int, default=0,
                     help="run a decode-only workload's decode through the paged call with this page size")
     args = ap.parse_args(argv)
@@ -477,7 +486,9 @@ def main(argv=None):
 
     # ---- the headline: the mixed step through qknorm_rope_attn_mixed_step ----------------------------------
     w = build_workload(args.workload, device=dev, parity=False)
-    runner = Runner(w, torch, da, fused=True, paged_page_size=args.page_size if w.prefill is None else 0)
+    use_bound = not args.no_weight_bound
+    runner = Runner(w, torch, da, fused=True, paged_page_size=args.page_size if w.prefill is None else 0,
+                    use_bound=use_bound)
     F, B = runner.work()
     ideal_s = F / (PEAK_MFMA_TFLOPS * 1e12) + B / (PEAK_HBM_GBPS * 1e9)
     # Every kernel timed once over a few steps (which perturbs the step) to find the dominant one ...
@@ -507,7 +518,7 @@ def main(argv=None):
 
     def run_side(name, reps, warmup, timed_names, per_call=False, fused=False, paged=0, evict=False, keep=None):
         sw = build_workload(name, device=dev, parity=False)
-        r = Runner(sw, torch, da, fused=fused, paged_page_size=paged)
+        r = Runner(sw, torch, da, fused=fused, paged_page_size=paged, use_bound=use_bound)
         if keep:  # time only these calls of the workload (e.g. the decode half of the mixed step)
             r.calls = [c for c in r.calls if c[0].startswith(keep)]
             if keep == "decode":
@@ -613,6 +624,7 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded normal qkv, norm weights 1+0.1N, cache contents N(0,1))",
+        "qk_weight_bound_passed": use_bound,
         "config": {"workload": args.workload, "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128,
                    "prefill_seqlens": [4096] * 4 if args.workload == "mixed_qwen3_8b" else None,
                    "decode_requests": 128 if args.workload == "mixed_qwen3_8b" else None,

@@ -44,6 +44,7 @@ from .binding import (  # noqa: F401
     qknorm_rope_attn_workspace_bytes,
     qknorm_rope_attn_status_string,
     qknorm_rope_attn_last_hip_error,
+    qknorm_rope_attn_unshifted_weight_limit,
     qknorm_rope_attn_version,
     qknorm_rope_attn_set_kernel_timing,
     qknorm_rope_attn_read_kernel_timing,

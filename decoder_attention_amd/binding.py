@@ -39,7 +39,7 @@ class QkraConfig(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("rms_eps", ctypes.c_float),
-        ("reserved", ctypes.c_int32),
+        ("qk_weight_bound", ctypes.c_float),
         ("rope_base", ctypes.c_double),
     ]
 
@@ -90,6 +90,7 @@ _SIGNATURES = {
     "qknorm_rope_attn_workspace_bytes": (_SZ, [ctypes.POINTER(QkraConfig), _I32, _I32, _I32]),
     "qknorm_rope_attn_status_string": (ctypes.c_char_p, [_I32]),
     "qknorm_rope_attn_last_hip_error": (_I32, []),
+    "qknorm_rope_attn_unshifted_weight_limit": (ctypes.c_float, [_I32]),
     "qknorm_rope_attn_version": (_I32, []),
     "qknorm_rope_attn_set_kernel_timing": (_I32, [_I32]),
     "qknorm_rope_attn_read_kernel_timing": (_I32, [ctypes.POINTER(ctypes.c_double),
@@ -185,13 +186,13 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_config(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype=QKRA_BF16, rms_eps: float = 1e-6,
-                rope_base: float = 1e6) -> QkraConfig:
+                rope_base: float = 1e6, qk_weight_bound: float = 0.0) -> QkraConfig:
     if not isinstance(dtype, int):
         import torch
 
         dtype = {torch.bfloat16: QKRA_BF16, torch.float32: QKRA_FP32}[dtype]
-    return QkraConfig(int(num_q_heads), int(num_kv_heads), int(head_dim), int(dtype), float(rms_eps), 0,
-                      float(rope_base))
+    return QkraConfig(int(num_q_heads), int(num_kv_heads), int(head_dim), int(dtype), float(rms_eps),
+                      float(qk_weight_bound), float(rope_base))
 
 
 # ---- the C ABI, one Python function per exported symbol -------------------
@@ -285,6 +286,10 @@ def qknorm_rope_attn_status_string(status: int) -> str:
 
 def qknorm_rope_attn_last_hip_error() -> int:
     return int(lib().qknorm_rope_attn_last_hip_error())
+
+
+def qknorm_rope_attn_unshifted_weight_limit(head_dim: int) -> float:
+    return float(lib().qknorm_rope_attn_unshifted_weight_limit(int(head_dim)))
 
 
 def qknorm_rope_attn_version() -> int:

@@ -31,7 +31,7 @@ int32_t check_config(const qkra_config* cfg) {
   if (cfg == nullptr) return QKRA_ERR_INVALID_ARGUMENT;
   if (cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0) return QKRA_ERR_INVALID_ARGUMENT;
   if (cfg->num_q_heads % cfg->num_kv_heads != 0) return QKRA_ERR_INVALID_ARGUMENT;
-  if (cfg->reserved != 0) return QKRA_ERR_INVALID_ARGUMENT;
+  if (!(cfg->qk_weight_bound >= 0.0f) || !std::isfinite(cfg->qk_weight_bound)) return QKRA_ERR_INVALID_ARGUMENT;
   if (!(cfg->rms_eps >= 0.0f) || !std::isfinite(cfg->rms_eps)) return QKRA_ERR_INVALID_ARGUMENT;
   if (!(cfg->rope_base > 0.0) || !std::isfinite(cfg->rope_base)) return QKRA_ERR_INVALID_ARGUMENT;
   if (cfg->head_dim != 64 && cfg->head_dim != 128) return QKRA_ERR_UNSUPPORTED;
@@ -171,6 +171,15 @@ float softmax_scale_log2(int head_dim) {
   return static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(head_dim)));
 }
 
+// Which bf16 prefill attention kernels a call launches.
+enum class SoftmaxPath { kBoth, kUnshifted, kShifted };
+SoftmaxPath softmax_path(const qkra_config* cfg, const int32_t* cache_lens) {
+  if (cfg->dtype != QKRA_BF16 || cache_lens != nullptr || cfg->qk_weight_bound <= 0.0f) return SoftmaxPath::kBoth;
+  return cfg->qk_weight_bound <= prefill_unshifted_limit(cfg->head_dim, softmax_scale_log2(cfg->head_dim))
+             ? SoftmaxPath::kUnshifted
+             : SoftmaxPath::kShifted;
+}
+
 }  // namespace
 }  // namespace qkra
 
@@ -202,7 +211,12 @@ QKRA_API const char* qknorm_rope_attn_status_string(int32_t status) {
 
 QKRA_API int32_t qknorm_rope_attn_last_hip_error(void) { return g_last_hip_error; }
 
-QKRA_API int32_t qknorm_rope_attn_version(void) { return 300; }
+QKRA_API float qknorm_rope_attn_unshifted_weight_limit(int32_t head_dim) {
+  if (head_dim != 64 && head_dim != 128) return 0.0f;
+  return prefill_unshifted_limit(head_dim, softmax_scale_log2(head_dim));
+}
+
+QKRA_API int32_t qknorm_rope_attn_version(void) { return 400; }
 
 }  // extern "C"
 
@@ -305,14 +319,20 @@ int32_t prefill_impl(const qkra_config* cfg, const void* qkv, const void* q_norm
   pa.max_seqlen = max_seqlen;
   pa.scale_log2 = softmax_scale_log2(cfg->head_dim);
   if (paged) pa.paged = *paged;
+  // A plain bf16 prefill with the caller's weight bound launches only the softmax kernel it selects.
+  const SoftmaxPath path = softmax_path(cfg, cache_lens);
   if (defer && !paged && cfg->dtype == QKRA_BF16 && cache_lens == nullptr) {  // attention runs in the fused step
+    // The fused launch is the unshifted kernel; only a bound selecting it spares the running-max launch.
+    pa.single_path = path == SoftmaxPath::kUnshifted;
     defer->args = pa;
     defer->set = true;
     return QKRA_OK;
   }
   if (cfg->dtype == QKRA_BF16) {
-    err = timed(kKernelPrefillMfma, stream, [&] { return launch_prefill_attn_bf16(pa, true, stream); });
-    if (err == hipSuccess)
+    pa.single_path = path != SoftmaxPath::kBoth;
+    if (path != SoftmaxPath::kShifted)
+      err = timed(kKernelPrefillMfma, stream, [&] { return launch_prefill_attn_bf16(pa, true, stream); });
+    if (err == hipSuccess && path != SoftmaxPath::kUnshifted)
       err = timed(kKernelPrefillMfmaShifted, stream, [&] { return launch_prefill_attn_bf16(pa, false, stream); });
   } else
     err = timed(kKernelPrefillFp32, stream, [&] { return launch_prefill_attn_fp32(pa, stream); });
@@ -445,7 +465,10 @@ int32_t decode_impl(const qkra_config* cfg, const void* qkv, const void* q_norm_
     if (fused) {
       err = timed(kKernelFusedStep, stream, [&] { return launch_fused_step(*fused, da, stream); });
       if (err != hipSuccess) return hip_status(err);
-      err = timed(kKernelPrefillMfmaShifted, stream, [&] { return launch_prefill_attn_bf16(*fused, false, stream); });
+      // The running-max kernel takes the items the fused launch's unshifted prefill cannot; with the caller's
+      // weight bound selecting the unshifted softmax there are none.
+      if (!fused->single_path)
+        err = timed(kKernelPrefillMfmaShifted, stream, [&] { return launch_prefill_attn_bf16(*fused, false, stream); });
     } else {
       err = timed(kKernelDecodeSplit, stream, [&] { return launch_decode_mfma(da, stream); });
     }

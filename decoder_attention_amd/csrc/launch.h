@@ -109,7 +109,11 @@ struct PrefillAttnArgs {
   int num_q_heads, num_kv_heads, head_dim, cache_capacity, num_seqs, max_seqlen;
   float scale_log2;         // log2(e) / sqrt(D)
   PagedTable paged;         // table null: contiguous caches (k_cache/v_cache are the pools otherwise)
+  bool single_path = false; // bf16: only one of the two prefill attention kernels is launched
 };
+// The largest max|w_q| * max|w_k| for which the unshifted bf16 prefill
+// kernel takes a request (and every kernel computes this same value).
+float prefill_unshifted_limit(int head_dim, float scale_log2);
 // bf16: two kernels over the same grid, both launched by every call.
 // unshifted = true launches the one that takes p = 2^s without a shift (a
 // workgroup returns at once unless its request has no cached history and the

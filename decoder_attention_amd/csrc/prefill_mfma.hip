@@ -169,7 +169,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ past_lens, bf16* __restrict__ out,
     int num_q_heads, int num_kv_heads,
     int cache_capacity, int num_seqs, int tiles_per_seq, int chunks_per_kv, int num_items,
-    float rms_eps, float scale_log2, float bound_limit, DecodeRole dec, PagedTable paged) {
+    float rms_eps, float scale_log2, float bound_limit, DecodeRole dec, PagedTable paged, int single_path) {
   constexpr int TBN = 8 / HC;       // token blocks (of 32) per workgroup
   constexpr int TM = 32 * TBN;      // tokens per workgroup
   constexpr int DS = D / 16;        // k-steps over D for the scores
@@ -220,10 +220,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   // shifted one once the weights are reduced, before anything else is
   // loaded.  The unshifted kernel tests the weights once its first K/V tile
   // and Q loads are in flight (below).
+  // With `single_path` the host launched only this kernel (the caller's
+  // weight bound selected it): the running-max kernel then takes every item.
   if constexpr (kBounded) {
     if (past != 0) return;
   } else {
-    if (past == 0 && scores_bounded(weight_max_lane<D>(q_norm_weight, k_norm_weight), 0, bound_limit)) return;
+    if (!single_path && past == 0 &&
+        scores_bounded(weight_max_lane<D>(q_norm_weight, k_norm_weight), 0, bound_limit))
+      return;
   }
   const int cu0 = cu_seqlens[seq];
   const int seqlen = min(cu_seqlens[seq + 1] - cu0, cache_capacity - past);
@@ -589,6 +593,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   if constexpr (kBounded) {
     if (!scores_bounded(wmax, past, bound_limit)) {
       __builtin_amdgcn_s_waitcnt(0);  // leave with no load outstanding
+      if (single_path) {
+        // The weights break the caller's bound that launched this kernel
+        // alone: no kernel computes these rows, so they are written as NaN
+        // (bf16 0x7fc0), whole 16-byte pieces, D/8 lanes per row.
+        constexpr int LPR = D / 8, RPI = 64 / LPR;
+        const u32x4 nan8 = {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          for (int r = lane / LPR; r < 32; r += RPI) {
+            const int tok = qfirst[qb] + r;
+            if (tok < seqlen)
+              *reinterpret_cast<u32x4*>(out + (static_cast<size_t>(cu0 + tok) * num_q_heads + qhead[qb]) * D +
+                                        8 * (lane % LPR)) = nan8;
+          }
+      }
       return;
     }
   }
@@ -670,14 +689,15 @@ hipError_t launch_typed(const PrefillAttnArgs& a, hipStream_t stream) {
   if (items <= 0) return hipSuccess;
   const long long grid = (items + 7) / 8 * 8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const float bound_limit = BOUND_LOG2 / (1.02f * static_cast<float>(D) * a.scale_log2);
+  const float bound_limit = prefill_unshifted_limit(D, a.scale_log2);
   launch_kernel((prefill_mfma_kernel<D, HC, kBounded, 0, kPaged>), dim3(static_cast<unsigned>(grid)), dim3(NTHREADS), 0, stream,
                      static_cast<const bf16*>(a.qkv), static_cast<const bf16*>(a.q_norm_weight),
                      static_cast<const bf16*>(a.k_norm_weight), a.rope_table,
                      static_cast<const bf16*>(a.k_cache),
                      static_cast<const bf16*>(a.v_cache), a.cu_seqlens, a.past_lens, static_cast<bf16*>(a.out),
                      a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.num_seqs, tiles, chunks_per_kv,
-                     static_cast<int>(items), a.rms_eps, a.scale_log2, bound_limit, DecodeRole{}, a.paged);
+                     static_cast<int>(items), a.rms_eps, a.scale_log2, bound_limit, DecodeRole{}, a.paged,
+                     a.single_path ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -708,7 +728,7 @@ hipError_t launch_fused_typed(const PrefillAttnArgs& a, const DecodeAttnArgs& d,
   const long long items = static_cast<long long>(a.num_kv_heads) * chunks_per_kv * a.num_seqs * tiles;
   const long long grid = kFusedDecodeWgs + (items + 7) / 8 * 8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const float bound_limit = BOUND_LOG2 / (1.02f * static_cast<float>(D) * a.scale_log2);
+  const float bound_limit = prefill_unshifted_limit(D, a.scale_log2);
   const DecodeRole dec{static_cast<const bf16*>(d.q), static_cast<const bf16*>(d.k_cache),
                        static_cast<const bf16*>(d.v_cache), d.cache_lens, d.plan, d.partials, d.cache_capacity,
                        1, d.num_units, kFusedDecodeWgs};
@@ -717,7 +737,8 @@ hipError_t launch_fused_typed(const PrefillAttnArgs& a, const DecodeAttnArgs& d,
                      static_cast<const bf16*>(a.k_norm_weight), a.rope_table, static_cast<const bf16*>(a.k_cache),
                      static_cast<const bf16*>(a.v_cache), a.cu_seqlens, a.past_lens, static_cast<bf16*>(a.out),
                      a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.num_seqs, tiles, chunks_per_kv,
-                     static_cast<int>(items), a.rms_eps, a.scale_log2, bound_limit, dec, PagedTable{});
+                     static_cast<int>(items), a.rms_eps, a.scale_log2, bound_limit, dec, PagedTable{},
+                     a.single_path ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -734,6 +755,10 @@ hipError_t launch_fused_dim(const PrefillAttnArgs& a, const DecodeAttnArgs& d, h
 }
 
 }  // namespace
+
+float prefill_unshifted_limit(int head_dim, float scale_log2) {
+  return BOUND_LOG2 / (1.02f * static_cast<float>(head_dim) * scale_log2);
+}
 
 bool fused_step_supported(int head_dim, int group) {
   return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);

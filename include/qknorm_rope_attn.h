@@ -84,9 +84,24 @@ typedef struct qkra_config {
   int32_t head_dim;      /* D: 64 or 128; independent of the hidden size */
   int32_t dtype;         /* QKRA_BF16 or QKRA_FP32 */
   float rms_eps;         /* >= 0, added to mean(x^2) inside the square root */
-  int32_t reserved;      /* must be 0 */
+  /* 0, or the caller's upper bound on max|q_norm_weight| * max|k_norm_weight|
+   * (static for a layer).  A bf16 prefill bounds every score by this product
+   * (times sqrt(D) log2(e)) and then takes the softmax with no shift when it is
+   * small enough (qknorm_rope_attn_unshifted_weight_limit(D)); the choice is
+   * made on the device from the weights, so by default both softmax kernels
+   * are launched and one of them returns at once.  With a bound here the host
+   * launches only the one it selects.  The device check stays: if the weights
+   * break a bound that selected the unshifted softmax, the rows it cannot
+   * compute are written as NaN, never as wrong numbers.  Must be finite and
+   * >= 0.  Appends (calls with cache_lens) and fp32 ignore it. */
+  float qk_weight_bound;
   double rope_base;      /* > 0, e.g. 1e4 or 1e6 */
 } qkra_config;
+
+/* Largest max|q_norm_weight| * max|k_norm_weight| for which a bf16 prefill of
+ * head dimension D takes the softmax without a shift (0 for an unsupported D).
+ * Pure host computation. */
+QKRA_API float qknorm_rope_attn_unshifted_weight_limit(int32_t head_dim);
 
 /*
  * Prefill of `num_seqs` requests packed into `num_tokens` rows.

@@ -52,7 +52,7 @@ def test_status_strings_and_version():
     for code in range(8):
         assert da.qknorm_rope_attn_status_string(code)
     assert da.qknorm_rope_attn_status_string(99) == "unknown status"
-    assert da.qknorm_rope_attn_version() == 300  # 0.3.0: qknorm_rope_attn_decode_noalloc
+    assert da.qknorm_rope_attn_version() == 400  # 0.4.0: paged caches, the caller's weight bound
     assert da.qknorm_rope_attn_last_hip_error() == 0
     assert da.qknorm_rope_attn_kernel_name(1) == "prefill_attn_mfma_bf16"
     assert da.qknorm_rope_attn_kernel_name(10) == "prefill_attn_mfma_bf16_shifted"
@@ -515,3 +515,14 @@ def test_paged_calls_need_a_descriptor_and_accept_empty_batches():
         da.QKRA_ERR_INVALID_ARGUMENT
     assert f(*args, None, 0, 0, 0, 0, None, None, None, 0, 0) == 0
     assert da.qknorm_rope_attn_last_hip_error() == 0
+
+
+def test_weight_bound_field_and_unshifted_limit():
+    # The limit: 48 / (1.02 * D * log2(e) / sqrt(D)) -- 2.88 for D = 128, 4.08 for D = 64.
+    assert da.qknorm_rope_attn_unshifted_weight_limit(128) == pytest.approx(48 / (1.02 * 128 * 1.4426950408889634
+                                                                                  / 128 ** 0.5), rel=1e-6)
+    assert da.qknorm_rope_attn_unshifted_weight_limit(64) == pytest.approx(4.0797, rel=1e-3)
+    assert da.qknorm_rope_attn_unshifted_weight_limit(96) == 0.0
+    for bad in (-1.0, float("nan"), float("inf")):
+        cfg, a = prefill_args(cfg=da.make_config(32, 8, 128, da.QKRA_BF16, qk_weight_bound=bad))
+        assert call_prefill(cfg, a) == da.QKRA_ERR_INVALID_ARGUMENT

@@ -102,3 +102,93 @@ def test_scores_beyond_fp32_range_need_the_shift(head_dim):
     _set_weights(p, np.full(d, 4.0), np.full(d, 4.0))
     note(f"prefill D={head_dim} with q = k and weights 4 (self scores ~2^261)")
     _run_and_check(p, "q = k, weights 4")
+
+
+# ---- the caller's weight bound (qkra_config.qk_weight_bound) -------------------------------------------------
+# With a bound the host launches only the softmax kernel the bound selects.  Launches are counted with the
+# library's kernel timing (ids 1: unshifted, 10: running max).
+
+def _launches(fn):
+    da.qknorm_rope_attn_set_kernel_timing((1 << 1) | (1 << 10))
+    da.qknorm_rope_attn_read_kernel_timing()
+    fn()
+    torch.cuda.synchronize()
+    k = da.qknorm_rope_attn_read_kernel_timing()
+    da.qknorm_rope_attn_set_kernel_timing(False)
+    return {name: n for name, (_, n) in k.items()}
+
+
+def _prefill_out(p, bound):
+    h = p.heads
+    cfg = da.make_config(h.num_q_heads, h.num_kv_heads, h.head_dim, p.qkv.dtype, h.rms_eps, h.rope_base,
+                         qk_weight_bound=bound)
+    out = torch.full((p.num_tokens, h.num_q_heads * h.head_dim), float("nan"), dtype=p.qkv.dtype, device=DEV)
+    launches = _launches(lambda: da.prefill(cfg, p.qkv, p.q_norm_weight, p.k_norm_weight, p.positions,
+                                            p.cu_seqlens, p.max_seqlen, p.k_cache, p.v_cache, out=out))
+    return out, launches
+
+
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_weight_bound_launches_one_kernel(head_dim):
+    h = HeadConfig(16, 4, head_dim, 1e-6, 1e6)
+    lens = [300, 1, 0, 129]
+    p = make_prefill_inputs(h, lens, seed=64, device=DEV, capacity=max(lens))
+    wq, wk = f64(p.q_norm_weight), f64(p.k_norm_weight)
+    prod = float(np.abs(wq).max() * np.abs(wk).max())
+    limit = da.qknorm_rope_attn_unshifted_weight_limit(head_dim)
+    assert prod < limit
+    base, both = _prefill_out(p, 0.0)                       # no bound: both kernels launched
+    assert both == {"prefill_attn_mfma_bf16": 1, "prefill_attn_mfma_bf16_shifted": 1}
+    small, one = _prefill_out(p, prod * 1.01)               # a true bound under the limit: the unshifted kernel
+    assert one == {"prefill_attn_mfma_bf16": 1}
+    assert torch.equal(small.view(torch.int16), base.view(torch.int16))
+    large, one = _prefill_out(p, limit * 2)                 # a bound past the limit: the running-max kernel only
+    assert one == {"prefill_attn_mfma_bf16_shifted": 1}
+    ref = oracle_prefill(p)
+    assert_close(f64(large), ref["out"], BF16_TOL, "running-max kernel for every item")
+    note(f"D={head_dim}: weight bound {prod:.3f} (limit {limit:.3f}): one launch, same bits")
+
+
+def test_weight_bound_broken_by_the_weights_gives_nan_rows():
+    """A bound that selects the unshifted softmax while the weights exceed the limit: no kernel can compute the
+    rows, and they are written as NaN rather than left as whatever the buffer held."""
+    h = HeadConfig(32, 8, 128, 1e-6, 1e6)
+    lens = [70, 5]
+    p = make_prefill_inputs(h, lens, seed=65, device=DEV, capacity=max(lens))
+    wq, wk = f64(p.q_norm_weight), f64(p.k_norm_weight)
+    wq[5], wk[77] = 2.5, -2.5
+    _set_weights(p, wq, wk)
+    h2 = p.heads
+    cfg = da.make_config(h2.num_q_heads, h2.num_kv_heads, h2.head_dim, p.qkv.dtype, h2.rms_eps, h2.rope_base,
+                         qk_weight_bound=1.0)
+    out = torch.zeros((p.num_tokens, 32 * 128), dtype=p.qkv.dtype, device=DEV)
+    launches = _launches(lambda: da.prefill(cfg, p.qkv, p.q_norm_weight, p.k_norm_weight, p.positions,
+                                            p.cu_seqlens, p.max_seqlen, p.k_cache, p.v_cache, out=out))
+    assert launches == {"prefill_attn_mfma_bf16": 1}
+    assert torch.isnan(out.float()).all(), "rows the broken bound left uncomputed must be NaN"
+
+
+def test_weight_bound_in_the_mixed_step():
+    """The mixed step with a true bound: no running-max launch after the fused one, and the same bits."""
+    from workloads import make_decode_inputs
+
+    h = HeadConfig(32, 8, 128, 1e-6, 1e6)
+    p = make_prefill_inputs(h, [300, 1, 129], seed=66, device=DEV, capacity=300)
+    d = make_decode_inputs(h, [5, 700, 3000], seed=67, device=DEV)
+    d.q_norm_weight.copy_(p.q_norm_weight)
+    d.k_norm_weight.copy_(p.k_norm_weight)
+    prod = float(np.abs(f64(p.q_norm_weight)).max() * np.abs(f64(p.k_norm_weight)).max())
+    outs = []
+    for bound, want in ((0.0, {"prefill_attn_mfma_bf16_shifted": 1}), (prod, {})):
+        cfg = da.make_config(32, 8, 128, torch.bfloat16, 1e-6, 1e6, qk_weight_bound=bound)
+        pk, pv, dk, dv = p.k_cache.clone(), p.v_cache.clone(), d.k_cache.clone(), d.v_cache.clone()
+        res = {}
+
+        def run():
+            res["out"] = da.mixed_step(cfg, p.q_norm_weight, p.k_norm_weight, p.qkv, p.positions, p.cu_seqlens,
+                                       p.max_seqlen, pk, pv, d.qkv, d.positions, d.cache_lens, d.max_cache_len, dk,
+                                       dv)
+        assert _launches(run) == want
+        outs.append(res["out"][:2])
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
