@@ -75,3 +75,11 @@ def test_layer_step_workloads_present():
     from workloads import WORKLOADS
 
     assert {"residual_rmsnorm_qwen3_8b", "next_token_qwen3_8b"} <= set(WORKLOADS)
+
+
+def test_prefill_half_workload_shape():
+    w = build_workload("prefill_4x4096_qwen3_8b", parity=False)
+    p = w.prefill
+    assert w.decode is None and p.seqlens == [4096] * 4 and p.max_seqlen == 4096
+    assert p.qkv.shape == (4 * 4096, (32 + 2 * 8) * 128)
+    assert p.positions[:4096].tolist() == list(range(4096))

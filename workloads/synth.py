@@ -422,6 +422,19 @@ def _mixed_qwen3_8b(dtype, device, parity):
                           "lengths U[1,16384], Hq=32 Hkv=8 D=128", pre, dec)
 
 
+def _prefill_4x4096_qwen3_8b(dtype, device, parity):
+    # The mixed step's prefill half alone: the same draws as mixed_qwen3_8b, without its decode caches.
+    h = HeadConfig(32, 8, 128, 1e-6, 1e6)
+    g = torch.Generator().manual_seed(1005)
+    torch.randint(1, 16384 + 1, (128,), generator=g)  # the decode lengths, drawn first there
+    rows = _draw_rows(g, 4 * 4096 + 128, h, dtype)
+    wq = _draw_norm_weight(g, h, dtype)
+    wk = _draw_norm_weight(g, h, dtype)
+    pre = _prefill_from_rows(h, rows[:4 * 4096], wq, wk, [4096] * 4, 4096, dtype, device, parity)
+    return WorkloadInputs("prefill_4x4096_qwen3_8b",
+                          "the mixed step's prefill half alone: 4x4096 tokens, Hq=32 Hkv=8 D=128", pre, None)
+
+
 def _chunked_qwen3_8b(dtype, device, parity):
     h = HeadConfig(32, 8, 128, 1e-6, 1e6)
     g = torch.Generator().manual_seed(1006)
@@ -476,6 +489,7 @@ WORKLOADS: Dict[str, object] = {
     "long_prefill_32k": _long_prefill_32k,
     "mixed_qwen3_8b": _mixed_qwen3_8b,
     "chunked_qwen3_8b": _chunked_qwen3_8b,
+    "prefill_4x4096_qwen3_8b": _prefill_4x4096_qwen3_8b,
     "residual_rmsnorm_qwen3_8b": _residual_rmsnorm_qwen3_8b,
     "next_token_qwen3_8b": _next_token_qwen3_8b,
 }
