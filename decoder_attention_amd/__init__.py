@@ -32,6 +32,11 @@ from .binding import (  # noqa: F401
     qkra_calibrate_stream_read,
     qkra_calibrate_mfma_bf16,
     qkra_calibrate_mfma_flop,
+    phase_stamps_symbols,
+    qkra_phase_stamps_bytes,
+    qkra_phase_stamps_clear,
+    qkra_phase_stamps_read,
+    select_library,
     lib,
     make_config,
     qknorm_rope_attn_prefill,

@@ -103,15 +103,27 @@ _SIGNATURES = {
 }
 
 
+_lib_path = LIB_PATH
+
+
+def select_library(path: str) -> None:
+    """Load `path`, another build of the same sources (the phase-stamps profiling build), in place of the
+    normal library.  Must come before the first call into the library."""
+    global _lib_path
+    if _lib is not None and os.path.abspath(path) != os.path.abspath(_lib_path):
+        raise RuntimeError(f"{_lib_path} is already loaded")
+    _lib_path = path
+
+
 def lib() -> ctypes.CDLL:
     """Load the HIP library (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
+        if not os.path.exists(_lib_path):
             raise RuntimeError(
-                f"HIP library {LIB_PATH} is missing; build it first "
+                f"HIP library {_lib_path} is missing; build it first "
                 "(python -c 'import __graft_entry__ as g; g.build()' or python decoder_attention_amd/build.py)")
-        handle = ctypes.CDLL(LIB_PATH)
+        handle = ctypes.CDLL(_lib_path)
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(handle, name)
             fn.restype = res
@@ -165,6 +177,43 @@ def qkra_calibrate_mfma_bf16(iterations: int, sink, workgroups: int, stream=None
 
 def qkra_calibrate_mfma_flop(iterations: int, workgroups: int) -> int:
     return int(calibration_lib().qkra_calibrate_mfma_flop(int(iterations), int(workgroups)))
+
+
+# ---- the profiling build's phase stamps (include/qkra_phase_stamps.h) ----------
+_STAMPS_SIGNATURES = {
+    "qkra_phase_stamps_read": (_I32, [_P, _SZ]),
+    "qkra_phase_stamps_clear": (_I32, [_P]),
+    "qkra_phase_stamps_bytes": (_SZ, []),
+}
+
+
+def phase_stamps_symbols():
+    return sorted(_STAMPS_SIGNATURES)
+
+
+def _stamps():
+    handle = lib()
+    if not hasattr(handle, "qkra_phase_stamps_read"):
+        raise RuntimeError(f"{_lib_path} is not the phase-stamps build; select_library() it first")
+    for name, (res, args) in _STAMPS_SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
+def qkra_phase_stamps_bytes() -> int:
+    return int(_stamps().qkra_phase_stamps_bytes())
+
+
+def qkra_phase_stamps_clear(stream=None) -> int:
+    return _stamps().qkra_phase_stamps_clear(_stream(stream))
+
+
+def qkra_phase_stamps_read(dst, nbytes: int) -> int:
+    """`dst`: a host address (int) or a CPU tensor / NumPy array with the buffer protocol's data pointer."""
+    ptr = dst if isinstance(dst, int) else (dst.ctypes.data if hasattr(dst, "ctypes") else dst.data_ptr())
+    return _stamps().qkra_phase_stamps_read(ptr, int(nbytes))
 
 
 def _ptr(x) -> Optional[int]:

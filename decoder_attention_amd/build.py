@@ -25,6 +25,10 @@ SOURCES = ["qknorm_rope.hip", "prefill_mfma.hip", "prefill_fp32.hip", "decode.hi
 # The benchmark's roofline calibration kernels: a library of their own, outside the attention ABI.
 CALIB_SOURCES = ["calibrate.hip"]
 CALIB_LIB_PATH = os.path.join(PKG_DIR, "libqkra_calibrate.so")
+# The profiling build: the same sources with per-workgroup phase stamps in the
+# bf16 prefill attention kernels (include/qkra_phase_stamps.h).
+STAMPS_LIB_PATH = os.path.join(PKG_DIR, "libqknorm_rope_attn_stamps.so")
+STAMPS_BUILD_DIR = os.path.join(PKG_DIR, "_build_stamps")
 ARCH = "gfx950"
 CFLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-fvisibility=hidden",
@@ -80,6 +84,13 @@ def build_calibration(verbose: bool = False) -> str:
     return build_library(verbose, out_path=CALIB_LIB_PATH, sources=CALIB_SOURCES)
 
 
+def build_phase_stamps(verbose: bool = False) -> str:
+    """The profiling build with phase stamps (libqknorm_rope_attn_stamps.so); returns its path."""
+    return build_library(verbose, extra_flags=["-DQKRA_PHASE_STAMPS"], out_path=STAMPS_LIB_PATH,
+                         build_dir=STAMPS_BUILD_DIR)
+
+
 if __name__ == "__main__":
     print(build_library(verbose="-v" in sys.argv))
     print(build_calibration(verbose="-v" in sys.argv))
+    print(build_phase_stamps(verbose="-v" in sys.argv))

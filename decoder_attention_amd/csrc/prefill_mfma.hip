@@ -63,6 +63,7 @@
 #include "decode_body.h"
 #include "device_common.h"
 #include "launch.h"
+#include "../../include/qkra_phase_stamps.h"
 
 namespace qkra {
 namespace {
@@ -96,6 +97,43 @@ __device__ __forceinline__ float half_wave_max(float x) {
 }
 
 constexpr int NSLOT = 3;  // LDS tile slots
+
+// ---- phase stamps (the profiling build, -DQKRA_PHASE_STAMPS, only) ----------
+// Every prefill workgroup's wavefronts record the 100 MHz constant clock
+// (s_memrealtime) at fixed points of their life and where they ran, so the
+// time of a work item splits into its prologue (item decode, first loads,
+// Q normalise and rotate), its tile loop and its epilogue.  The record's
+// address stays in vector registers, so the stamps take no scalar register
+// across the tile loop.  In the normal build every stamp compiles to nothing.
+#ifdef QKRA_PHASE_STAMPS
+static_assert(QKRA_STAMP_SLOTS == 8 && QKRA_STAMP_WAVES == NWAVES, "the stamp record layout");
+__device__ unsigned long long g_phase_stamps[static_cast<size_t>(QKRA_STAMP_WGS) * QKRA_STAMP_WAVES * QKRA_STAMP_SLOTS];
+#endif
+struct PhaseStamps {
+#ifdef QKRA_PHASE_STAMPS
+  unsigned long long addr;
+  __device__ __forceinline__ PhaseStamps() {
+    addr = reinterpret_cast<unsigned long long>(
+        g_phase_stamps +
+        (static_cast<size_t>(blockIdx.x % QKRA_STAMP_WGS) * QKRA_STAMP_WAVES + (threadIdx.x >> 6)) * QKRA_STAMP_SLOTS);
+    asm volatile("" : "+v"(addr));
+  }
+  __device__ __forceinline__ void mark(int slot, unsigned long long v) const {
+    if ((threadIdx.x & 63) == 0 && blockIdx.x < QKRA_STAMP_WGS) reinterpret_cast<unsigned long long*>(addr)[slot] = v;
+  }
+  __device__ __forceinline__ void now(int slot) const { mark(slot, __builtin_amdgcn_s_memrealtime()); }
+  // HW_ID (wave, SIMD, CU, shader array, engine), XCC_ID, the item's tiles and its logical index.
+  __device__ __forceinline__ void where(int ntiles, int logical) const {
+    mark(QKRA_STAMP_WHERE, (__builtin_amdgcn_s_getreg((15 << 11) | 4) & 0xffffull) |
+                               ((__builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xfull) << 16) |
+                               ((static_cast<unsigned long long>(ntiles) & 0xffffull) << 20) |
+                               (static_cast<unsigned long long>(logical) << 36));
+  }
+#else
+  __device__ __forceinline__ void now(int) const {}
+  __device__ __forceinline__ void where(int, int) const {}
+#endif
+};
 
 // The decode role of the fused step kernel: the first `wgs` workgroups each
 // run kFusedDecodeWavesPerWg wavefronts of the decode split (decode_body.h)
@@ -185,6 +223,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   __shared__ __attribute__((aligned(16))) bf16 sV[NSLOT][D * VST];
 
   // ---- work item (XCD-aware remap; per request, heaviest tiles first) -------
+  const PhaseStamps stamps;
+  stamps.now(QKRA_STAMP_ENTRY);
   int bid = blockIdx.x;
   int nb = gridDim.x;  // a multiple of 8
   if constexpr (kDecGW > 0) {
@@ -611,9 +651,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
       return;
     }
   }
+  stamps.now(QKRA_STAMP_ISSUED);
   store_tile(C0{});
   if (ntiles > 1) load_tile(1);
   q_finish();
+  stamps.now(QKRA_STAMP_Q_READY);
   __syncthreads();
   if (ntiles > 1) store_tile(C1{});
   __syncthreads();
@@ -628,8 +670,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   // Unrolled by 2*NSLOT: the score buffers alternate every step and the LDS
   // slots cycle every NSLOT steps.
   static_assert(NSLOT == 3, "the unroll below assumes a ring of three slots");
+  stamps.now(QKRA_STAMP_LOOP);
   for (int kt = 0; kt < ntiles; kt += 6) {
     step(std::integral_constant<int, 0>{}, kt, sA, sB);
+    if (kt == 0) stamps.now(QKRA_STAMP_FIRST_STEP);
     if (kt + 1 >= ntiles) break;
     step(std::integral_constant<int, 1>{}, kt + 1, sB, sA);
     if (kt + 2 >= ntiles) break;
@@ -641,6 +685,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     if (kt + 5 >= ntiles) break;
     step(std::integral_constant<int, 5>{}, kt + 5, sB, sA);
   }
+  stamps.now(QKRA_STAMP_LOOP_END);
 
   // ---- normalise and store.  A lane holds query l32 and d = 32db + 8(j/4) +
   // 4hi + j%4, so storing from registers would write 16 bytes into each of 32
@@ -677,6 +722,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
         *reinterpret_cast<u32x4*>(out + (static_cast<size_t>(cu0 + tok) * num_q_heads + qhead[qb]) * D + 8 * c) = v;
     }
   }
+  stamps.now(QKRA_STAMP_END);
+  stamps.where(ntiles, logical);
 }
 
 template <int D, int HC, bool kBounded, bool kPaged>
@@ -777,3 +824,24 @@ hipError_t launch_prefill_attn_bf16(const PrefillAttnArgs& a, bool unshifted, hi
 }
 
 }  // namespace qkra
+
+#ifdef QKRA_PHASE_STAMPS
+extern "C" {
+
+QKRA_STAMPS_API size_t qkra_phase_stamps_bytes(void) { return sizeof(qkra::g_phase_stamps); }
+
+QKRA_STAMPS_API int32_t qkra_phase_stamps_read(void* dst, size_t bytes) {
+  if (dst == nullptr) return 1;
+  const size_t n = bytes < sizeof(qkra::g_phase_stamps) ? bytes : sizeof(qkra::g_phase_stamps);
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(qkra::g_phase_stamps), n, 0, hipMemcpyDeviceToHost) == hipSuccess ? 0 : 6;
+}
+
+QKRA_STAMPS_API int32_t qkra_phase_stamps_clear(void* hip_stream) {
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(qkra::g_phase_stamps)) != hipSuccess) return 6;
+  return hipMemsetAsync(ptr, 0, sizeof(qkra::g_phase_stamps), static_cast<hipStream_t>(hip_stream)) == hipSuccess
+             ? 0 : 6;
+}
+
+}  // extern "C"
+#endif
