@@ -122,16 +122,21 @@ struct PhaseStamps {
     if ((threadIdx.x & 63) == 0 && blockIdx.x < QKRA_STAMP_WGS) reinterpret_cast<unsigned long long*>(addr)[slot] = v;
   }
   __device__ __forceinline__ void now(int slot) const { mark(slot, __builtin_amdgcn_s_memrealtime()); }
+  __device__ __forceinline__ unsigned long long hw_where() const {
+    return (__builtin_amdgcn_s_getreg((15 << 11) | 4) & 0xffffull) |
+           ((__builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xfull) << 16);
+  }
   // HW_ID (wave, SIMD, CU, shader array, engine), XCC_ID, the item's tiles and its logical index.
   __device__ __forceinline__ void where(int ntiles, int logical) const {
-    mark(QKRA_STAMP_WHERE, (__builtin_amdgcn_s_getreg((15 << 11) | 4) & 0xffffull) |
-                               ((__builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xfull) << 16) |
-                               ((static_cast<unsigned long long>(ntiles) & 0xffffull) << 20) |
+    mark(QKRA_STAMP_WHERE, hw_where() | ((static_cast<unsigned long long>(ntiles) & 0xffffull) << 20) |
                                (static_cast<unsigned long long>(logical) << 36));
   }
+  // A workgroup of the fused step's decode role: bit 63 set, no item.
+  __device__ __forceinline__ void where_decode_role() const { mark(QKRA_STAMP_WHERE, hw_where() | (1ull << 63)); }
 #else
   __device__ __forceinline__ void now(int) const {}
   __device__ __forceinline__ void where(int, int) const {}
+  __device__ __forceinline__ void where_decode_role() const {}
 #endif
 };
 
@@ -240,6 +245,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
                                       dec.v_cache, dec.cache_lens, dec.plan, dec.partials, num_q_heads, num_kv_heads,
                                       dec.cache_capacity, dec.chunks_per_kv, dec.num_units, scale_log2);
       }
+      stamps.now(QKRA_STAMP_END);
+      stamps.where_decode_role();
       return;
     }
     bid -= dec.wgs;  // a multiple of 8: the XCD mapping below is unchanged

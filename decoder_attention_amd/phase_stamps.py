@@ -1,11 +1,13 @@
 """Per-workgroup phase times of the bf16 prefill attention kernel.
 
-Runs one prefill (or chunk-append) workload through the profiling build of the
+Runs one prefill (or chunk-append) workload, or the mixed step of a workload
+with both halves (its prefill and decode in the fused kernel), through the profiling build of the
 library (libqknorm_rope_attn_stamps.so, include/qkra_phase_stamps.h), whose
 prefill kernels stamp the 100 MHz constant clock at fixed points of every
 workgroup's life, and prints where the time goes: per work item (prologue,
 first step, later steps, epilogue) and per CU (prologue, tile loop, epilogue,
-gaps between one workgroup's end and the next one's start, idle tail).
+gaps between one workgroup's end and the next one's start, idle tail); for the
+mixed step also when the decode-role and prefill-role workgroups ran.
 
     python -m decoder_attention_amd.phase_stamps --workload prefill_4x4096_qwen3_8b
 
@@ -71,13 +73,31 @@ def _prefill_call(da, torch, w, use_bound: bool):
     return call, h, a.seqlens, a.past_lens
 
 
+def _mixed_call(da, torch, w):
+    """A closure that issues the workload's mixed step (prefill and decode in one fused launch) once."""
+    p, d = w.prefill, w.decode
+    h = p.heads
+    bound = float(p.q_norm_weight.float().abs().max()) * float(p.k_norm_weight.float().abs().max())
+    cfg = da.make_config(h.num_q_heads, h.num_kv_heads, h.head_dim, p.qkv.dtype, h.rms_eps, h.rope_base,
+                         qk_weight_bound=bound)
+    po, do, pws, dws = da.mixed_step(cfg, p.q_norm_weight, p.k_norm_weight, p.qkv, p.positions, p.cu_seqlens,
+                                     p.max_seqlen, p.k_cache, p.v_cache, d.qkv, d.positions, d.cache_lens,
+                                     d.max_cache_len, d.k_cache, d.v_cache)
+
+    def call():
+        da.mixed_step(cfg, p.q_norm_weight, p.k_norm_weight, p.qkv, p.positions, p.cu_seqlens, p.max_seqlen,
+                      p.k_cache, p.v_cache, d.qkv, d.positions, d.cache_lens, d.max_cache_len, d.k_cache, d.v_cache,
+                      prefill_out=po, prefill_workspace=pws, decode_out=do, decode_workspace=dws)
+    return call
+
+
 def summarize(rec: np.ndarray) -> dict:
     """rec: uint64 [workgroups, waves, slots] as the profiling build writes it."""
     from types import SimpleNamespace
 
     S = SimpleNamespace(ENTRY=0, ISSUED=1, Q_READY=2, LOOP=3, FIRST_STEP=4, LOOP_END=5, END=6, WHERE=7)
     r = rec.astype(np.int64)
-    ran = (r[:, :, S.END] > 0).all(axis=1)
+    ran = (r[:, :, S.END] > 0).all(axis=1) & (r[:, 0, S.WHERE] >= 0)  # bit 63: the fused step's decode role
     r = r[ran]
     if r.shape[0] == 0:
         raise SystemExit("no workgroup of the prefill kernel ran a work item")
@@ -134,6 +154,58 @@ def summarize(rec: np.ndarray) -> dict:
             "later_step_us_by_tiles": by_tiles}
 
 
+def summarize_roles(rec: np.ndarray, bins: int = 10) -> dict:
+    """The fused mixed step: when the decode-role and prefill-role workgroups ran, and on how many CUs."""
+    r = rec.astype(np.int64)
+    r = r[(r[:, :, 6] > 0).all(axis=1)]
+    dec = r[:, 0, 7] < 0
+    start, end = r[:, :, 0].min(1) * TICK_US, r[:, :, 6].max(1) * TICK_US
+    base = start.min()
+    start, end = start - base, end - base
+    span = end.max()
+    cu = (((r[:, 0, 7] >> 16) & 0xF) << 8) | ((r[:, 0, 7] >> 8) & 0xFF)
+    out = {"span_us": float(span)}
+    for role, m in (("decode", dec), ("prefill", ~dec)):
+        if not m.any():
+            continue
+        out[role] = {"workgroups": int(m.sum()), "cus": int(len(set(cu[m].tolist()))),
+                     "first_start_us": float(start[m].min()), "last_end_us": float(end[m].max()),
+                     "end_p10_us": float(np.percentile(end[m], 10)), "end_p50_us": float(np.percentile(end[m], 50)),
+                     "end_p90_us": float(np.percentile(end[m], 90)),
+                     "busy_cu_us": float((end[m] - start[m]).sum())}
+    # CUs busy with each role, averaged over equal slices of the span
+    edges = np.linspace(0.0, span, bins + 1)
+    occ = {"decode": [], "prefill": []}
+    for a, b in zip(edges, edges[1:]):
+        for role, m in (("decode", dec), ("prefill", ~dec)):
+            ov = np.clip(np.minimum(end[m], b) - np.maximum(start[m], a), 0.0, None)
+            occ[role].append(float(ov.sum() / (b - a)))
+    out["cus_busy_by_slice"] = occ
+    out["slice_us"] = float(span / bins)
+    return out
+
+
+def markdown_roles(name: str, res: dict, cmd: str) -> str:
+    lines = [f"# Phase stamps: the fused mixed-step kernel, {name}", "", f"Command: `{cmd}`.", "",
+             f"Kernel span {res['span_us']:.1f} us (first workgroup start to last workgroup end, s_memrealtime at "
+             "100 MHz).  The decode role is the first workgroups of the grid; each runs its wavefronts' share of "
+             "the decode split, then every other workgroup runs one prefill work item.", "",
+             "| role | workgroups | CUs | first start (us) | end p10 | end p50 | end p90 | last end | CU-us |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for role in ("decode", "prefill"):
+        if role in res:
+            v = res[role]
+            lines.append(f"| {role} | {v['workgroups']} | {v['cus']} | {v['first_start_us']:.1f} | "
+                         f"{v['end_p10_us']:.1f} | {v['end_p50_us']:.1f} | {v['end_p90_us']:.1f} | "
+                         f"{v['last_end_us']:.1f} | {v['busy_cu_us']:.0f} |")
+    lines += ["", f"CUs busy with each role, mean over slices of {res['slice_us']:.1f} us:", "",
+              "| slice | " + " | ".join(str(i) for i in range(len(res["cus_busy_by_slice"]["decode"]))) + " |",
+              "|---|" + "---|" * len(res["cus_busy_by_slice"]["decode"])]
+    for role in ("decode", "prefill"):
+        lines.append(f"| {role} | " + " | ".join(f"{x:.0f}" for x in res["cus_busy_by_slice"][role]) + " |")
+    return "\n".join(lines) + "\n"
+
+
 def markdown(name: str, res: dict, cmd: str) -> str:
     it, cu = res["per_item_us"], res["per_cu_us"]
     lines = [f"# Phase stamps: bf16 prefill attention, {name}", "",
@@ -176,7 +248,11 @@ def main(argv=None) -> int:
 
     da = _load()
     w = build_workload(args.workload, device="cuda:0", parity=False)
-    call, _, _, _ = _prefill_call(da, torch, w, not args.no_weight_bound)
+    mixed = w.prefill is not None and w.decode is not None
+    if mixed:
+        call = _mixed_call(da, torch, w)
+    else:
+        call, _, _, _ = _prefill_call(da, torch, w, not args.no_weight_bound)
     torch.cuda.synchronize()
     t_end = time.perf_counter() + args.warmup_seconds
     while time.perf_counter() < t_end:
@@ -189,13 +265,22 @@ def main(argv=None) -> int:
     nbytes = da.qkra_phase_stamps_bytes()
     host = np.zeros(nbytes // 8, dtype=np.uint64)
     da.check(da.qkra_phase_stamps_read(host, nbytes), "qkra_phase_stamps_read")
-    res = summarize(host.reshape(-1, 8, 8))
-    if args.json:
+    rec = host.reshape(-1, 8, 8)
+    res = summarize(rec)
+    cmd = "python3 -m decoder_attention_amd.phase_stamps --workload " + args.workload
+    if args.no_weight_bound:
+        cmd += " --no-weight-bound"
+    if mixed:
+        roles = summarize_roles(rec)
+        if args.json:
+            print(json.dumps({"workload": args.workload, "roles": roles, "prefill_items": res}))
+        else:
+            print(markdown_roles(args.workload, roles, cmd), end="")
+            print()
+            print(markdown(args.workload + " (the prefill role's items)", res, cmd).split("\n", 4)[4], end="")
+    elif args.json:
         print(json.dumps({"workload": args.workload, **res}))
     else:
-        cmd = "python3 -m decoder_attention_amd.phase_stamps --workload " + args.workload
-        if args.no_weight_bound:
-            cmd += " --no-weight-bound"
         print(markdown(args.workload, res, cmd), end="")
     return 0
 

@@ -16,7 +16,9 @@
  * QKRA_STAMP_END untouched, so clear the records before the launch to tell
  * them apart.  Slot QKRA_STAMP_WHERE holds HW_ID bits 0-15 (wave, SIMD, CU,
  * shader array, shader engine), XCC_ID bits 16-19, the item's K/V tile count
- * at bits 20-35 and its logical item index from bit 36.
+ * at bits 20-35 and its logical item index at bits 36-62.  In the fused
+ * mixed-step kernel the workgroups of the decode role stamp only
+ * QKRA_STAMP_ENTRY and QKRA_STAMP_END, and set bit 63 of QKRA_STAMP_WHERE.
  */
 #ifndef QKRA_PHASE_STAMPS_H
 #define QKRA_PHASE_STAMPS_H

@@ -56,3 +56,22 @@ def test_summary_of_a_hand_made_record():
     assert abs(cu["tail_idle"] - 12.0) < 1e-9     # (0 + 24) / 2
     md = phase_stamps.markdown("w", res, "cmd")
     assert "| prologue | 9.00 |" in md
+
+
+def test_role_summary_of_a_fused_step_record():
+    # Two decode-role workgroups (bit 63) on CUs 1 and 2, three prefill items on CUs 3, 3 and 1.
+    rec = np.zeros((5, 8, 8), dtype=np.uint64)
+    rows = [(0, 50000, True, 1), (0, 40000, True, 2), (100, 3000, False, 3), (3100, 9000, False, 3),
+            (50100, 60000, False, 1)]
+    for i, (st, en, dec, cu) in enumerate(rows):
+        rec[i, :, 0] = st
+        rec[i, :, 1:6] = [st + 10, st + 20, st + 30, st + 40, en - 10]
+        rec[i, :, 6] = en
+        rec[i, :, 7] = np.uint64((1 << 63) | (cu << 8)) if dec else np.uint64((cu << 8) | (3 << 20) | (i << 36))
+    r = phase_stamps.summarize_roles(rec, bins=4)
+    assert abs(r["span_us"] - 600.0) < 1e-9
+    assert r["decode"]["workgroups"] == 2 and r["decode"]["cus"] == 2 and abs(r["decode"]["last_end_us"] - 500) < 1e-9
+    assert r["prefill"]["workgroups"] == 3 and r["prefill"]["cus"] == 2
+    assert abs(r["decode"]["busy_cu_us"] - 900.0) < 1e-9
+    assert [round(x, 6) for x in r["cus_busy_by_slice"]["decode"]] == [2.0, 2.0, round(5 / 3, 6), round(1 / 3, 6)]
+    assert phase_stamps.summarize(rec)["workgroups"] == 3  # the prefill items only
