@@ -98,6 +98,27 @@ typedef struct qkra_config {
   double rope_base;      /* > 0, e.g. 1e4 or 1e6 */
 } qkra_config;
 
+/*
+ * Finite-input ranges.  With finite inputs every call returns finite results
+ * (each within the stated tolerance of the exact layer) when, additionally:
+ *  - every qkv element of a Q or K head has |x| < 2^60, so that the fp32 sum of
+ *    squares over a head row stays finite;
+ *  - with the running-max softmax (decode, appends, fp32 mode, and a bf16
+ *    prefill whose weights exceed qknorm_rope_attn_unshifted_weight_limit(D)),
+ *    (keys a row attends to) * max|v| < 2^119: the max is raised lazily, only
+ *    when a score passes it by more than 8 in log2 units, so a probability
+ *    stays at most 2^8 inside the fp32 accumulators' 2^128; and
+ *    max|q_norm_weight| * max|k_norm_weight| * D < 2^120, so that a score is
+ *    finite;
+ *  - with the softmax without a shift (a bf16 prefill with no history and
+ *    weights within that limit), every probability is at most 2^48, so
+ *    (keys a row attends to) * max|v| < 2^79 (for example |v| < 2^64 for rows of
+ *    up to 32768 keys).
+ * V enters only the products with the probabilities, so outputs are linear in
+ * V: inside these ranges a power-of-two scale of V scales every output by
+ * exactly that power.
+ */
+
 /* Largest max|q_norm_weight| * max|k_norm_weight| for which a bf16 prefill of
  * head dimension D takes the softmax without a shift (0 for an unsupported D).
  * Pure host computation. */

@@ -192,3 +192,67 @@ def test_weight_bound_in_the_mixed_step():
         outs.append(res["out"][:2])
     assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
     assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+
+
+# ---- the finite V range each path guarantees (include/qknorm_rope_attn.h) ---------------------------------
+# Softmax weights do not depend on V, so every output is linear in V: scaling V by 2^e scales each product,
+# partial sum, row total and the bf16 rounding of the output by exactly 2^e while nothing overflows.  At the
+# stated limits (keys per row times max|V| below 2^79 without a shift, below 2^119 with the running max) the
+# rows stay finite and equal the unscaled ones times 2^e, bit for bit.
+
+def _scaled_v(qkv, h, e):
+    out = qkv.clone()
+    v0 = (h.num_q_heads + h.num_kv_heads) * h.head_dim
+    out[:, v0:] = (out[:, v0:].float() * 2.0**e).to(out.dtype)
+    return out
+
+
+@pytest.mark.parametrize("path,e", [("unshifted", 64), ("running_max", 104)])
+def test_prefill_v_range_scales_exactly(path, e):
+    h = HeadConfig(32, 8, 128, 1e-6, 1e6)
+    lens = [2048, 300]  # up to 2^11 keys per row; drawn |v| < 2^3
+    p = make_prefill_inputs(h, lens, seed=68, device=DEV, capacity=max(lens))
+    prod = float(np.abs(f64(p.q_norm_weight)).max() * np.abs(f64(p.k_norm_weight)).max())
+    bound = prod if path == "unshifted" else 2 * da.qknorm_rope_attn_unshifted_weight_limit(128)
+    assert float(p.qkv.float().abs().max()) < 8 and (2048 * 8 * 2.0**e < 2.0**(79 if path == "unshifted" else 119))
+    cfg = da.make_config(32, 8, 128, torch.bfloat16, 1e-6, 1e6, qk_weight_bound=bound)
+    outs, vcs = [], []
+    for scale in (0, e):
+        qkv = _scaled_v(p.qkv, h, scale)
+        kc, vc = p.k_cache.clone(), p.v_cache.clone()
+        launches = _launches(lambda: outs.append(da.prefill(cfg, qkv, p.q_norm_weight, p.k_norm_weight, p.positions,
+                                                            p.cu_seqlens, p.max_seqlen, kc, vc)[0]))
+        assert launches == {"prefill_attn_mfma_bf16" + ("" if path == "unshifted" else "_shifted"): 1}
+        vcs.append(vc)
+    base, scaled = outs
+    assert torch.isfinite(scaled.float()).all()
+    want = (base.float() * 2.0**e).to(torch.bfloat16)
+    assert torch.equal(scaled.view(torch.int16), want.view(torch.int16)), f"{path}: out scales by 2^{e} exactly"
+    for r, L in enumerate(lens):
+        got = vcs[1][r, :, :L].float()
+        assert torch.equal(got, vcs[0][r, :, :L].float() * 2.0**e)
+    note(f"prefill {path}: V x 2^{e} gives out x 2^{e} bit for bit")
+
+
+def test_decode_v_range_scales_exactly():
+    from workloads import make_decode_inputs
+
+    h = HeadConfig(32, 8, 128, 1e-6, 1e6)
+    e = 104  # 3001 keys * |v| < 8 * 2^104 < 2^119
+    d = make_decode_inputs(h, [5, 700, 3000], seed=69, device=DEV)
+    cfg = da.make_config(32, 8, 128, torch.bfloat16, 1e-6, 1e6)
+    outs = []
+    for scale in (0, e):
+        qkv = _scaled_v(d.qkv, h, scale)
+        kc, vc = d.k_cache.clone(), d.v_cache.clone()
+        for b, L in enumerate([5, 700, 3000]):
+            vc[b, :, :L] = (vc[b, :, :L].float() * 2.0**scale).to(vc.dtype)
+        outs.append(da.decode(cfg, qkv, d.q_norm_weight, d.k_norm_weight, d.positions, d.cache_lens,
+                              d.max_cache_len, kc, vc)[0])
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs[1].float()).all()
+    want = (outs[0].float() * 2.0**e).to(torch.bfloat16)
+    assert torch.equal(outs[1].view(torch.int16), want.view(torch.int16)), "decode: out scales by 2^104 exactly"
+    assert float(d.qkv.float().abs().max()) < 8
+    assert all(float(d.v_cache[b, :, :L].float().abs().max()) < 8 for b, L in enumerate([5, 700, 3000]))
+    note("decode: V x 2^104 gives out x 2^104 bit for bit")
