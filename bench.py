@@ -441,6 +441,38 @@ def cpu_baseline(w, F_total, B_total):
             "sample": "; ".join(parts) + f"; {t_total:.1f} s per step", "step_seconds": t_total}
 
 
+def oracle_host_seconds(w, F_total, B_total, sample_rows=0):
+    """The oracle's host time for one call of a side workload: as cpu_baseline times it, or, for a prefill too
+    long for that (one KV head over 32k tokens), Q/K-norm + RoPE of every token and `sample_rows` output rows
+    spread over the request (all heads each), scaled by the causal FLOP of the sampled rows."""
+    if not sample_rows or w.prefill is None:
+        b = cpu_baseline(w, F_total, B_total)
+        return {"seconds": b["step_seconds"], "sample": b["sample"], "cores": b["cores"]}
+    import numpy as np
+
+    import oracle
+
+    p = w.prefill
+    h = p.heads
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    qkv, wq, wk, pos = f64(p.qkv), f64(p.q_norm_weight), f64(p.k_norm_weight), p.positions.cpu().numpy()
+    cu = p.cu_seqlens.cpu().tolist()
+    t0 = time.perf_counter()
+    qt, kt, v = oracle.qk_norm_rope(qkv, wq, wk, pos, h.num_q_heads, h.num_kv_heads, h.head_dim, h.rms_eps,
+                                    h.rope_base)
+    t_norm = time.perf_counter() - t0
+    lo, hi = cu[0], cu[1]
+    rows = sorted(set(int(x) for x in np.linspace(lo, hi - 1, sample_rows)))
+    t0 = time.perf_counter()
+    oracle.prefill_rows(qt, kt, v, cu, rows)
+    t_rows = time.perf_counter() - t0
+    f_rows = sum(4.0 * h.head_dim * h.num_q_heads * (r - lo + 1) for r in rows)
+    total = t_norm + t_rows * F_total / f_rows
+    return {"seconds": total, "cores": len(os.sched_getaffinity(0)),
+            "sample": f"Q/K-norm + RoPE of all {p.num_tokens} tokens in {t_norm:.2f} s; {len(rows)} rows spread "
+                      f"over request 0 (every head) in {t_rows:.2f} s, scaled by causal FLOP to all rows"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -546,6 +578,8 @@ def main(argv=None):
         calls = out.pop("calls_ms")
         side["single_t64_hq4_hkv2_d64"] = {"prefill_us": calls["prefill"] * 1e3, "decode_us": calls["decode_step_0"] * 1e3,
                                           "reps": 50, "bound": "latency"}
+        if not args.no_cpu_baseline:  # the oracle's prefill of the same 64 tokens on the host
+            side["single_t64_hq4_hkv2_d64"]["cpu_oracle_prefill"] = oracle_host_seconds(sw, r.work()[0], 0.0)
         del sw, r
         # Prefill-only workloads against the MFMA roofline (the attention kernel timed in the same calls).
         for name, reps in (("qwen3_0p6b_prefill_varlen8", 50), ("long_prefill_32k", 12), ("chunked_qwen3_8b", 20)):
@@ -557,6 +591,8 @@ def main(argv=None):
             others = {n: k[n][0] / k[n][1] for n in PREFILL_KERNELS if n in k and n != kname}
             if others:
                 out["kernel"]["other_path_avg_launch_ms"] = others
+            if not args.no_cpu_baseline and name != "chunked_qwen3_8b":
+                out["cpu_oracle"] = oracle_host_seconds(sw, Fs, 0.0, sample_rows=96 if name == "long_prefill_32k" else 0)
             side[name] = out
             del sw, r
             torch.cuda.empty_cache()
@@ -568,6 +604,8 @@ def main(argv=None):
             out["call_gbps"] = Bs / (out["ms_per_call"] / 1e3) / 1e9
             out["call_gbps_flushed"] = Bs / (out["ms_per_call_flushed"] / 1e3) / 1e9
             out["kernel"] = roofline_for("decode_attn_split", k, 0.0, Bs, key, measured=measured)
+            if not args.no_cpu_baseline and key == "qwen3_4b_decode64":
+                out["cpu_oracle"] = oracle_host_seconds(sw, 0.0, Bs)
             side[key] = out
             del sw, r
             torch.cuda.empty_cache()
