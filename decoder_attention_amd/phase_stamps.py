@@ -148,10 +148,16 @@ def summarize(rec: np.ndarray) -> dict:
         m = (steps >= lo) & (steps <= hi) & multi
         if m.any():
             by_tiles[f"{lo}-{hi}"] = float(np.mean(later[m] / (steps[m] - 1)))
+    per_xcd = {}
+    for x in sorted(set(xcc.tolist())):
+        m = xcc == x
+        per_xcd[int(x)] = {"items": int(m.sum()), "last_end_us": float(wg_end[m].max() - base),
+                           "later_step_us": float(np.mean(later[m & multi] / (steps[m & multi] - 1)))
+                           if (m & multi).any() else None}
     return {"workgroups": int(r.shape[0]), "cus": len(per_cu), "workgroups_per_cu": float(np.mean(count)),
             "kernel_span_us": float(span), "per_item_us": item, "per_cu_us": cu_sum,
             "per_cu_share": {k: v / span for k, v in cu_sum.items()},
-            "later_step_us_by_tiles": by_tiles}
+            "later_step_us_by_tiles": by_tiles, "per_xcd": per_xcd}
 
 
 def summarize_roles(rec: np.ndarray, bins: int = 10) -> dict:
@@ -228,6 +234,14 @@ def markdown(name: str, res: dict, cmd: str) -> str:
     if res["later_step_us_by_tiles"]:
         lines += ["", "Later steps (after the first), us per step, by the item's tile count: " +
                   ", ".join(f"{k}: {v:.2f}" for k, v in res["later_step_us_by_tiles"].items()) + "."]
+    if res.get("per_xcd"):
+        lines += ["", "Per XCD (XCC_ID): items, last item end (us from the kernel's start), later-step time (us):", "",
+                  "| XCD | " + " | ".join(str(x) for x in res["per_xcd"]) + " |",
+                  "|---|" + "---|" * len(res["per_xcd"])]
+        lines.append("| items | " + " | ".join(str(v["items"]) for v in res["per_xcd"].values()) + " |")
+        lines.append("| last end | " + " | ".join(f"{v['last_end_us']:.0f}" for v in res["per_xcd"].values()) + " |")
+        lines.append("| step | " + " | ".join("-" if v["later_step_us"] is None else f"{v['later_step_us']:.2f}"
+                                                 for v in res["per_xcd"].values()) + " |")
     return "\n".join(lines) + "\n"
 
 
