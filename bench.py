@@ -298,6 +298,9 @@ def timed_reps(runner, reps: int, warmup: int, mask: int, evict: bool = False, p
     return times, per, kernels
 
 
+WRITES_AS_MUCH_AS_READS = {"qknorm_rope_kv_prefill", "fused_add_rmsnorm"}
+
+
 def roofline_for(name, kernels, F, B, workload, layer_bytes=None, measured=None):
     """The roofline object of kernel `name` from its timed launches."""
     if name not in kernels:
@@ -333,14 +336,19 @@ def roofline_for(name, kernels, F, B, workload, layer_bytes=None, measured=None)
     rf["launches"] = launches
     rf["traffic"] = measured_traffic(name, workload)
     if measured:
-        m = measured.get("hbm_gbps" if rf["unit"] == "GB/s" else "mfma_tflops")
+        # Kernels that write about as many bytes as they read are set against the copy, the rest against the
+        # streaming read or the MFMA loop.
+        kind = ("stream_copy" if name in WRITES_AS_MUCH_AS_READS else "stream_read") if rf["unit"] == "GB/s" \
+            else "mfma_loop"
+        m = measured.get({"stream_copy": "copy_gbps", "stream_read": "hbm_gbps", "mfma_loop": "mfma_tflops"}[kind])
         if m:
             rf["frac_of_measured_peak"] = rf["achieved"] / m
+            rf["measured_peak"] = kind
     return rf
 
 
 def calibration(torch, da):
-    """What this part sustains: a 4 GiB streaming read and a bf16 MFMA loop (median of 10 launches each)."""
+    """What this part sustains: a 4 GiB streaming read, a 2 GiB copy and a bf16 MFMA loop (median of 10 launches each)."""
     dev = "cuda"
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
@@ -364,6 +372,10 @@ def calibration(torch, da):
         reads[wg] = med(lambda: da.check(da.qkra_calibrate_stream_read(buf, nbytes, sink, wg), "stream_read"))
     wg_read = min(reads, key=reads.get)
     t_read = reads[wg_read]
+    half = nbytes // 2  # copy the first 2 GiB of the buffer onto the second
+    src, dst = buf[: half // 4], buf[half // 4:]
+    t_copy = med(lambda: da.check(da.qkra_calibrate_stream_copy(src, dst, half), "stream_copy"))
+    del src, dst
     iters, wg_mfma = 2000, 512
     t_mfma = med(lambda: da.check(da.qkra_calibrate_mfma_bf16(iters, sink, wg_mfma), "mfma_loop"))
     flop = da.qkra_calibrate_mfma_flop(iters, wg_mfma)
@@ -372,6 +384,9 @@ def calibration(torch, da):
             "stream_read": f"4 GiB, each wavefront a contiguous share, 16-byte non-temporal loads, 8 in flight; "
                            f"best of 512/1024/2048 workgroups of 256 ({wg_read}), median of 10",
             "stream_read_gbps_by_workgroups": {str(k): nbytes / (v / 1e3) / 1e9 for k, v in reads.items()},
+            "copy_gbps": 2 * half / (t_copy / 1e3) / 1e9,
+            "stream_copy": "2 GiB onto 2 GiB, one 16-byte piece per thread with non-temporal loads and stores; read "
+                           "plus written bytes over the time, median of 10",
             "mfma_loop": f"{iters} rounds of 4 independent v_mfma_f32_32x32x16_bf16 per wavefront, "
                          f"{wg_mfma} workgroups of 4 wavefronts, median of 10"}
 

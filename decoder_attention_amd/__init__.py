@@ -30,6 +30,7 @@ from .binding import (  # noqa: F401
     calibration_lib,
     calibration_symbols,
     qkra_calibrate_stream_read,
+    qkra_calibrate_stream_copy,
     qkra_calibrate_mfma_bf16,
     qkra_calibrate_mfma_flop,
     phase_stamps_symbols,

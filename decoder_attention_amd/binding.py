@@ -140,6 +140,7 @@ def exported_symbols():
 _calib = None
 _CALIB_SIGNATURES = {
     "qkra_calibrate_stream_read": (_I32, [_P, _SZ, _P, _I32, _P]),
+    "qkra_calibrate_stream_copy": (_I32, [_P, _P, _SZ, _P]),
     "qkra_calibrate_mfma_bf16": (_I32, [ctypes.c_int64, _P, _I32, _P]),
     "qkra_calibrate_mfma_flop": (_SZ, [ctypes.c_int64, _I32]),
 }
@@ -169,6 +170,10 @@ def calibration_symbols():
 def qkra_calibrate_stream_read(buf, nbytes: int, sink, workgroups: int, stream=None) -> int:
     return calibration_lib().qkra_calibrate_stream_read(_ptr(buf), int(nbytes), _ptr(sink), int(workgroups),
                                                         _stream(stream))
+
+
+def qkra_calibrate_stream_copy(src, dst, nbytes: int, stream=None) -> int:
+    return calibration_lib().qkra_calibrate_stream_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream))
 
 
 def qkra_calibrate_mfma_bf16(iterations: int, sink, workgroups: int, stream=None) -> int:

@@ -11,6 +11,8 @@
 //   flight (the access shape of the decode's K/V stream).  The XOR of
 //   everything read is stored only if it equals a value it cannot take, so no
 //   load is removed and nothing is written.
+// * stream copy: one 16-byte piece per thread, non-temporal load and store
+//   (the ceiling of a kernel that writes as much as it reads).
 // * MFMA loop: each wavefront runs four independent chains of
 //   v_mfma_f32_32x32x16_bf16 on register operands (32768 FLOP each), two
 //   wavefronts per SIMD, as the prefill kernel runs.
@@ -55,6 +57,16 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* 
   if (acc == 0x9e3779b9u && threadIdx.x == 1023) sink[0] = acc;  // never taken: threadIdx.x < 256
 }
 
+// A copy: every thread moves one 16-byte piece (non-temporal load and store),
+// a workgroup 4 KB, with as many workgroups as pieces allow.  Of the walks
+// tried (a contiguous share per wavefront with 4 or 8 pieces in flight, 8-32 KB
+// per workgroup, two streams per workgroup) this one moves the most bytes.
+__global__ __launch_bounds__(kReadThreads) void stream_copy_kernel(const u32x4* __restrict__ src,
+                                                                   u32x4* __restrict__ dst, size_t pieces) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * kReadThreads + threadIdx.x;
+  if (i < pieces) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
 __global__ __launch_bounds__(256, 2) void mfma_loop_kernel(int64_t iterations, float* __restrict__ sink) {
   const int lane = threadIdx.x & 63;
   bf16x8 a, b;
@@ -92,6 +104,22 @@ QKRA_CALIB_API int32_t qkra_calibrate_stream_read(const void* buf, size_t bytes,
   hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(workgroups)), dim3(kReadThreads), 0,
                      static_cast<hipStream_t>(hip_stream), static_cast<const u32x4*>(buf), bytes / 16,
                      static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+QKRA_CALIB_API int32_t qkra_calibrate_stream_copy(const void* src, void* dst, size_t bytes, void* hip_stream) {
+  if (src == nullptr || dst == nullptr || bytes % 16 != 0 ||
+      ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) != 0)
+    return 1;
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return 1;  // overlapping buffers
+  const size_t pieces = bytes / 16;
+  const size_t blocks = (pieces + kReadThreads - 1) / kReadThreads;
+  if (blocks > 0x7fffffffull) return 1;
+  if (blocks == 0) return 0;
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kReadThreads), 0,
+                     static_cast<hipStream_t>(hip_stream), static_cast<const u32x4*>(src), static_cast<u32x4*>(dst),
+                     pieces);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 

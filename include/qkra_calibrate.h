@@ -38,6 +38,14 @@ QKRA_CALIB_API int32_t qkra_calibrate_stream_read(const void* buf, size_t bytes,
                                                   int32_t workgroups, void* hip_stream);
 
 /*
+ * Copies `bytes` (a multiple of 16) from `src` to `dst` (both 16-byte aligned,
+ * not overlapping: 1 otherwise): one 16-byte piece per thread, non-temporal
+ * load and store, 256 threads per workgroup, as many workgroups as pieces.
+ * Rate = 2 * bytes / kernel time (bytes read plus bytes written).
+ */
+QKRA_CALIB_API int32_t qkra_calibrate_stream_copy(const void* src, void* dst, size_t bytes, void* hip_stream);
+
+/*
  * `workgroups` workgroups of 4 wavefronts (two per SIMD when there are two
  * per CU), each running `iterations` rounds of four independent
  * v_mfma_f32_32x32x16_bf16 on register operands.  `sink` (workgroups floats)

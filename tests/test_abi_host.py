@@ -38,7 +38,7 @@ def test_calibration_library_exports_every_declared_symbol():
     # The benchmark's roofline calibration kernels live in a library of their own (include/qkra_calibrate.h).
     text = (HEADER.parent / "qkra_calibrate.h").read_text()
     names = sorted(set(re.findall(r"QKRA_CALIB_API\s+[\w\s\*]*?\b(qkra_calibrate_\w+)\s*\(", text)))
-    assert names == da.calibration_symbols() and len(names) == 3
+    assert names == da.calibration_symbols() and len(names) == 4
     lib = da.calibration_lib()
     for name in names:
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
@@ -46,6 +46,9 @@ def test_calibration_library_exports_every_declared_symbol():
     assert da.qkra_calibrate_stream_read(None, 16, BASE, 8, 0) == 1   # refused before any launch
     assert da.qkra_calibrate_stream_read(BASE, 17, BASE, 8, 0) == 1
     assert da.qkra_calibrate_mfma_bf16(0, BASE, 8, 0) == 1
+    assert da.qkra_calibrate_stream_copy(BASE, BASE + 32, 64, 0) == 1   # overlapping
+    assert da.qkra_calibrate_stream_copy(BASE, None, 64, 0) == 1
+    assert da.qkra_calibrate_stream_copy(BASE, BASE + 64, 17, 0) == 1
 
 
 def test_status_strings_and_version():
