@@ -228,6 +228,8 @@ namespace {
 struct DeferredPrefill {
   PrefillAttnArgs args{};
   bool set = false;
+  QkNormRopeArgs k1{};  // kernel 1 of the prefill, launched with the decode's as one launch
+  bool k1_set = false;
 };
 
 int32_t prefill_impl(const qkra_config* cfg, const void* qkv, const void* q_norm_weight, const void* k_norm_weight,
@@ -296,8 +298,16 @@ int32_t prefill_impl(const qkra_config* cfg, const void* qkv, const void* q_norm
   ka.k_cache = k_cache;
   ka.v_cache = v_cache;
   if (paged) ka.paged = *paged;
-  hipError_t err = timed(kKernelQkNormRopePrefill, stream, [&] { return launch_qknorm_rope(ka, stream); });
-  if (err != hipSuccess) return hip_status(err);
+  // A bf16 prefill whose attention the fused step runs: kernel 1 goes out with the decode's, in one launch.
+  const bool attn_deferred = defer && !paged && cfg->dtype == QKRA_BF16 && cache_lens == nullptr;
+  hipError_t err = hipSuccess;
+  if (attn_deferred) {
+    defer->k1 = ka;
+    defer->k1_set = true;
+  } else {
+    err = timed(kKernelQkNormRopePrefill, stream, [&] { return launch_qknorm_rope(ka, stream); });
+    if (err != hipSuccess) return hip_status(err);
+  }
 
   PrefillAttnArgs pa{};
   pa.q = workspace;
@@ -321,7 +331,7 @@ int32_t prefill_impl(const qkra_config* cfg, const void* qkv, const void* q_norm
   if (paged) pa.paged = *paged;
   // A plain bf16 prefill with the caller's weight bound launches only the softmax kernel it selects.
   const SoftmaxPath path = softmax_path(cfg, cache_lens);
-  if (defer && !paged && cfg->dtype == QKRA_BF16 && cache_lens == nullptr) {  // attention runs in the fused step
+  if (attn_deferred) {  // attention runs in the fused step
     // The fused launch is the unshifted kernel; only a bound selecting it spares the running-max launch.
     pa.single_path = path == SoftmaxPath::kUnshifted;
     defer->args = pa;
@@ -374,7 +384,7 @@ namespace {
 int32_t decode_impl(const qkra_config* cfg, const void* qkv, const void* q_norm_weight, const void* k_norm_weight,
                     const int32_t* positions, const int32_t* cache_lens, int32_t num_seqs, int32_t max_cache_len,
                     void* k_cache, void* v_cache, int32_t cache_capacity, void* out, void* workspace,
-                    size_t workspace_bytes, void* hip_stream, bool validate_only, const PrefillAttnArgs* fused,
+                    size_t workspace_bytes, void* hip_stream, bool validate_only, const DeferredPrefill* fused,
                     const PagedTable* paged = nullptr) {
   const int32_t cs = check_config(cfg);
   if (cs != QKRA_OK) return cs;
@@ -440,7 +450,11 @@ int32_t decode_impl(const qkra_config* cfg, const void* qkv, const void* q_norm_
     ka.plan_units = static_cast<int>(decode_units(cfg, num_seqs));
     ka.plan_nchunks = cfg->num_kv_heads * (group / decode_heads_per_wave(group));
   }
-  hipError_t err = timed(kKernelQkNormRopeDecode, stream, [&] { return launch_qknorm_rope(ka, stream); });
+  hipError_t err;
+  if (fused && fused->k1_set)  // the mixed step: the prefill's rows and these in one launch
+    err = timed(kKernelQkNormRopePrefill, stream, [&] { return launch_qknorm_rope_pair(fused->k1, ka, stream); });
+  else
+    err = timed(kKernelQkNormRopeDecode, stream, [&] { return launch_qknorm_rope(ka, stream); });
   if (err != hipSuccess) return hip_status(err);
 
   DecodeAttnArgs da{};
@@ -463,12 +477,13 @@ int32_t decode_impl(const qkra_config* cfg, const void* qkv, const void* q_norm_
     da.num_units = static_cast<int>(decode_units(cfg, num_seqs));
     da.heads_per_wave = decode_heads_per_wave(cfg->num_q_heads / cfg->num_kv_heads);
     if (fused) {
-      err = timed(kKernelFusedStep, stream, [&] { return launch_fused_step(*fused, da, stream); });
+      err = timed(kKernelFusedStep, stream, [&] { return launch_fused_step(fused->args, da, stream); });
       if (err != hipSuccess) return hip_status(err);
       // The running-max kernel takes the items the fused launch's unshifted prefill cannot; with the caller's
       // weight bound selecting the unshifted softmax there are none.
-      if (!fused->single_path)
-        err = timed(kKernelPrefillMfmaShifted, stream, [&] { return launch_prefill_attn_bf16(*fused, false, stream); });
+      if (!fused->args.single_path)
+        err = timed(kKernelPrefillMfmaShifted, stream,
+                    [&] { return launch_prefill_attn_bf16(fused->args, false, stream); });
     } else {
       err = timed(kKernelDecodeSplit, stream, [&] { return launch_decode_mfma(da, stream); });
     }
@@ -637,8 +652,7 @@ QKRA_API int32_t qknorm_rope_attn_mixed_step(
   if (st != QKRA_OK) return st;
   return decode_impl(cfg, decode_qkv, q_norm_weight, k_norm_weight, decode_positions, cache_lens, num_decode_seqs,
                      max_cache_len, decode_k_cache, decode_v_cache, decode_cache_capacity, decode_out,
-                     decode_workspace, decode_workspace_bytes, hip_stream, false,
-                     deferred.set ? &deferred.args : nullptr);
+                     decode_workspace, decode_workspace_bytes, hip_stream, false, deferred.set ? &deferred : nullptr);
 }
 
 // ---- steps next to the attention layer ----------------------------------------

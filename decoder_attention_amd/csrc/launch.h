@@ -90,6 +90,9 @@ struct QkNormRopeArgs {
   PagedTable paged;         // table null: contiguous caches
 };
 hipError_t launch_qknorm_rope(const QkNormRopeArgs& a, hipStream_t stream);
+// A bf16 prefill batch (rope table, no history) and a bf16 decode batch (with its plan) in one launch; both
+// contiguous and with the same norm weights (the mixed step).
+hipError_t launch_qknorm_rope_pair(const QkNormRopeArgs& prefill, const QkNormRopeArgs& decode, hipStream_t stream);
 
 // Kernel 2: causal GQA attention over the prefill caches.  Request r's new token j
 // sits at slot P_r + j and sees slots 0..P_r + j (P_r = past_lens[r], or 0).

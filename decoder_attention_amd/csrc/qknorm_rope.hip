@@ -54,28 +54,20 @@ __device__ __forceinline__ void pack4(const float y[4], u32x4* r) {
   r->z = __float_as_uint(y[2]); r->w = __float_as_uint(y[3]);
 }
 
+// One row of a batch: its Q and K heads normalised and rotated (Q only
+// without a rope table), its V heads copied, K~ and V into the cache.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
-    const T* __restrict__ qkv, const T* __restrict__ q_weight, const T* __restrict__ k_weight,
+__device__ __forceinline__ void qknorm_rope_row(
+    const int row_id, const T* __restrict__ qkv, const T* __restrict__ q_weight, const T* __restrict__ k_weight,
     const int32_t* __restrict__ positions, const int32_t* __restrict__ seq_info,
     const int32_t* __restrict__ slot_offsets, int decode_mode,
     int num_seqs, int num_q_heads, int num_kv_heads, int cache_capacity, float eps,
     double log2_base, T* __restrict__ q_out, float* __restrict__ rope_table, T* __restrict__ k_cache,
-    T* __restrict__ v_cache, int num_rows, int32_t* __restrict__ plan, int plan_units, int plan_nchunks,
-    PagedTable paged) {
+    T* __restrict__ v_cache, PagedTable paged, float* s_cos, float* s_sin) {
   using Raw = typename Raw4<T>::type;
   constexpr int HALF = D / 2;
   constexpr int LPH = HALF / 4;  // lanes per head row
   constexpr int HPW = 64 / LPH;  // head rows per wavefront pass
-  __shared__ float s_cos[HALF];
-  __shared__ float s_sin[HALF];
-
-  const int row_id = blockIdx.x;
-  if (row_id == num_rows) {  // bf16 decode: the block past the rows builds the split kernel's plan
-    __shared__ int32_t s_scan[256];
-    build_decode_plan<256>(seq_info, plan, plan_units, plan_nchunks, cache_capacity, s_scan);
-    return;
-  }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
@@ -207,6 +199,76 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
 }
 
 template <typename T, int D>
+__global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
+    const T* __restrict__ qkv, const T* __restrict__ q_weight, const T* __restrict__ k_weight,
+    const int32_t* __restrict__ positions, const int32_t* __restrict__ seq_info,
+    const int32_t* __restrict__ slot_offsets, int decode_mode,
+    int num_seqs, int num_q_heads, int num_kv_heads, int cache_capacity, float eps,
+    double log2_base, T* __restrict__ q_out, float* __restrict__ rope_table, T* __restrict__ k_cache,
+    T* __restrict__ v_cache, int num_rows, int32_t* __restrict__ plan, int plan_units, int plan_nchunks,
+    PagedTable paged) {
+  __shared__ float s_cos[D / 2];
+  __shared__ float s_sin[D / 2];
+  const int row_id = blockIdx.x;
+  if (row_id == num_rows) {  // bf16 decode: the block past the rows builds the split kernel's plan
+    __shared__ int32_t s_scan[256];
+    build_decode_plan<256>(seq_info, plan, plan_units, plan_nchunks, cache_capacity, s_scan);
+    return;
+  }
+  qknorm_rope_row<T, D>(row_id, qkv, q_weight, k_weight, positions, seq_info, slot_offsets, decode_mode, num_seqs,
+                        num_q_heads, num_kv_heads, cache_capacity, eps, log2_base, q_out, rope_table, k_cache,
+                        v_cache, paged, s_cos, s_sin);
+}
+
+// Two batches in one launch of single-wavefront blocks (the mixed step: the
+// decode rows with q~, a block for the split kernel's plan, then the prefill
+// rows with their rope table), so the decode rows run beside the prefill rows
+// instead of in a launch of their own.  Both use the same norm weights and
+// contiguous caches.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void qknorm_rope_kv_pair_kernel(
+    const T* __restrict__ q_weight, const T* __restrict__ k_weight, int num_q_heads, int num_kv_heads, float eps,
+    double log2_base,
+    const T* __restrict__ p_qkv, const int32_t* __restrict__ p_positions, const int32_t* __restrict__ p_cu,
+    int p_num_seqs, int p_cache_capacity, float* __restrict__ p_rope_table, T* __restrict__ p_k_cache,
+    T* __restrict__ p_v_cache, int p_rows,
+    const T* __restrict__ d_qkv, const int32_t* __restrict__ d_positions, const int32_t* __restrict__ d_lens,
+    int d_cache_capacity, T* __restrict__ d_q_out, T* __restrict__ d_k_cache, T* __restrict__ d_v_cache,
+    int d_rows, int32_t* __restrict__ plan, int plan_units, int plan_nchunks) {
+  __shared__ float s_cos[D / 2];
+  __shared__ float s_sin[D / 2];
+  // The decode rows (every head of a row in one wavefront, so each takes longer than a prefill row) and the plan
+  // go first, beside the prefill rows that follow.
+  const int block = blockIdx.x;
+  if (block < d_rows) {
+    qknorm_rope_row<T, D>(block, d_qkv, q_weight, k_weight, d_positions, d_lens, nullptr, 1, d_rows, num_q_heads,
+                          num_kv_heads, d_cache_capacity, eps, log2_base, d_q_out, nullptr, d_k_cache, d_v_cache,
+                          PagedTable{}, s_cos, s_sin);
+  } else if (block == d_rows) {
+    __shared__ int32_t s_scan[64];
+    build_decode_plan<64>(d_lens, plan, plan_units, plan_nchunks, d_cache_capacity, s_scan);
+  } else {
+    qknorm_rope_row<T, D>(block - d_rows - 1, p_qkv, q_weight, k_weight, p_positions, p_cu, nullptr, 0, p_num_seqs,
+                          num_q_heads, num_kv_heads, p_cache_capacity, eps, log2_base, nullptr, p_rope_table,
+                          p_k_cache, p_v_cache, PagedTable{}, s_cos, s_sin);
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_pair_typed(const QkNormRopeArgs& p, const QkNormRopeArgs& d, hipStream_t stream) {
+  const int blocks = p.num_rows + d.num_rows + 1;
+  launch_kernel((qknorm_rope_kv_pair_kernel<T, D>), dim3(blocks), dim3(64), 0, stream,
+                static_cast<const T*>(p.q_norm_weight), static_cast<const T*>(p.k_norm_weight), p.num_q_heads,
+                p.num_kv_heads, p.rms_eps, p.log2_rope_base,
+                static_cast<const T*>(p.qkv), p.positions, p.seq_info, p.num_seqs, p.cache_capacity, p.rope_table,
+                static_cast<T*>(p.k_cache), static_cast<T*>(p.v_cache), p.num_rows,
+                static_cast<const T*>(d.qkv), d.positions, d.seq_info, d.cache_capacity, static_cast<T*>(d.q_out),
+                static_cast<T*>(d.k_cache), static_cast<T*>(d.v_cache), d.num_rows, d.plan, d.plan_units,
+                d.plan_nchunks);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
 hipError_t launch_typed(const QkNormRopeArgs& a, hipStream_t stream) {
   // bf16 prefill (K and V heads only): one wavefront per token, whose four
   // prefetched passes cover its 2*Hkv rows for Hkv <= 8 and whose fp64 angles
@@ -231,6 +293,20 @@ hipError_t launch_qknorm_rope(const QkNormRopeArgs& a, hipStream_t stream) {
   const bool bf = a.dtype == 0;
   if (a.head_dim == 128) return bf ? launch_typed<bf16, 128>(a, stream) : launch_typed<float, 128>(a, stream);
   if (a.head_dim == 64) return bf ? launch_typed<bf16, 64>(a, stream) : launch_typed<float, 64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_qknorm_rope_pair(const QkNormRopeArgs& prefill, const QkNormRopeArgs& decode, hipStream_t stream) {
+  // bf16 only: a prefill batch with its rope table and no history, a decode batch with its plan; contiguous caches,
+  // one set of norm weights.
+  if (prefill.dtype != 0 || decode.dtype != 0 || !prefill.rope_table || prefill.slot_offsets || prefill.decode_mode ||
+      !decode.decode_mode || !decode.plan || decode.rope_table || prefill.paged.table || decode.paged.table ||
+      prefill.q_norm_weight != decode.q_norm_weight || prefill.k_norm_weight != decode.k_norm_weight ||
+      prefill.head_dim != decode.head_dim || prefill.num_q_heads != decode.num_q_heads ||
+      prefill.num_kv_heads != decode.num_kv_heads)
+    return hipErrorInvalidValue;
+  if (prefill.head_dim == 128) return launch_pair_typed<bf16, 128>(prefill, decode, stream);
+  if (prefill.head_dim == 64) return launch_pair_typed<bf16, 64>(prefill, decode, stream);
   return hipErrorInvalidValue;
 }
 
