@@ -74,4 +74,15 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, NT ? 2 : 0));
 }
 
+// 16 bytes per lane from a buffer straight into LDS (gfx950 buffer_load_dwordx4
+// ... lds): lane i's piece lands at lds + 16 i bytes, so one instruction
+// fills 1 KB of consecutive LDS.  An offset >= the resource's range writes
+// zeros.  Counted by vmcnt, like any vector-memory load.
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t offset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, offset, 0, 0, 0);
+}
+
+// s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt left at their maxima).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 }  // namespace qkra

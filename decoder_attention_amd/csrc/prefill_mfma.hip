@@ -20,11 +20,12 @@
 //    16 of the 32 keys of a block, so the row max needs one exchange with lane
 //    ^ 32 and the row sum none until the very end.
 //  * O^T = V^T P^T with the same instruction: P^T goes straight from the
-//    score accumulators into the B operand (after rounding to bf16), and V is
-//    staged in LDS transposed ([d][key]) with the keys of every 16-key step
-//    permuted so that each lane's 8 keys are one 16-byte read.  The O^T
-//    accumulator is again one query per lane, so the online-softmax rescale
-//    is a per-lane multiply.
+//    score accumulators into the B operand (after rounding to bf16).  V stays
+//    row-major in LDS, as the cache holds it; the V^T operand comes from it
+//    through gfx950's transposing LDS read (ds_read_b64_tr_b16), two per
+//    operand, whose lanes receive exactly the keys the P^T operand holds.
+//    The O^T accumulator is again one query per lane, so the online-softmax
+//    rescale is a per-lane multiply.
 //  * Softmax in the log2 domain: q~ is multiplied by log2(e)/sqrt(D) before
 //    its bf16 rounding, so a score is already the exponent of 2 that softmax
 //    takes.  Softmax is unchanged by a common shift of a row's scores, and
@@ -43,15 +44,20 @@
 //    run only up to the causal diagonal of the workgroup's last token; tiles
 //    entirely above a wavefront's rows are skipped by that wavefront; only
 //    tiles that cross the diagonal are masked.
-//  * Keys at or past the request's length read as zeros (buffer loads with
-//    the range ending at the last key), so whatever the cache holds there
+//  * K/V tiles go from global memory straight into LDS (buffer loads with
+//    the LDS flag, no registers, no LDS stores): 16 bytes per lane, the
+//    lanes spread over the rows so that the tile lands with its padded row
+//    strides.  Keys at or past the request's length read as zeros (the
+//    buffer range ends at the last key), so whatever the cache holds there
 //    never reaches the accumulators.
-//  * Three LDS slots: step kt forms tile kt+1's scores while it turns tile
-//    kt's scores into probabilities and multiplies them by tile kt's V; tile
-//    kt+2 is loaded from global memory meanwhile and stored into the third
-//    slot.  One barrier per step.  The tile loop is unrolled by six so that
-//    every slot index, hence every LDS address offset, is a compile-time
-//    constant.
+//  * Three LDS slots, each K and V slot an array of its own: step kt forms
+//    tile kt+1's scores while it turns tile kt's scores into probabilities
+//    and multiplies them by tile kt's V; tile kt+2 streams into the third
+//    slot meanwhile.  Separate arrays let the compiler see that the loads
+//    into one slot do not touch the slots being read, so it waits for them
+//    only at the step's end.  One barrier per step.  The tile loop is
+//    unrolled by six so that every slot, hence every LDS address, is a
+//    compile-time constant.
 //  * Grid: work items ordered by (KV-head chunk, request, query tile from the
 //    last), and block ids remapped so that consecutive items land on the same
 //    XCD (the hardware deals workgroups round-robin over the 8 XCDs).  The
@@ -97,6 +103,13 @@ __device__ __forceinline__ float half_wave_max(float x) {
 }
 
 constexpr int NSLOT = 3;  // LDS tile slots
+
+// ds_read_b64_tr_b16 from a generic pointer into LDS (the address-space cast
+// keeps which LDS array it reads, so loads into other arrays need not be
+// waited for).
+__device__ __forceinline__ dbody::s16x4 read_tr16(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) dbody::s16x4*)(const_cast<bf16*>(p)));
+}
 
 // ---- phase stamps (the profiling build, -DQKRA_PHASE_STAMPS, only) ----------
 // Every prefill workgroup's wavefronts record the 100 MHz constant clock
@@ -219,13 +232,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   constexpr int DB = D / 32;        // 32-wide blocks of D in the output
   constexpr int KB = BN / 32;       // 32-key blocks per tile
   constexpr int KSTEPS = BN / 16;   // 16-key steps per tile
-  constexpr int KST = D + 8;        // LDS row stride of K (elements)
-  constexpr int VST = BN + 8;       // LDS row stride of V^T (elements)
-  constexpr int KCH = BN * D / 8;   // 16-byte K chunks per tile
-  constexpr int KCHUNKS = (KCH + NTHREADS - 1) / NTHREADS;
-  constexpr int VITEMS = (BN / 4) * (D / 8);  // (4 keys x 8 d) V items per tile
-  __shared__ __attribute__((aligned(16))) bf16 sK[NSLOT][BN * KST];
-  __shared__ __attribute__((aligned(16))) bf16 sV[NSLOT][D * VST];
+  constexpr int KST = D + 8;        // LDS row stride of K (elements): 16 bytes of pad
+  constexpr int VRS = D + 32;       // LDS row stride of V, row-major (elements): 64 bytes of pad
+  // One LDS array per slot: the compiler then knows that a tile load into
+  // one slot does not touch another, and waits for it only where its slot is read.
+  __shared__ __attribute__((aligned(16))) bf16 sK0[BN * KST], sK1[BN * KST], sK2[BN * KST];
+  __shared__ __attribute__((aligned(16))) bf16 sV0[BN * VRS], sV1[BN * VRS], sV2[BN * VRS];
+  auto kslot = [&](auto sc) -> bf16* {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s == 0) return sK0; else if constexpr (s == 1) return sK1; else return sK2;
+  };
+  auto vslot = [&](auto sc) -> bf16* {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s == 0) return sV0; else if constexpr (s == 1) return sV1; else return sV2;
+  };
+  // The six slot arrays by a wave-uniform index (K slots first).
+  auto region = [&](int i) -> bf16* {
+    return i == 0 ? sK0 : i == 1 ? sK1 : i == 2 ? sK2 : i == 3 ? sV0 : i == 4 ? sV1 : sV2;
+  };
 
   // ---- work item (XCD-aware remap; per request, heaviest tiles first) -------
   const PhaseStamps stamps;
@@ -236,11 +260,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     if (bid < dec.wgs) {  // decode role (the fused step): its wavefronts' tiles in the K and V slots
       const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
       constexpr int DT = kDecodeStepKeys * (D + 8);  // elements of one decode tile
-      static_assert(3 * 2 * DT <= NSLOT * BN * KST && 3 * 2 * DT <= NSLOT * D * VST &&
-                        kFusedDecodeWavesPerWg == 6 && NWAVES >= 6,
-                    "three decode wavefronts' K and V tiles fit in each of the K and V slot arrays");
+      static_assert(2 * DT <= BN * KST && 2 * DT <= BN * VRS && kFusedDecodeWavesPerWg == 6 && NWAVES >= 6,
+                    "a decode wavefront's K and V tiles fit in one slot array");
       if (wv < kFusedDecodeWavesPerWg) {
-        bf16* base = wv < 3 ? &sK[0][0] + wv * 2 * DT : &sV[0][0] + (wv - 3) * 2 * DT;
+        bf16* base = region(wv);
         dbody::decode_wave<D, kDecGW>(base, base + DT, bid * kFusedDecodeWavesPerWg + wv, dec.q, dec.k_cache,
                                       dec.v_cache, dec.cache_lens, dec.plan, dec.partials, num_q_heads, num_kv_heads,
                                       dec.cache_capacity, dec.chunks_per_kv, dec.num_units, scale_log2);
@@ -309,16 +332,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   // reads whole 128-byte lines (a lane-per-row load touches 32 lines per
   // instruction and made the prologue twice as long).  The row's sum of
   // squares is reduced over its QLPR lanes.  Each wavefront then passes its
-  // 32 x D tile through its own LDS region (in slots 1 and 2, free until the
-  // second tile is stored) into the fragment layout.  Rows past the
-  // request's end are zero.
+  // 32 x D tile through its own LDS region into the fragment layout.  Rows
+  // past the request's end are zero.
   constexpr int QLPR = D / 16;       // lanes per row
   constexpr int QRPI = 64 / QLPR;    // rows per load instruction
   constexpr int QNG = 32 / QRPI;     // load groups per 32-row block
   constexpr int EST = D + 8;         // LDS row stride of a staged 32 x D tile (elements)
-  static_assert(NWAVES / 2 * 32 * EST <= (NSLOT - 1) * BN * KST &&
-                    NWAVES / 2 * 32 * EST <= (NSLOT - 1) * D * VST,
-                "the staged Q tiles fit in LDS slots 1 and 2");
+  // Slots 0 and 1 take the first two K/V tiles while Q is staged: wavefronts 0-1 stage in slot 2 of the K
+  // array, 2-3 in slot 2 of the V array, the others in a region of their own.
+  static_assert(NWAVES == 8 && 2 * 32 * EST <= BN * KST && 2 * 32 * EST <= BN * VRS, "Q staging layout");
+  __shared__ __attribute__((aligned(16))) bf16 sQ[(NWAVES - 4) * 32 * EST];
   const int qj = lane % QLPR;
   const int qr = lane / QLPR;
   bf16x8 qf[QB][DS];
@@ -350,7 +373,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   auto q_finish = [&]() {
     const u32x4 wlo = *reinterpret_cast<const u32x4*>(q_norm_weight + 8 * qj);
     const u32x4 whi = *reinterpret_cast<const u32x4*>(q_norm_weight + D / 2 + 8 * qj);
-    bf16* stage = (wave < NWAVES / 2 ? &sK[1][0] : &sV[1][0]) + (wave % (NWAVES / 2)) * 32 * EST;
+    bf16* stage = wave < 2 ? sK2 + wave * 32 * EST : (wave < 4 ? sV2 + (wave - 2) * 32 * EST : sQ + (wave - 4) * 32 * EST);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -418,76 +441,70 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   const bf16* kbase = k_cache + head_off;
   const bf16* vbase = v_cache + head_off;
 
-  // ---- global -> registers -> LDS staging -------------------------------------
-  // Buffer loads over rows k0 .. kv_end-1 of the tile: the resource is formed
-  // per tile in scalar registers and every lane's offset is loop-invariant.
-  // Rows at or past kv_end read as zeros (finite; every such key lies after
-  // every stored query row and is removed by the causal mask).
-  u32x4 kreg[KCHUNKS];
-  u32x4 vreg[4];
-  const int v_kq = tid % (BN / 4);   // which 4-key quad of the tile
-  const int v_dq = tid / (BN / 4);   // which 8-wide slice of D
-  const bool v_loader = tid < VITEMS;
-  const uint32_t v_off = static_cast<uint32_t>((4 * v_kq * D + v_dq * 8) * 2);
-
-  auto load_tile = [&](int kt) {
+  // ---- global -> LDS, by DMA --------------------------------------------------
+  // Buffer loads that write LDS directly (no registers): each instruction
+  // moves 64 16-byte pieces to 1 KB of consecutive LDS, lane i to piece i,
+  // and a lane whose offset is past the buffer range writes zeros without
+  // touching memory.  The pieces are assigned so that LDS holds K rows at a
+  // stride of D+8 elements and V rows (row-major) at D+32; the lanes that
+  // land on a row's pad take an offset past the range.  The resource covers
+  // the tile's rows below kv_end, so rows at or past kv_end arrive as zeros
+  // too (finite, so p = 0 times V stays 0; every such key lies after every
+  // stored query row and is removed by the causal mask).  Each wavefront
+  // issues instructions wave, wave + 8, ... of a tile; its lane offsets are
+  // loop-invariant.  The 16-byte padding spreads a K fragment read over all
+  // banks; V's 64 bytes do the same for the transposing reads below.
+  constexpr int KRC = KST / 8, VRC = VRS / 8;               // 16-byte pieces per LDS row
+  constexpr int KDMA = BN * KRC / 64, VDMA = BN * VRC / 64;  // instructions per tile
+  constexpr int KJ = (KDMA + NWAVES - 1) / NWAVES, VJ = (VDMA + NWAVES - 1) / NWAVES;
+  static_assert(BN * KRC % 64 == 0 && BN * VRC % 64 == 0, "whole instructions per tile");
+  constexpr uint32_t kPastRange = 0x7ffffff0u;
+  uint32_t koff[KJ], voff[VJ];
+#pragma unroll
+  for (int j = 0; j < KJ; ++j) {
+    const int p = 64 * (wave + NWAVES * j) + lane, r = p / KRC, c = p % KRC;
+    koff[j] = c < D / 8 ? static_cast<uint32_t>(r * D * 2 + c * 16) : kPastRange;
+  }
+#pragma unroll
+  for (int j = 0; j < VJ; ++j) {
+    const int p = 64 * (wave + NWAVES * j) + lane, r = p / VRC, c = p % VRC;
+    voff[j] = c < D / 8 ? static_cast<uint32_t>(r * D * 2 + c * 16) : kPastRange;
+  }
+  auto load_tile = [&](int kt, auto slotc) {
     const int k0 = kt * BN;
-    uint32_t bytes = static_cast<uint32_t>(kv_end - k0) * D * 2;
+    const uint32_t bytes = static_cast<uint32_t>(min(kv_end - k0, BN)) * D * 2;
     const bf16* kt_base = kbase + static_cast<size_t>(k0) * D;
     const bf16* vt_base = vbase + static_cast<size_t>(k0) * D;
     if constexpr (kPaged) {  // the tile's rows, from the page that holds them
       const size_t row = paged_row(paged, seq, g, k0, num_kv_heads, D);
       kt_base = k_cache + row;
       vt_base = v_cache + row;
-      bytes = static_cast<uint32_t>(min(kv_end - k0, BN)) * D * 2;
     }
     const auto rk = buffer_rsrc(kt_base, bytes);
     const auto rv = buffer_rsrc(vt_base, bytes);
-    static_for<KCHUNKS>([&](auto i) {
-      const int c = tid + NTHREADS * i;  // 16-byte chunk c of the tile's contiguous rows
-      if (KCH % NTHREADS == 0 || c < KCH) kreg[i] = buffer_load16<false>(rk, static_cast<uint32_t>(c) * 16);
+    static_for<KJ>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int i = wave + NWAVES * j;
+      if (j + 1 < KJ || i < KDMA) buffer_load16_lds(rk, kslot(slotc) + i * 512, koff[j]);
     });
-    if (v_loader) {
-      static_for<4>([&](auto r) { vreg[r] = buffer_load16<false>(rv, v_off + decltype(r)::value * D * 2); });
-    }
-  };
-
-  // LDS slots are compile-time constants (the tile loop below is unrolled by
-  // the ring length), so every fragment address is one base register plus an
-  // immediate offset.
-  auto store_tile = [&](auto slotc) {
-    constexpr int slot = decltype(slotc)::value;
-    static_for<KCHUNKS>([&](auto i) {
-      const int c = tid + NTHREADS * i;
-      if (KCH % NTHREADS == 0 || c < KCH)
-        *reinterpret_cast<u32x4*>(&sK[slot][(c / (D / 8)) * KST + (c % (D / 8)) * 8]) = kreg[i];
+    static_for<VJ>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int i = wave + NWAVES * j;
+      if (j + 1 < VJ || i < VDMA) buffer_load16_lds(rv, vslot(slotc) + i * 512, voff[j]);
     });
-    if (v_loader) {
-      // Keys 4*kq..4*kq+3 of one 8-wide d slice, written transposed.  Within
-      // each 16-key step the key quads are stored in the order 0, 2, 1, 3, so
-      // that lane half `hi` finds its keys {4hi..4hi+3, 8+4hi..8+4hi+3} as 8
-      // contiguous elements.
-      const int step = v_kq >> 2;
-      const int quad = v_kq & 3;
-      const int pos = 16 * step + 4 * ((quad & 1) * 2 + (quad >> 1));
-      const u32x4 w0 = vreg[0], w1 = vreg[1], w2 = vreg[2], w3 = vreg[3];
-      static_for<4>([&](auto pc) {
-        constexpr int p = decltype(pc)::value;
-        const u32x2 lo = {__builtin_amdgcn_perm(w1[p], w0[p], 0x05040100u),
-                          __builtin_amdgcn_perm(w3[p], w2[p], 0x05040100u)};
-        const u32x2 hv = {__builtin_amdgcn_perm(w1[p], w0[p], 0x07060302u),
-                          __builtin_amdgcn_perm(w3[p], w2[p], 0x07060302u)};
-        *reinterpret_cast<u32x2*>(&sV[slot][(v_dq * 8 + 2 * p) * VST + pos]) = lo;
-        *reinterpret_cast<u32x2*>(&sV[slot][(v_dq * 8 + 2 * p + 1) * VST + pos]) = hv;
-      });
-    }
   };
+  // V^T operands come from row-major V by transposing reads: lane (hi, g16, l16)
+  // of a read gives keys R0 .. R0+3 of column C0 + l16, R0 = 16ks + 4hi (then
+  // + 8), C0 = 32db + 16g16, i.e. d = 32db + l32 and the keys the P^T operand
+  // of lane half hi holds.  With rows 320 (D = 128) or 192 (D = 64) bytes apart
+  // the 64 lanes' 8-byte reads cover every bank exactly twice.
+  const int vlane = (4 * hi + ((lane & 15) >> 2)) * VRS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   // ---- the matrix and softmax pieces ----------------------------------------
   // S^T = K Q^T for the tile in `slot`: lane holds query l32 and, per 32-key
   // block kb, keys 32kb + 8(j/4) + 4hi + j%4 in register j.
   auto scores = [&](auto slotc, f32x16 (&S)[QB][KB]) {
-    constexpr int slot = decltype(slotc)::value;
+    const bf16* sk = kslot(slotc);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -496,7 +513,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     for (int ds = 0; ds < DS; ++ds) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[slot][(kb * 32 + l32) * KST + 16 * ds + 8 * hi]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sk[(kb * 32 + l32) * KST + 16 * ds + 8 * hi]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           S[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ds], S[qb][kb], 0, 0, 0);
@@ -580,12 +597,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
 
   // O^T += V^T P^T for the tile in `slot`.
   auto pv = [&](auto slotc, const bf16x8 (&pf)[QB][KSTEPS]) {
-    constexpr int slot = decltype(slotc)::value;
+    const bf16* sv = vslot(slotc) + vlane;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[slot][(db * 32 + l32) * VST + 16 * ks + 8 * hi]);
+        const bf16* vp = sv + 16 * ks * VRS + 32 * db;
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(read_tr16(vp), read_tr16(vp + 8 * VRS),
+                                                                             0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][ks], acc[qb][db], 0, 0, 0);
@@ -596,8 +615,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   // scores and m_run already covers them.  Step kt forms tile kt+1's scores
   // on the matrix cores while the vector units turn tile kt into
   // probabilities, then issues tile kt's P.V while the vector units mask and
-  // reduce tile kt+1.  Tile kt+2 is fetched from global memory meanwhile and
-  // written to the third LDS slot.
+  // reduce tile kt+1.  Tile kt+2 streams into the third LDS slot meanwhile.
   // The next tile's scores are formed even on a wavefront's last tile (from
   // whatever the slot holds, and then dropped): that keeps the score, the
   // probability and the P.V work of a step in one branch-free block, so the
@@ -610,7 +628,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     using SlotS = std::integral_constant<int, (J + 1) % NSLOT>;
     using SlotLd = std::integral_constant<int, (J + 2) % NSLOT>;
     const bool prefetch = kt + 2 < ntiles;
-    if (prefetch) load_tile(kt + 2);
+    if (prefetch) load_tile(kt + 2, SlotLd{});
     if (kt < wtiles) {
       bf16x8 pf[QB][KSTEPS];
       scores(SlotS{}, Snext);
@@ -625,17 +643,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
         }
       }
     }
-    if (prefetch) store_tile(SlotLd{});
+    if (prefetch) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wavefront's tile kt+2 is in LDS
     __syncthreads();
   };
 
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
-  // Tile 0's loads go out first, then Q's.  Tile 0 is stored as soon as it
-  // lands (Q is still in flight), tile 1's loads go out, and Q is finished
-  // meanwhile; tile 1 enters slot 1 once every wavefront has read its Q
-  // fragments from there.
-  load_tile(0);
+  // Tiles 0 and 1 stream into slots 0 and 1 while Q is loaded, normalised,
+  // rotated and staged (in slot 2 and a region of its own).
+  load_tile(0, C0{});
+  if (ntiles > 1) load_tile(1, C1{});
   q_issue();
   if constexpr (kBounded) {
     if (!scores_bounded(wmax, past, bound_limit)) {
@@ -659,12 +676,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     }
   }
   stamps.now(QKRA_STAMP_ISSUED);
-  store_tile(C0{});
-  if (ntiles > 1) load_tile(1);
   q_finish();
   stamps.now(QKRA_STAMP_Q_READY);
-  __syncthreads();
-  if (ntiles > 1) store_tile(C1{});
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // tiles 0 and 1 are in LDS
   __syncthreads();
   f32x16 sA[QB][KB], sB[QB][KB];
   scores(C0{}, sA);
@@ -700,9 +714,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   // tile row-major into its own LDS region (the K/V slots are free: the last
   // step ended with a barrier) and stores whole rows from there, 16 lanes
   // per row, 16 bytes each.
-  static_assert(NWAVES / 2 * 32 * EST <= NSLOT * BN * KST && NWAVES / 2 * 32 * EST <= NSLOT * D * VST,
-                "the output tiles fit in the K and V slots");
-  bf16* stile = (wave < NWAVES / 2 ? &sK[0][0] : &sV[0][0]) + (wave % (NWAVES / 2)) * 32 * EST;
+  static_assert(NWAVES == 8 && 2 * 32 * EST <= BN * KST && 2 * 32 * EST <= BN * VRS,
+                "two output tiles fit in each slot array");
+  bf16* stile = region(wave / 2) + (wave % 2) * 32 * EST;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + xor_shuffle(l_run[qb], 32);
