@@ -33,10 +33,10 @@ from .build import STAMPS_LIB_PATH
 TICK_US = 0.01  # s_memrealtime counts a 100 MHz clock
 
 
-def _load():
+def _load(path=STAMPS_LIB_PATH):
     import decoder_attention_amd as da
 
-    da.select_library(STAMPS_LIB_PATH)
+    da.select_library(path)
     da.lib()
     return da
 
@@ -252,6 +252,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-weight-bound", action="store_true",
                     help="do not pass the norm weights' bound (both softmax kernels are launched)")
     ap.add_argument("--json", action="store_true", help="print the summary as one JSON line")
+    ap.add_argument("--library", default=STAMPS_LIB_PATH,
+                    help="a library built with -DQKRA_PHASE_STAMPS (default: the package's profiling build)")
     args = ap.parse_args(argv)
     import torch
 
@@ -260,7 +262,7 @@ def main(argv=None) -> int:
         sys.path.insert(0, root)
     from workloads import build_workload
 
-    da = _load()
+    da = _load(os.path.abspath(args.library))
     w = build_workload(args.workload, device="cuda:0", parity=False)
     mixed = w.prefill is not None and w.decode is not None
     if mixed:
