@@ -16,12 +16,12 @@
 // table, four otherwise).  The D/2 rotation angles
 // of the row are formed once in fp64 (position * base^(-2i/D), then sin/cos)
 // and kept in LDS, so positions up to tens of thousands keep full fp32
-// accuracy in cos/sin.  Each head row is handled by D/8 lanes: a lane holds 4
-// elements of the first half and the 4 matching elements of the second half,
-// so every rotate-half pair stays inside one lane and the rotation needs no
-// cross-lane traffic; only the sum of squares is reduced across the D/8 lanes.
-// Loads and stores are 8 B (bf16) or 16 B (fp32) per lane, contiguous across
-// the lanes of a head.  A wavefront's first four passes are loaded before the
+// accuracy in cos/sin.  Each head row is handled by D/16 (bf16) or D/8 (fp32)
+// lanes: a lane holds 16 bytes of the first half and the matching 16 bytes of
+// the second half, so every rotate-half pair stays inside one lane and the
+// rotation needs no cross-lane traffic; only the sum of squares is reduced
+// across the row's lanes.  Loads and stores are 16 B per lane, contiguous
+// across the lanes of a head (8-byte pieces ran 2-3% slower).  A wavefront's first four passes are loaded before the
 // request lookup and the angle computation, so those latencies overlap.  With
 // a block table the cache rows are found through it (a paged pool); slots
 // still count from the request's first entry.
@@ -33,25 +33,21 @@
 namespace qkra {
 namespace {
 
-template <typename T> struct Raw4;
-template <> struct Raw4<bf16> { typedef u32x2 type; };
-template <> struct Raw4<float> { typedef u32x4 type; };
+// A lane's 16-byte piece of a half row: 8 bf16 or 4 fp32 elements.
+template <typename T> constexpr int kLaneElems = 16 / sizeof(T);
 
-__device__ __forceinline__ void unpack4(u32x2 r, float x[4]) {
-  x[0] = bf16_lo_to_f32(r.x); x[1] = bf16_hi_to_f32(r.x);
-  x[2] = bf16_lo_to_f32(r.y); x[3] = bf16_hi_to_f32(r.y);
+__device__ __forceinline__ void unpack(u32x4 r, float x[8], const bf16*) {
+  x[0] = bf16_lo_to_f32(r.x); x[1] = bf16_hi_to_f32(r.x); x[2] = bf16_lo_to_f32(r.y); x[3] = bf16_hi_to_f32(r.y);
+  x[4] = bf16_lo_to_f32(r.z); x[5] = bf16_hi_to_f32(r.z); x[6] = bf16_lo_to_f32(r.w); x[7] = bf16_hi_to_f32(r.w);
 }
-__device__ __forceinline__ void unpack4(u32x4 r, float x[4]) {
-  x[0] = __uint_as_float(r.x); x[1] = __uint_as_float(r.y);
-  x[2] = __uint_as_float(r.z); x[3] = __uint_as_float(r.w);
+__device__ __forceinline__ void unpack(u32x4 r, float x[4], const float*) {
+  x[0] = __uint_as_float(r.x); x[1] = __uint_as_float(r.y); x[2] = __uint_as_float(r.z); x[3] = __uint_as_float(r.w);
 }
-__device__ __forceinline__ void pack4(const float y[4], u32x2* r) {
-  r->x = pack_bf16x2(y[0], y[1]);
-  r->y = pack_bf16x2(y[2], y[3]);
+__device__ __forceinline__ u32x4 pack(const float y[8], const bf16*) {
+  return u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
 }
-__device__ __forceinline__ void pack4(const float y[4], u32x4* r) {
-  r->x = __float_as_uint(y[0]); r->y = __float_as_uint(y[1]);
-  r->z = __float_as_uint(y[2]); r->w = __float_as_uint(y[3]);
+__device__ __forceinline__ u32x4 pack(const float y[4], const float*) {
+  return u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
 }
 
 // One row of a batch: its Q and K heads normalised and rotated (Q only
@@ -64,16 +60,18 @@ __device__ __forceinline__ void qknorm_rope_row(
     int num_seqs, int num_q_heads, int num_kv_heads, int cache_capacity, float eps,
     double log2_base, T* __restrict__ q_out, float* __restrict__ rope_table, T* __restrict__ k_cache,
     T* __restrict__ v_cache, PagedTable paged, float* s_cos, float* s_sin) {
-  using Raw = typename Raw4<T>::type;
+  using Raw = u32x4;
+  constexpr int E = kLaneElems<T>;  // elements per lane and half row
+  constexpr const T* kT = nullptr;   // selects the element type's unpack and pack
   constexpr int HALF = D / 2;
-  constexpr int LPH = HALF / 4;  // lanes per head row
+  constexpr int LPH = HALF / E;  // lanes per head row
   constexpr int HPW = 64 / LPH;  // head rows per wavefront pass
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
   const int sub = lane % LPH;
   const int hslot = lane / LPH;
-  const int i0 = sub * 4;
+  const int i0 = sub * E;
   const int heads = num_q_heads + 2 * num_kv_heads;
   const T* row = qkv + static_cast<size_t>(row_id) * heads * D;
   // With a rope table the attention kernel rotates Q itself: only K and V heads here.
@@ -132,16 +130,16 @@ __device__ __forceinline__ void qknorm_rope_row(
   }
   __syncthreads();
 
-  float cs[4], sn[4], wq1[4], wq2[4], wk1[4], wk2[4];
+  float cs[E], sn[E], wq1[E], wq2[E], wk1[E], wk2[E];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
+  for (int e = 0; e < E; ++e) {
     cs[e] = s_cos[i0 + e];
     sn[e] = s_sin[i0 + e];
   }
-  unpack4(*reinterpret_cast<const Raw*>(q_weight + i0), wq1);
-  unpack4(*reinterpret_cast<const Raw*>(q_weight + HALF + i0), wq2);
-  unpack4(*reinterpret_cast<const Raw*>(k_weight + i0), wk1);
-  unpack4(*reinterpret_cast<const Raw*>(k_weight + HALF + i0), wk2);
+  unpack(*reinterpret_cast<const Raw*>(q_weight + i0), wq1, kT);
+  unpack(*reinterpret_cast<const Raw*>(q_weight + HALF + i0), wq2, kT);
+  unpack(*reinterpret_cast<const Raw*>(k_weight + i0), wk1, kT);
+  unpack(*reinterpret_cast<const Raw*>(k_weight + HALF + i0), wk2, kT);
 
   int pass = 0;
   for (int hb = head0 + wave * HPW; hb < heads; hb += nwaves * HPW, ++pass) {
@@ -159,12 +157,12 @@ __device__ __forceinline__ void qknorm_rope_row(
       r1 = __builtin_nontemporal_load(reinterpret_cast<const Raw*>(row + head * D + i0));
       r2 = __builtin_nontemporal_load(reinterpret_cast<const Raw*>(row + head * D + HALF + i0));
     }
-    float x1[4], x2[4];
-    unpack4(r1, x1);
-    unpack4(r2, x2);
+    float x1[E], x2[E];
+    unpack(r1, x1, kT);
+    unpack(r2, x2, kT);
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
+    for (int e = 0; e < E; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
 #pragma unroll
     for (int m = 1; m < LPH; m <<= 1) ss += xor_shuffle(ss, m);
     if (!active) continue;
@@ -180,9 +178,9 @@ __device__ __forceinline__ void qknorm_rope_row(
     const bool is_q = head < num_q_heads;
     if (!is_q && !slot_ok) continue;
     const float inv_rms = rsqrtf(ss * (1.0f / D) + eps);
-    float y1[4], y2[4];
+    float y1[E], y2[E];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < E; ++e) {
       const float a = x1[e] * inv_rms * (is_q ? wq1[e] : wk1[e]);
       const float b = x2[e] * inv_rms * (is_q ? wq2[e] : wk2[e]);
       y1[e] = a * cs[e] - b * sn[e];
@@ -190,11 +188,8 @@ __device__ __forceinline__ void qknorm_rope_row(
     }
     T* dst = is_q ? q_out + (static_cast<size_t>(row_id) * num_q_heads + head) * D
                   : k_cache + cache_row(paged, req, head - num_q_heads, slot, num_kv_heads, cache_capacity, D);
-    Raw o1, o2;
-    pack4(y1, &o1);
-    pack4(y2, &o2);
-    *reinterpret_cast<Raw*>(dst + i0) = o1;
-    *reinterpret_cast<Raw*>(dst + HALF + i0) = o2;
+    *reinterpret_cast<Raw*>(dst + i0) = pack(y1, kT);
+    *reinterpret_cast<Raw*>(dst + HALF + i0) = pack(y2, kT);
   }
 }
 
@@ -271,7 +266,7 @@ hipError_t launch_pair_typed(const QkNormRopeArgs& p, const QkNormRopeArgs& d, h
 template <typename T, int D>
 hipError_t launch_typed(const QkNormRopeArgs& a, hipStream_t stream) {
   // bf16 prefill (K and V heads only): one wavefront per token, whose four
-  // prefetched passes cover its 2*Hkv rows for Hkv <= 8 and whose fp64 angles
+  // prefetched passes cover its 2*Hkv rows for Hkv <= 16 at D = 128 and whose fp64 angles
   // then overlap other tokens' work on the CU (four wavefronts waiting on the
   // first one's angles made the kernel a third slower).  Otherwise four.
   const int threads = a.rope_table ? 64 : 256;
