@@ -328,6 +328,7 @@ int32_t prefill_impl(const qkra_config* cfg, const void* qkv, const void* q_norm
   pa.num_seqs = num_seqs;
   pa.max_seqlen = max_seqlen;
   pa.scale_log2 = softmax_scale_log2(cfg->head_dim);
+  pa.tile_major = !cache_lens && num_seqs > 1 && static_cast<long long>(num_seqs) * max_seqlen == num_tokens;
   if (paged) pa.paged = *paged;
   // A plain bf16 prefill with the caller's weight bound launches only the softmax kernel it selects.
   const SoftmaxPath path = softmax_path(cfg, cache_lens);

@@ -113,6 +113,10 @@ struct PrefillAttnArgs {
   float scale_log2;         // log2(e) / sqrt(D)
   PagedTable paged;         // table null: contiguous caches (k_cache/v_cache are the pools otherwise)
   bool single_path = false; // bf16: only one of the two prefill attention kernels is launched
+  // bf16: work items ordered by query tile across the requests (heaviest first over the whole batch)
+  // instead of request by request.  Set where no item can be empty: every request holds max_seqlen
+  // tokens and none has history.
+  bool tile_major = false;
 };
 // The largest max|w_q| * max|w_k| for which the unshifted bf16 prefill
 // kernel takes a request (and every kernel computes this same value).

@@ -60,7 +60,12 @@
 //    compile-time constant.
 //  * Grid: work items ordered by (KV-head chunk, request, query tile from the
 //    last), and block ids remapped so that consecutive items land on the same
-//    XCD (the hardware deals workgroups round-robin over the 8 XCDs).  The
+//    XCD (the hardware deals workgroups round-robin over the 8 XCDs).  For a
+//    batch of equal-length requests with no history the order is (KV-head
+//    chunk, query tile from the last, request): heaviest first over the whole
+//    batch, which shortens the tail; where lengths differ, that order puts the
+//    empty items of the short requests (each still a workgroup launch) among
+//    the first, and the request order is kept.  The
 //    CUs of an XCD then work on the tiles of one request and KV head at a
 //    time, whose K/V stays in that XCD's L2 (ordering by tile across requests
 //    instead made a chunked prefill onto long caches fetch its history from
@@ -103,6 +108,11 @@ __device__ __forceinline__ float half_wave_max(float x) {
 }
 
 constexpr int NSLOT = 3;  // LDS tile slots
+
+// Launch flags: the host launched only the kernel its weight bound selects;
+// work items in query-tile order across the requests.
+constexpr int kFlagSinglePath = 1;
+constexpr int kFlagTileMajor = 2;
 
 // ds_read_b64_tr_b16 from a generic pointer into LDS (the address-space cast
 // keeps which LDS array it reads, so loads into other arrays need not be
@@ -225,7 +235,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ past_lens, bf16* __restrict__ out,
     int num_q_heads, int num_kv_heads,
     int cache_capacity, int num_seqs, int tiles_per_seq, int chunks_per_kv, int num_items,
-    float rms_eps, float scale_log2, float bound_limit, DecodeRole dec, PagedTable paged, int single_path) {
+    float rms_eps, float scale_log2, float bound_limit, DecodeRole dec, PagedTable paged, int flags) {
+  const bool single_path = (flags & kFlagSinglePath) != 0;
   constexpr int TBN = 8 / HC;       // token blocks (of 32) per workgroup
   constexpr int TM = 32 * TBN;      // tokens per workgroup
   constexpr int DS = D / 16;        // k-steps over D for the scores
@@ -280,8 +291,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   const int per_chunk = tiles_per_seq * num_seqs;
   const int chunk = logical / per_chunk;
   const int rem = logical - chunk * per_chunk;
-  const int seq = rem / tiles_per_seq;
-  const int tile = tiles_per_seq - 1 - rem % tiles_per_seq;
+  const bool tile_major = (flags & kFlagTileMajor) != 0;
+  const int seq = tile_major ? rem % num_seqs : rem / tiles_per_seq;
+  const int tile = tiles_per_seq - 1 - (tile_major ? rem / num_seqs : rem % tiles_per_seq);
   // Entries cached before the chunk (its token t sits at slot past + t).
   // Lengths are clamped to the cache so out-of-contract inputs cannot address past it.
   const int past = past_lens ? min(max(past_lens[seq], 0), cache_capacity) : 0;
@@ -747,6 +759,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   stamps.where(ntiles, logical);
 }
 
+int launch_flags(const PrefillAttnArgs& a) {
+  return (a.single_path ? kFlagSinglePath : 0) | (a.tile_major ? kFlagTileMajor : 0);
+}
+
 template <int D, int HC, bool kBounded, bool kPaged>
 hipError_t launch_typed(const PrefillAttnArgs& a, hipStream_t stream) {
   constexpr int TM = 32 * (8 / HC);
@@ -765,7 +781,7 @@ hipError_t launch_typed(const PrefillAttnArgs& a, hipStream_t stream) {
                      static_cast<const bf16*>(a.v_cache), a.cu_seqlens, a.past_lens, static_cast<bf16*>(a.out),
                      a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.num_seqs, tiles, chunks_per_kv,
                      static_cast<int>(items), a.rms_eps, a.scale_log2, bound_limit, DecodeRole{}, a.paged,
-                     a.single_path ? 1 : 0);
+                     launch_flags(a));
   return hipGetLastError();
 }
 
@@ -806,7 +822,7 @@ hipError_t launch_fused_typed(const PrefillAttnArgs& a, const DecodeAttnArgs& d,
                      static_cast<const bf16*>(a.v_cache), a.cu_seqlens, a.past_lens, static_cast<bf16*>(a.out),
                      a.num_q_heads, a.num_kv_heads, a.cache_capacity, a.num_seqs, tiles, chunks_per_kv,
                      static_cast<int>(items), a.rms_eps, a.scale_log2, bound_limit, dec, PagedTable{},
-                     a.single_path ? 1 : 0);
+                     launch_flags(a));
   return hipGetLastError();
 }
 
