@@ -11,7 +11,7 @@ import harness
 import oracle
 from harness import (BF16_TOL, FP32_TOL, assert_close, bits, check_prefill_caches, f64, layer_kw, note,
                      oracle_prefill, run_prefill, sample_tokens, tol_for)
-from workloads import HeadConfig, build_workload, make_prefill_inputs
+from workloads import HeadConfig, build_workload, make_prefill_inputs, prefill_inputs_from_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -30,6 +30,9 @@ CASES = [
     (12, 4, 128, [70, 129], 1e6),
     (32, 4, 64, [100], 1e6),
     (48, 3, 128, [77, 2], 1e4),
+    # Equal-length batches (work items in query-tile order across the requests).
+    (16, 4, 128, [160, 160], 1e6),
+    (8, 2, 64, [96, 96, 96], 1e4),
 ]
 
 
@@ -54,6 +57,26 @@ def test_prefill_matches_oracle(case, dtype):
     if got["q_tilde"] is not None:  # fp32 mode keeps q~ in the workspace
         assert_close(f64(got["q_tilde"]), ref["q_tilde"], tol, "q~ in the workspace")
     check_prefill_caches(p, k_before, v_before, ref, tol)
+
+
+@pytest.mark.parametrize("hq,hkv,d,length", [(32, 8, 128, 200), (16, 2, 64, 130)])
+def test_item_order_leaves_results_unchanged(hq, hkv, d, length):
+    """Every work item is computed the same way whatever order the grid runs them in.  An equal-length
+    batch (items by query tile across the requests) and the same requests followed by a shorter one (items
+    request by request) give bit-identical rows and caches for the shared requests, and both match the
+    oracle."""
+    h = HeadConfig(hq, hkv, d, 1e-6, 1e6)
+    longer = make_prefill_inputs(h, [length] * 3 + [7], seed=4242 + d, device=DEV, capacity=length + 3)
+    n = 3 * length
+    equal = prefill_inputs_from_rows(h, longer.qkv[:n], longer.q_norm_weight, longer.k_norm_weight, [length] * 3,
+                                     device=DEV, capacity=length + 3)
+    note(f"item order hq{hq} hkv{hkv} d{d} L{length}")
+    a = run_prefill(equal)["out"]
+    b = run_prefill(longer)["out"]
+    assert torch.equal(bits(a), bits(b[:n])), "rows differ between the two item orders"
+    assert torch.equal(bits(equal.k_cache), bits(longer.k_cache[:3])), "K cache differs"
+    assert torch.equal(bits(equal.v_cache), bits(longer.v_cache[:3])), "V cache differs"
+    assert_close(f64(a), oracle_prefill(equal)["out"], BF16_TOL, "out")
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])

@@ -17,6 +17,7 @@ from .synth import (  # noqa: F401
     WORKLOADS,
     build_workload,
     make_prefill_inputs,
+    prefill_inputs_from_rows,
     make_decode_inputs,
     make_append_inputs,
     make_norm_inputs,

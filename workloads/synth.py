@@ -229,6 +229,14 @@ def make_prefill_inputs(h: HeadConfig, seqlens: Sequence[int], seed: int, dtype=
     return _prefill_from_rows(h, rows, wq, wk, seqlens, capacity, dtype, device, parity)
 
 
+def prefill_inputs_from_rows(h: HeadConfig, rows: torch.Tensor, q_norm_weight: torch.Tensor,
+                             k_norm_weight: torch.Tensor, seqlens: Sequence[int], dtype=torch.bfloat16,
+                             device="cpu", capacity: Optional[int] = None, parity: bool = True) -> PrefillInputs:
+    """A prefill batch over given packed rows and norm weights (e.g. a prefix of another batch's rows)."""
+    return _prefill_from_rows(h, rows.cpu(), q_norm_weight.cpu(), k_norm_weight.cpu(), seqlens, capacity, dtype,
+                              device, parity)
+
+
 def make_decode_inputs(h: HeadConfig, cache_lens: Sequence[int], seed: int, dtype=torch.bfloat16,
                        device="cpu", capacity: Optional[int] = None, parity: bool = True) -> DecodeInputs:
     """One new token per request on top of a cache holding ``cache_lens[b]`` entries."""
