@@ -60,16 +60,16 @@
 //    compile-time constant.
 //  * Grid: work items ordered by (KV-head chunk, request, query tile from the
 //    last), and block ids remapped so that consecutive items land on the same
-//    XCD (the hardware deals workgroups round-robin over the 8 XCDs).  For a
-//    batch of equal-length requests with no history the order is (KV-head
-//    chunk, query tile from the last, request): heaviest first over the whole
-//    batch, which shortens the tail; where lengths differ, that order puts the
-//    empty items of the short requests (each still a workgroup launch) among
-//    the first, and the request order is kept.  The
+//    XCD (the hardware deals workgroups round-robin over the 8 XCDs).  The
 //    CUs of an XCD then work on the tiles of one request and KV head at a
 //    time, whose K/V stays in that XCD's L2 (ordering by tile across requests
 //    instead made a chunked prefill onto long caches fetch its history from
-//    HBM about 25 times); within a request the heaviest tiles go first.
+//    HBM about 25 times); within a request the heaviest tiles go first.  For
+//    a batch of equal-length requests with no history the order is (KV-head
+//    chunk, query tile from the last, request): heaviest first over the whole
+//    batch, which shortens the tail.  Where lengths differ that order would
+//    put the empty items of the short requests (each still a workgroup
+//    launch) among the first, so the request order is kept.
 
 #include "decode_body.h"
 #include "device_common.h"
