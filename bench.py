@@ -391,6 +391,43 @@ def calibration(torch, da):
                          f"{wg_mfma} workgroups of 4 wavefronts, median of 10"}
 
 
+def same_size_copy(torch, da, total_bytes, reps=20, batch=10):
+    """GB/s (read plus written) of the calibration copy moving `total_bytes` in all (half read, half written):
+    the ceiling of a kernel of that size that writes as much as it reads, its ramp and tail included.  Each
+    sample times `batch` copies launched back to back between two events (so the launch itself is hidden,
+    as for a kernel inside a step); the median of `reps` samples.  None without the calibration library."""
+    half = int(total_bytes // 2) // 16 * 16
+    if half <= 0:
+        return None
+    src = torch.empty(half // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    try:
+        run = lambda: da.check(da.qkra_calibrate_stream_copy(src, dst, half), "stream_copy")  # noqa: E731
+        run()
+    except RuntimeError:
+        return None
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(batch):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / batch)
+    del src, dst
+    return 2 * half / (spread(ts)[0] / 1e3) / 1e9
+
+
+def with_same_size_copy(rf, gbps):
+    """Adds the same-size copy's rate to a roofline object that is set against the copy."""
+    if rf is not None and gbps:
+        rf["same_size_copy_gbps"] = gbps
+        rf["frac_of_same_size_copy"] = rf["achieved"] / gbps
+    return rf
+
+
 def cpu_baseline(w, F_total, B_total):
     """The oracle, as it stands, on the host: the whole decode half at full size, and one (request, KV head)
     group of the prefill scaled by FLOP (the groups are independent and cost the same)."""
@@ -642,8 +679,10 @@ def main(argv=None):
             "decode_call_gbps": Bs / (calls["decode"] / 1e3) / 1e9,
             "prefill_kernel": roofline_for(kname, k, Fs, Bs, "mixed_qwen3_8b", measured=measured),
             "decode_kernel": roofline_for("decode_attn_split", k, Fs, Bs, "mixed_qwen3_8b", measured=measured),
-            "kernel1_prefill": roofline_for("qknorm_rope_kv_prefill", k, Fs, Bs, "mixed_qwen3_8b",
-                                            {"qknorm_rope_kv_prefill": k1_bytes}, measured=measured)}
+            "kernel1_prefill": with_same_size_copy(
+                roofline_for("qknorm_rope_kv_prefill", k, Fs, Bs, "mixed_qwen3_8b",
+                             {"qknorm_rope_kv_prefill": k1_bytes}, measured=measured),
+                same_size_copy(torch, da, k1_bytes))}
         del sw, r
         torch.cuda.empty_cache()
         # Steps next to the attention layer: the fused add + RMSNorm against HBM; the last-row gather and the
@@ -655,7 +694,9 @@ def main(argv=None):
             t, per, k = timed_reps(r, 50, 5, mask_of([n for n in lb if n in ids]), per_call=True)
             entry = {"calls_us": {c: spread(v)[0] * 1e3 for c, v in per.items()}, "reps": 50}
             if "fused_add_rmsnorm" in lb:
-                entry["kernel"] = roofline_for("fused_add_rmsnorm", k, 0.0, 0.0, name, lb, measured=measured)
+                entry["kernel"] = with_same_size_copy(
+                    roofline_for("fused_add_rmsnorm", k, 0.0, 0.0, name, lb, measured=measured),
+                    same_size_copy(torch, da, lb["fused_add_rmsnorm"]))
             else:
                 entry["bound"] = "latency"
             side[name] = entry
