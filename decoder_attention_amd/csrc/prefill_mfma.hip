@@ -222,9 +222,10 @@ __device__ __forceinline__ bool scores_bounded(WeightMax w, int past, float limi
 // One work item, with the softmax path fixed at compile time (kBounded: no
 // shift).  Each path is a kernel of its own: in one kernel, the register
 // allocation shared by the two tile loops spilled in the shifted one and
-// slowed both.  Every call launches both kernels over the same grid; each
-// workgroup of the one whose path its request and the weights do not select
-// returns at once.
+// slowed both.  Without the caller's weight bound a call launches both
+// kernels over the same grid, and each workgroup of the one whose path its
+// request and the weights do not select returns at once; with it, only the
+// selected kernel is launched (flag kFlagSinglePath).
 // kPaged: k_cache and v_cache are pools read through `paged` (a K/V tile of
 // BN keys always lies in one page: pages hold a multiple of BN slots).
 template <int D, int HC, bool kBounded, int kDecGW = 0, bool kPaged = false>
