@@ -18,7 +18,9 @@
 //    operand, Q^T stays in registers as the B operand for the whole loop.  In
 //    the 32x32 accumulator layout a lane then holds one query (lane % 32) and
 //    16 of the 32 keys of a block, so the row max needs one exchange with lane
-//    ^ 32 and the row sum none until the very end.
+//    ^ 32.  The row sum is formed on the matrix cores as well: a 16x16x32
+//    product of a 0/1 selection matrix with each P^T operand hands every lane
+//    its own query's sum over both lane halves.
 //  * O^T = V^T P^T with the same instruction: P^T goes straight from the
 //    score accumulators into the B operand (after rounding to bf16).  V stays
 //    row-major in LDS, as the cache holds it; the V^T operand comes from it
@@ -57,7 +59,8 @@
 //    into one slot do not touch the slots being read, so it waits for them
 //    only at the step's end.  One barrier per step.  The tile loop is
 //    unrolled by six so that every slot, hence every LDS address, is a
-//    compile-time constant.
+//    compile-time constant.  Steps whose next tile masks nothing for any row
+//    of the workgroup run first, in groups of six, as straight blocks.
 //  * Grid: work items ordered by (KV-head chunk, request, query tile from the
 //    last), and block ids remapped so that consecutive items land on the same
 //    XCD (the hardware deals workgroups round-robin over the 8 XCDs).  The
@@ -436,11 +439,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
-  float m_run[QB], l_run[QB];
+  float m_run[QB];
+  // Row sums on the matrix cores (see probs below): every element of
+  // lsum[qb] holds the sum for the lane's query, over both key halves.
+  f32x4 lsum[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = kNegInf;
-    l_run[qb] = 0.f;
+    lsum[qb] = f32x4{};
   }
 
   const int kv_end = past + min(seqlen, t0 + TM);
@@ -573,7 +579,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
       if (__any(need)) {
         const float m_new = need ? mx[qb] : m_run[qb];
         const float alpha = need ? fast_exp2(m_run[qb] - m_new) : 1.0f;
-        l_run[qb] *= alpha;
+        lsum[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
         m_run[qb] = m_new;
@@ -582,15 +588,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   };
 
   // p = 2^s (bounded path) or 2^(s - m), rounded to bf16 as the B operand of
-  // the P.V product; the row sum accumulates the same rounded values (dot
-  // with (1, 1)).  16-key step ks uses registers 8*(ks%2) .. +7 of key block
-  // ks/2.
-  const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
+  // the P.V product; the row sum accumulates the same rounded values, on the
+  // matrix cores (a chain of 16 v_dot2 per tile cost more than the four
+  // small products below).  16-key step ks uses registers 8*(ks%2) .. +7 of
+  // key block ks/2.
+  // Taken as the B operand of v_mfma_f32_16x16x32_bf16, P^T operand pf[qb][ks]
+  // puts lane l's eight probabilities (all of query l % 32) in column l % 16,
+  // k block l / 16.  Column n thus holds query n in k blocks 0 and 2 and query
+  // n + 16 in blocks 1 and 3.  With A[m][k] = 1 where bit 2 of m equals bit 0
+  // of k's block (0 elsewhere), output row m of column n is the sum of query
+  // n's (m / 4 even) or n + 16's (m / 4 odd) sixteen probabilities, and lane l
+  // receives rows 4 (l / 16) .. +3 of column l % 16: its own query's sum.
+  const bf16 sel1 = static_cast<bf16>(((lane >> 2) & 1) == ((lane >> 4) & 1) ? 1.0f : 0.0f);
+  const bf16x8 rsel = {sel1, sel1, sel1, sel1, sel1, sel1, sel1, sel1};
   auto probs = [&](f32x16 (&S)[QB][KB], bf16x8 (&pf)[QB][KSTEPS]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float nm = -m_run[qb];
-      float rs = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const int kb = ks >> 1, base = 8 * (ks & 1);
@@ -600,11 +614,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
           const float p0 = fast_exp2(kBounded ? S[qb][kb][base + 2 * e] : S[qb][kb][base + 2 * e] + nm);
           const float p1 = fast_exp2(kBounded ? S[qb][kb][base + 2 * e + 1] : S[qb][kb][base + 2 * e + 1] + nm);
           w[e] = pack_bf16x2(p0, p1);
-          rs = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[e]), ones, rs, false);
         }
         pf[qb][ks] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+        lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rsel, pf[qb][ks], lsum[qb], 0, 0, 0);
       }
-      l_run[qb] += rs;
     }
   };
 
@@ -660,6 +673,31 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     __syncthreads();
   };
 
+  // A step whose next tile lies at or below the diagonal of the workgroup's
+  // first row (tiles below kclean) masks nothing, and its tile kt + 2 exists:
+  // it runs as one straight block, with no per-wavefront test and no mask
+  // block between its P.V products and the barrier.
+  const int kclean = (past + t0 + 1) / BN;
+  const int nclean = min(kclean - 1, ntiles - 2);
+  auto clean_step = [&](auto jc, int kt, f32x16 (&Scur)[QB][KB], f32x16 (&Snext)[QB][KB]) {
+    constexpr int J = decltype(jc)::value;
+    using SlotPv = std::integral_constant<int, J % NSLOT>;
+    using SlotS = std::integral_constant<int, (J + 1) % NSLOT>;
+    using SlotLd = std::integral_constant<int, (J + 2) % NSLOT>;
+    load_tile(kt + 2, SlotLd{});
+    bf16x8 pf[QB][KSTEPS];
+    scores(SlotS{}, Snext);
+    probs(Scur, pf);
+    pv(SlotPv{}, pf);
+    if constexpr (!kBounded) {
+      float mx[QB];
+      tile_max(Snext, mx);
+      raise_max(mx);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  };
+
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
   // Tiles 0 and 1 stream into slots 0 and 1 while Q is loaded, normalised,
@@ -705,7 +743,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   // slots cycle every NSLOT steps.
   static_assert(NSLOT == 3, "the unroll below assumes a ring of three slots");
   stamps.now(QKRA_STAMP_LOOP);
-  for (int kt = 0; kt < ntiles; kt += 6) {
+  // Whole groups of six clean steps first, then the general loop from phase 0
+  // (a loop that chose between the two step kinds at every step spilled).
+  int kt0 = 0;
+  const int nclean6 = nclean >= 6 ? nclean - nclean % 6 : 0;
+  for (; kt0 < nclean6; kt0 += 6) {
+    clean_step(std::integral_constant<int, 0>{}, kt0, sA, sB);
+    if (kt0 == 0) stamps.now(QKRA_STAMP_FIRST_STEP);
+    clean_step(std::integral_constant<int, 1>{}, kt0 + 1, sB, sA);
+    clean_step(std::integral_constant<int, 2>{}, kt0 + 2, sA, sB);
+    clean_step(std::integral_constant<int, 3>{}, kt0 + 3, sB, sA);
+    clean_step(std::integral_constant<int, 4>{}, kt0 + 4, sA, sB);
+    clean_step(std::integral_constant<int, 5>{}, kt0 + 5, sB, sA);
+  }
+  for (int kt = kt0; kt < ntiles; kt += 6) {
     step(std::integral_constant<int, 0>{}, kt, sA, sB);
     if (kt == 0) stamps.now(QKRA_STAMP_FIRST_STEP);
     if (kt + 1 >= ntiles) break;
@@ -732,7 +783,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
   bf16* stile = region(wave / 2) + (wave % 2) * 32 * EST;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = l_run[qb] + xor_shuffle(l_run[qb], 32);
+    const float l_tot = lsum[qb][0];
     const float inv = 1.0f / l_tot;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
