@@ -54,9 +54,12 @@ __device__ __forceinline__ void decode_wave(
   constexpr int TILE = STEP * VROW;        // elements per tile
 
   const int lane = threadIdx.x & 63;
-  const int total = plan[0], per = plan[1];
+  // Plan entries and lengths are the same for every lane; readfirstlane keeps
+  // them (and the buffer resources formed from them) in scalar registers even
+  // where the compiler cannot use scalar loads for these pointers.
+  const int total = __builtin_amdgcn_readfirstlane(plan[0]), per = __builtin_amdgcn_readfirstlane(plan[1]);
   const int32_t* S0 = plan + 2;
-  const int first_unit = plan[3 + num_units + w];
+  const int first_unit = __builtin_amdgcn_readfirstlane(plan[3 + num_units + w]);
   if (first_unit < 0) return;  // idle wavefront (no barriers below)
   const int t0 = w * per;
   const int t1 = min(t0 + per, total);
@@ -74,14 +77,14 @@ __device__ __forceinline__ void decode_wave(
   };
   auto unit_at = [&](int i) {
     Unit u;
-    u.s0 = S0[i];
-    u.s1 = S0[i + 1];
+    u.s0 = __builtin_amdgcn_readfirstlane(S0[i]);
+    u.s1 = __builtin_amdgcn_readfirstlane(S0[i + 1]);
     u.b = i / nchunks;
     const int hc = i % nchunks;
     const int g = hc / chunks_per_kv;
     u.g = g;
     u.h0 = g * group + (hc % chunks_per_kv) * GW;
-    u.nkeys = min(cache_lens[u.b] + 1, cache_capacity);
+    u.nkeys = min(__builtin_amdgcn_readfirstlane(cache_lens[u.b]) + 1, cache_capacity);
     const size_t head_off = (static_cast<size_t>(u.b) * num_kv_heads + g) * cache_capacity * D;
     u.kb = k_cache + head_off;
     u.vb = v_cache + head_off;
@@ -124,7 +127,7 @@ __device__ __forceinline__ void decode_wave(
     uint32_t off = lin + static_cast<uint32_t>(t - u.s0) * (STEP * D * 2);
     if constexpr (kPaged) {  // the step's rows, from the page that holds them
       const int key0 = (t - u.s0) * STEP;
-      const size_t row = paged_row(paged, u.b, u.g, key0, num_kv_heads, D);
+      const size_t row = paged_row_uniform(paged, u.b, u.g, key0, num_kv_heads, D);
       kb = k_cache + row;
       vb = v_cache + row;
       range = live ? static_cast<uint32_t>(min(u.nkeys - key0, STEP)) * (D * 2) : 0u;

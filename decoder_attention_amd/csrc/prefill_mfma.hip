@@ -495,7 +495,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     const bf16* kt_base = kbase + static_cast<size_t>(k0) * D;
     const bf16* vt_base = vbase + static_cast<size_t>(k0) * D;
     if constexpr (kPaged) {  // the tile's rows, from the page that holds them
-      const size_t row = paged_row(paged, seq, g, k0, num_kv_heads, D);
+      const size_t row = paged_row_uniform(paged, seq, g, k0, num_kv_heads, D);
       kt_base = k_cache + row;
       vt_base = v_cache + row;
     }
