@@ -66,6 +66,9 @@ CASES = [
     (12, 4, 64, [31, 1000], [65, 9]),
     (48, 3, 128, [64, 200], [64, 64]),
     (8, 8, 128, [10], [300]),
+    # Histories that put the first masked tile just before, at and after the
+    # end of a group of six unmasked steps.
+    (32, 8, 128, [447, 446, 767, 383], [64, 64, 1, 130]),
 ]
 
 

@@ -33,6 +33,11 @@ CASES = [
     # Equal-length batches (work items in query-tile order across the requests).
     (16, 4, 128, [160, 160], 1e6),
     (8, 2, 64, [96, 96, 96], 1e4),
+    # Long enough for the unmasked steps that run in groups of six before the
+    # general loop: lengths on both sides of 7 and 9 tiles of 64 keys.
+    (32, 8, 128, [448, 449, 511, 577], 1e6),
+    (16, 16, 64, [833, 64], 1e4),
+    (64, 8, 64, [700], 1e6),
 ]
 
 
