@@ -127,7 +127,7 @@ __device__ __forceinline__ void decode_wave(
     uint32_t off = lin + static_cast<uint32_t>(t - u.s0) * (STEP * D * 2);
     if constexpr (kPaged) {  // the step's rows, from the page that holds them
       const int key0 = (t - u.s0) * STEP;
-      const size_t row = paged_row_uniform(paged, u.b, u.g, key0, num_kv_heads, D);
+      const size_t row = paged_row<true>(paged, u.b, u.g, key0, num_kv_heads, D);
       kb = k_cache + row;
       vb = v_cache + row;
       range = live ? static_cast<uint32_t>(min(u.nkeys - key0, STEP)) * (D * 2) : 0u;

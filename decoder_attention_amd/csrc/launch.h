@@ -54,19 +54,14 @@ struct PagedTable {
 };
 
 // Element offset of the first element of row s of request b, KV head g.
-__device__ __forceinline__ size_t paged_row(const PagedTable& pt, int b, int g, int s, int num_kv_heads, int head_dim) {
-  int page = pt.table[static_cast<size_t>(b) * pt.pages_per_seq + (s >> pt.page_shift)];
-  page = min(max(page, 0), pt.num_pages - 1);
-  return ((static_cast<size_t>(page) * num_kv_heads + g) * (static_cast<size_t>(1) << pt.page_shift) +
-          (s & ((1 << pt.page_shift) - 1))) * head_dim;
-}
-// The same for a row that the whole wavefront shares: the table entry is
-// made wave-uniform, so a buffer resource formed from it stays in scalar
+// kUniform: the row is the same for the whole wavefront; the table entry is
+// then made wave-uniform, so a buffer resource formed from it stays in scalar
 // registers (a resource in vector registers costs a waterfall loop around
 // every load that uses it).
-__device__ __forceinline__ size_t paged_row_uniform(const PagedTable& pt, int b, int g, int s, int num_kv_heads,
-                                                    int head_dim) {
-  int page = __builtin_amdgcn_readfirstlane(pt.table[static_cast<size_t>(b) * pt.pages_per_seq + (s >> pt.page_shift)]);
+template <bool kUniform = false>
+__device__ __forceinline__ size_t paged_row(const PagedTable& pt, int b, int g, int s, int num_kv_heads, int head_dim) {
+  int page = pt.table[static_cast<size_t>(b) * pt.pages_per_seq + (s >> pt.page_shift)];
+  if constexpr (kUniform) page = __builtin_amdgcn_readfirstlane(page);
   page = min(max(page, 0), pt.num_pages - 1);
   return ((static_cast<size_t>(page) * num_kv_heads + g) * (static_cast<size_t>(1) << pt.page_shift) +
           (s & ((1 << pt.page_shift) - 1))) * head_dim;

@@ -82,27 +82,19 @@
 namespace qkra {
 namespace {
 
-// Launch shape.  QB query blocks (of 32 rows) per wavefront and 8/QB
-// wavefronts per workgroup, so a workgroup always owns 8 query blocks; BN keys
-// per K/V tile.  QB = 1 gives two wavefronts per SIMD (their matrix and vector
-// work interleave); QB = 2 halves the LDS reads per MFMA but leaves one
-// wavefront per SIMD.
-#ifndef QKRA_PREFILL_QB
-#define QKRA_PREFILL_QB 1
-#endif
-#ifndef QKRA_PREFILL_BN
-#define QKRA_PREFILL_BN 64
-#endif
-constexpr int QB = QKRA_PREFILL_QB;
-constexpr int BN = QKRA_PREFILL_BN;
+// Launch shape: QB = 1 query block (32 rows) per wavefront and 8 wavefronts
+// per workgroup, so a workgroup owns 8 query blocks; BN keys per K/V tile.
+// Two wavefronts share each SIMD, so their matrix and vector work interleave.
+// The LDS slots, the DMA lane map and the Q and output staging below are laid
+// out for exactly this shape (their static_asserts say so).
+constexpr int QB = 1;
+constexpr int BN = 64;
 constexpr int NWAVES = 8 / QB;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr float TAU = 8.0f;   // lazy-rescale threshold (log2 units)
 // Largest score bound (log2 units) taken without a shift: p then lies in
 // [2^-48, 2^48], a row sum of up to 2^31 keys below 2^79.
 constexpr float BOUND_LOG2 = 48.0f;
-static_assert(QB == 1 || QB == 2, "QB");
-static_assert(BN == 32 || BN == 64, "BN");
 
 // Max of a value held by lanes l and l ^ 32 (gfx950 v_permlane32_swap).
 __device__ __forceinline__ float half_wave_max(float x) {
@@ -495,7 +487,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_mfma_kernel(
     const bf16* kt_base = kbase + static_cast<size_t>(k0) * D;
     const bf16* vt_base = vbase + static_cast<size_t>(k0) * D;
     if constexpr (kPaged) {  // the tile's rows, from the page that holds them
-      const size_t row = paged_row_uniform(paged, seq, g, k0, num_kv_heads, D);
+      const size_t row = paged_row<true>(paged, seq, g, k0, num_kv_heads, D);
       kt_base = k_cache + row;
       vt_base = v_cache + row;
     }
